@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs for the tensor-parallel DiT block shard.
+
+This module only draws random tensors and states workload shapes.  It holds
+none of the block's arithmetic: both the CPU oracle (``oracle/``) and the HIP
+path (``tensor_dit_transformer_amd``) consume what it returns, and neither is
+imported here.
+
+Distributions and draw order (one ``numpy.random.default_rng(seed)`` stream,
+float32 ``standard_normal`` scaled by the stated standard deviation):
+
+    x ~ N(0, 1)                                [T, D]
+    W_q, W_k, W_v ~ N(0, 0.02)                 [D, D]   (nn.Linear [out, in])
+    b_q, b_k, b_v ~ N(0, 0.01)                 [D]
+    W_o ~ N(0, 0.02)                           [D, H*d]
+    b_o ~ N(0, 0.01)                           [D]
+    W_up ~ N(0, 0.02)                          [F, D]
+    b_up ~ N(0, 0.01)                          [F]
+    W_dn ~ N(0, 0.02)                          [D, F]
+    b_dn ~ N(0, 0.01)                          [D]
+
+Tensors a workload lacks (no attention, or no MLP) are skipped, not drawn.
+For bf16 workloads every array is rounded to bfloat16 with torch's
+round-to-nearest-even conversion, so the GPU and the oracle read identical
+bits; the arrays are handed out as float32 numpy arrays holding those
+bf16-representable values, plus the raw uint16 bit patterns for upload.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import numpy as np
+
+WEIGHT_STD = 0.02
+BIAS_STD = 0.01
+
+# Names in the order they are drawn.
+DRAW_ORDER = ("x", "w_q", "w_k", "w_v", "b_q", "b_k", "b_v", "w_o", "b_o",
+              "w_up", "b_up", "w_dn", "b_dn")
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape of one block-shard workload (unsharded sizes)."""
+    name: str
+    tokens: int
+    hidden: int
+    num_heads: int      # 0: no attention half
+    head_dim: int
+    ffn: int            # 0: no MLP half
+    tp_degree: int
+    dtype: str          # "f32" or "bf16"
+    description: str = ""
+
+    @property
+    def has_attn(self) -> bool:
+        return self.num_heads > 0
+
+    @property
+    def has_mlp(self) -> bool:
+        return self.ffn > 0
+
+
+# The five workloads of the tensor-parallel block shard.  Token count 4608 is
+# 4096 image latents plus 512 text tokens; 16384 is a video-like latent.
+C1 = Workload("mlp_f32_T64_D256_F1024_P2", 64, 256, 0, 0, 1024, 2, "f32",
+              "fp32 MLP block, both ranks of tp_degree 2")
+C2 = Workload("mlp_bf16_T4608_D3072_F12288_P4", 4608, 3072, 0, 0, 12288, 4, "bf16",
+              "bf16 DiT MLP shard, one rank of tp_degree 4")
+C3 = Workload("attn_bf16_T4608_D3072_H24_P4", 4608, 3072, 24, 128, 0, 4, "bf16",
+              "bf16 DiT attention shard, one rank of tp_degree 4")
+C4 = Workload("block_bf16_T4608_D6144_H48_F18432_P4", 4608, 6144, 48, 128, 18432, 4,
+              "bf16", "bf16 wide DiT block shard, one rank of tp_degree 4")
+C5_P4 = Workload("block_bf16_T16384_D6144_H48_F18432_P4", 16384, 6144, 48, 128, 18432,
+                 4, "bf16", "bf16 full block, all 4 rank shards then partial reduce")
+C5_P2 = dataclasses.replace(C5_P4, name="block_bf16_T16384_D6144_H48_F18432_P2",
+                            tp_degree=2,
+                            description="bf16 full block, both rank shards then partial reduce")
+
+WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5_P4, C5_P2)}
+
+
+def _shapes(w: Workload) -> Dict[str, tuple]:
+    T, D, F = w.tokens, w.hidden, w.ffn
+    HD = w.num_heads * w.head_dim
+    shapes = {"x": (T, D)}
+    if w.has_attn:
+        shapes.update(w_q=(HD, D), w_k=(HD, D), w_v=(HD, D),
+                      b_q=(HD,), b_k=(HD,), b_v=(HD,),
+                      w_o=(D, HD), b_o=(D,))
+    if w.has_mlp:
+        shapes.update(w_up=(F, D), b_up=(F,), w_dn=(D, F), b_dn=(D,))
+    return shapes
+
+
+def _std(name: str) -> float:
+    if name == "x":
+        return 1.0
+    return WEIGHT_STD if name.startswith("w_") else BIAS_STD
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of a float32 array, rounded by torch
+    (round-to-nearest-even)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """float32 values of bfloat16 bit patterns (exact widening)."""
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class Inputs:
+    workload: Workload
+    values: Dict[str, np.ndarray]          # float32 arrays (bf16-representable if bf16)
+    bits: Optional[Dict[str, np.ndarray]]  # uint16 bf16 patterns (bf16 workloads only)
+
+    def __getitem__(self, k: str) -> np.ndarray:
+        return self.values[k]
+
+
+def make_inputs(w: Workload, seed: int = 0, tokens: Optional[int] = None) -> Inputs:
+    """Draw every tensor of workload ``w`` from ``default_rng(seed)``.
+
+    ``tokens`` overrides the token count (the weights are unchanged in shape and
+    drawn identically only when ``tokens`` equals ``w.tokens``)."""
+    if tokens is not None:
+        w = dataclasses.replace(w, tokens=tokens)
+    rng = np.random.default_rng(seed)
+    shapes = _shapes(w)
+    values: Dict[str, np.ndarray] = {}
+    for name in DRAW_ORDER:
+        if name not in shapes:
+            continue
+        a = rng.standard_normal(shapes[name], dtype=np.float32)
+        if _std(name) != 1.0:
+            a *= np.float32(_std(name))
+        values[name] = a
+    bits = None
+    if w.dtype == "bf16":
+        bits = {k: bf16_bits(v) for k, v in values.items()}
+        values = {k: bits_to_f32(b) for k, b in bits.items()}
+    return Inputs(w, values, bits)
+
+
+def random_matrix(shape, seed: int, std: float = 1.0, dtype: str = "bf16"):
+    """A seeded N(0, std^2) matrix for single-kernel cases (a rowwise GEMM fed a
+    seeded activation, attention fed a seeded packed QKV, the reduce fed seeded
+    partials).  Returns (float32 values, uint16 bits or None)."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    if dtype == "bf16":
+        b = bf16_bits(a)
+        return bits_to_f32(b), b
+    return a, None
+
+
+def sample_rows(tokens: int, n: int, seed: int = 1) -> np.ndarray:
+    """Sorted distinct row indices for row-sampled checks; always includes the
+    first and last row (the ragged tail)."""
+    rng = np.random.default_rng(seed)
+    n = min(n, tokens)
+    rows = set(rng.choice(tokens, size=n, replace=False).tolist())
+    rows.update({0, tokens - 1})
+    return np.array(sorted(rows), dtype=np.int64)
