@@ -1,0 +1,206 @@
+/*
+ * tp_shard.h -- C ABI of one tensor-parallel rank's share of a DiT block,
+ * running on one AMD Instinct MI355X (gfx950).
+ *
+ * What it computes follows the Diffusers tensor-parallelism page
+ * ("Paralelismo de tensor"; v0.43.0 Chinese twin "张量并行"), cited as
+ * [TP page, §section]:
+ *   - intro: each device holds a colwise or rowwise slice of each layer and
+ *     computes a partial result; an AllReduce at the layer boundary combines
+ *     the partials into the full output;
+ *   - §"Colwise e rowwise" (列向和行向), style table: "colwise" shards output
+ *     features (weight dim 0) and each rank computes a slice of the output
+ *     (to_q, to_k, to_v, the FFN in-projection); "rowwise" shards input
+ *     features (weight dim 1) and each rank computes a partial sum (to_out.0,
+ *     the FFN out-projection); always colwise then rowwise, one AllReduce at
+ *     the block boundary; colwise Q/K/V give each rank a subset of heads;
+ *   - §"Projeções fundidas" (融合投影): a packed Linear is sharded block by
+ *     block; a rowwise to_out may pack [inner_dim, mlp_hidden_dim];
+ *   - §"Restrições e verificação" (约束与验证): tp_degree divides the head
+ *     count and each packed block on its own, checked before any weight is
+ *     touched;
+ *   - §"Limitações": unsupported combinations raise an error instead of
+ *     silently doing something else.
+ *
+ * Readings where the pages are silent: attention is softmax(Q K^T/sqrt(d)) V
+ * per head, non-causal, unmasked; the MLP activation is GELU (tanh form);
+ * rank r owns heads [r*H/P, (r+1)*H/P) and the contiguous 1/P block of every
+ * sharded feature dimension; the rowwise bias is added once, by the reduce.
+ *
+ * Conventions for every call below:
+ *   - Matrices are row-major; "ld" arguments are row strides in ELEMENTS.
+ *     Weights use the nn.Linear layout [out_features, in_features].
+ *   - Device pointers must be 16-byte aligned and every row start too
+ *     (ld * element size a multiple of 16 bytes).
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and is asynchronous: no call synchronises the host, except
+ *     tp_block_shard_create (blocking host->device copies).
+ *   - The calling thread's current HIP device must be the one the shard was
+ *     created on.
+ *   - The caller owns every activation, partial and output buffer, and the
+ *     stream.  The library allocates device memory only in
+ *     tp_block_shard_create (the rank's weight slices); no call allocates.
+ *   - Every call validates all arguments before touching the device and
+ *     returns a tp_status; on error nothing is enqueued and
+ *     tp_last_error_detail() says why.  There is no fallback path.
+ */
+#ifndef TP_SHARD_H
+#define TP_SHARD_H
+
+#include <stdint.h>
+
+/* Symbols of this interface are the only ones the library exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define TP_API __attribute__((visibility("default")))
+#else
+#define TP_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tp_status {
+  TP_OK = 0,
+  TP_ERR_ARG = -1,           /* NULL/misaligned pointer, bad size, wrong layer */
+  TP_ERR_DIVISIBILITY = -2,  /* tp_degree does not divide heads / a packed block / ffn,
+                                or num_heads*head_dim != hidden */
+  TP_ERR_UNSUPPORTED = -3,   /* a valid request this library does not build */
+  TP_ERR_HIP = -4,           /* a HIP runtime call or kernel launch failed */
+  TP_ERR_OOM = -5            /* device allocation failed */
+} tp_status;
+
+typedef enum tp_dtype {
+  TP_F32 = 0,                /* fp32 activations and weights */
+  TP_BF16 = 1                /* bf16 activations and weights; fp32 accumulate */
+} tp_dtype;
+
+typedef enum tp_layer {
+  TP_QKV = 0,                /* colwise: packed [Q_r; K_r; V_r], blocks [1, 1, 1] */
+  TP_MLP_UP = 1,             /* colwise: FFN in-projection, fused bias + GELU-tanh */
+  TP_ATTN_OUT = 2,           /* rowwise: to_out.0 (attention out-projection) */
+  TP_MLP_DOWN = 3,           /* rowwise: FFN out-projection */
+  TP_BLOCK_OUT = 4           /* rowwise, packed over [inner_dim, ffn]: [o_r | h_r] */
+} tp_layer;
+
+/* UNSHARDED sizes of the block and this shard's place in the group.
+ * num_heads == 0: no attention layers; ffn == 0: no MLP layers. */
+typedef struct tp_block_config {
+  int32_t tp_degree;         /* P >= 1 */
+  int32_t rank;              /* 0 <= rank < P */
+  int64_t hidden;            /* D */
+  int64_t num_heads;         /* H; H * head_dim must equal D */
+  int64_t head_dim;          /* d */
+  int64_t ffn;               /* F */
+  tp_dtype dtype;
+} tp_block_config;
+
+/* UNSHARDED weights in HOST memory, element type = config dtype (bf16 as raw
+ * 16-bit patterns), row-major nn.Linear layout.  Only this rank's slices are
+ * read and copied to the device; the arrays are not retained.  Biases may be
+ * NULL (zero).  The rowwise biases (b_o, b_down) are not sharded: they are
+ * added once after the partial sum, by tp_partial_reduce. */
+typedef struct tp_block_weights {
+  const void *w_q, *w_k, *w_v;     /* [H*d, D] each */
+  const void *b_q, *b_k, *b_v;     /* [H*d] each, nullable */
+  const void *w_o;                 /* [D, H*d] */
+  const void *w_up;                /* [F, D] */
+  const void *b_up;                /* [F], nullable */
+  const void *w_down;              /* [D, F] */
+} tp_block_weights;
+
+typedef struct tp_block_shard tp_block_shard;  /* opaque; owns the device weight slices */
+
+/* Validate `cfg` and `w`, then allocate and upload rank cfg->rank's slices on
+ * the current HIP device [TP page, §Carregar um modelo fragmentado: each rank
+ * reads only its own slice of each weight]:
+ *   colwise (dim-0 rows):   W_qkv_r = [W_q[R_r,:]; W_k[R_r,:]; W_v[R_r,:]]  [3*D_r, D]
+ *                           W_up_r  = W_up[C_r,:]                           [F_r, D]
+ *   rowwise (dim-1 cols):   W_o_r   = W_o[:, R_r]                           [D, D_r]
+ *                           W_dn_r  = W_down[:, C_r]                        [D, F_r]
+ * with D_r = D/P, R_r = [r*D_r, (r+1)*D_r), F_r = F/P, C_r = [r*F_r, (r+1)*F_r).
+ * Checks, in order, before any allocation [TP page, §Restrições e
+ * verificação]: out != NULL (else TP_ERR_ARG); cfg, w != NULL; dtype known;
+ * P >= 1 and 0 <= rank < P; D > 0, H >= 0, F >= 0, not both H and F zero,
+ * d > 0 if H > 0 (TP_ERR_ARG); H*d == D, P | H, P | D (each Q/K/V block),
+ * P | F (TP_ERR_DIVISIBILITY); D, D_r, F_r multiples of 8
+ * (TP_ERR_UNSUPPORTED); the weights the enabled layers need are non-NULL
+ * (TP_ERR_ARG).  On any error *out is set to NULL and nothing is allocated
+ * (or everything allocated so far is freed). */
+TP_API tp_status tp_block_shard_create(const tp_block_config *cfg, const tp_block_weights *w,
+                                tp_block_shard **out);
+
+/* Free the shard's device memory.  The caller must have synchronised every
+ * stream that still uses it.  NULL is ignored. */
+TP_API void tp_block_shard_destroy(tp_block_shard *shard);
+
+/* Colwise projection [TP page, §Colwise e rowwise]:
+ *   y[t, n] = act( sum_k x[t, k] * W_r[n, k] + b_r[n] ),  t < tokens, n < N_r
+ * layer TP_QKV:    N_r = 3*D_r, columns [Q_r | K_r | V_r], act = identity;
+ * layer TP_MLP_UP: N_r = F_r, act = GELU-tanh.
+ * x: device [tokens, D] (ldx >= D); y: device [tokens, N_r] (ldy >= N_r); both
+ * in the config dtype.  tokens == 0 is a no-op; tokens < 0 is TP_ERR_ARG, as is
+ * a layer that is not colwise or was not configured. */
+TP_API tp_status tp_colwise_linear(tp_block_shard *shard, tp_layer layer, int64_t tokens,
+                            const void *x, int64_t ldx, void *y, int64_t ldy, void *stream);
+
+/* Both colwise projections of the block in one launch, over the packed
+ * weight [W_qkv_r; W_up_r] ([TP page, §Projeções fundidas]: a fused
+ * Q, K, V and MLP-in projection, sharded block by block):
+ *   qkv[t, 0:3*D_r] = x W_qkv_r^T + b_qkv_r      (ldqkv >= 3*D_r)
+ *   h  [t, 0:F_r]   = GELU-tanh(x W_up_r^T + b_up_r)  (ldh >= F_r)
+ * Needs both attention and MLP configured (else TP_ERR_ARG).  Results are
+ * identical to TP_QKV followed by TP_MLP_UP. */
+TP_API tp_status tp_colwise_qkv_up(tp_block_shard *shard, int64_t tokens, const void *x, int64_t ldx,
+                            void *qkv, int64_t ldqkv, void *h, int64_t ldh, void *stream);
+
+/* Attention over this rank's H/P heads [TP page, §Colwise e rowwise: colwise
+ * Q/K/V give each rank a subset of heads]: for local head j,
+ *   o[:, j*d:(j+1)*d] = softmax(Q_j K_j^T / sqrt(d)) V_j   (non-causal, no mask)
+ * with Q_j = qkv[:, j*d:(j+1)*d], K_j = qkv[:, D_r + j*d : ...],
+ * V_j = qkv[:, 2*D_r + j*d : ...].  qkv: device [tokens, 3*D_r]
+ * (ldqkv >= 3*D_r); o: device [tokens, D_r] (ldo >= D_r).  Softmax in fp32.
+ * Built for bf16 and head_dim 128 only; other combinations return
+ * TP_ERR_UNSUPPORTED.  Needs attention configured (else TP_ERR_ARG).
+ * o must not overlap qkv. */
+TP_API tp_status tp_attn_heads(tp_block_shard *shard, int64_t tokens, const void *qkv, int64_t ldqkv,
+                        void *o, int64_t ldo, void *stream);
+
+/* Rowwise projection, partial sum [TP page, §Colwise e rowwise]:
+ *   partial[t, n] (+)= sum_k x_local[t, k] * W_r[n, k],  n < D, k < K_r   (no bias)
+ * layer TP_ATTN_OUT:  K_r = D_r (x_local = o_r);
+ * layer TP_MLP_DOWN:  K_r = F_r (x_local = h_r);
+ * layer TP_BLOCK_OUT: K_r = D_r + F_r, x_local = [o_r | h_r], W_r = [W_o_r | W_dn_r]
+ *                     (a packed rowwise to_out over [inner_dim, mlp_hidden_dim],
+ *                     [TP page, §Projeções fundidas]); equals ATTN_OUT + MLP_DOWN.
+ * x_local: device, config dtype, ldx >= K_r; partial: device fp32 [tokens, D],
+ * ldp >= D.  accumulate = 0 stores, 1 adds to what partial holds. */
+TP_API tp_status tp_rowwise_linear_partial(tp_block_shard *shard, tp_layer layer, int64_t tokens,
+                                    const void *x_local, int64_t ldx, float *partial,
+                                    int64_t ldp, int accumulate, void *stream);
+
+/* The layer-boundary AllReduce of the TP page's intro, on one GPU: all
+ * simulated ranks' partials summed in rank order, then the rowwise biases:
+ *   out[t, c] = ((partials[0][t, c] + partials[1][t, c]) + ...) + biases[0][c] + ...
+ * in fp32.  partials: HOST array of n_partials DEVICE pointers, each fp32
+ * [tokens, hidden] with row stride ldp; biases: HOST array of n_biases DEVICE
+ * pointers to fp32 [hidden] (may be NULL when n_biases == 0); out: device
+ * fp32, ldo >= hidden.  1 <= n_partials <= 16, 0 <= n_biases <= 4 (else
+ * TP_ERR_UNSUPPORTED beyond, TP_ERR_ARG below); hidden a multiple of 4.  out
+ * may alias partials[0] exactly (same pointer and stride), nothing else. */
+TP_API tp_status tp_partial_reduce(const float *const *partials, int32_t n_partials, int64_t ldp,
+                            const float *const *biases, int32_t n_biases, int64_t tokens,
+                            int64_t hidden, float *out, int64_t ldo, void *stream);
+
+/* Static text naming a status code. */
+TP_API const char *tp_status_string(tp_status status);
+
+/* Text describing the last non-OK status returned to the calling thread
+ * (thread-local; valid until that thread's next call). */
+TP_API const char *tp_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_SHARD_H */

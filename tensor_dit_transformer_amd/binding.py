@@ -1,0 +1,275 @@
+"""ctypes binding of libtp_shard.so (include/tp_shard.h).
+
+Argument marshalling only: torch tensors supply device pointers and row
+strides, ``torch.cuda.current_stream()`` supplies the hipStream_t, numpy arrays
+supply the host weights for shard creation.  Every computation runs in the HIP
+library; there is no fallback of any kind.  If the library is missing, every
+entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtp_shard.so")
+
+# tp_status
+TP_OK = 0
+TP_ERR_ARG = -1
+TP_ERR_DIVISIBILITY = -2
+TP_ERR_UNSUPPORTED = -3
+TP_ERR_HIP = -4
+TP_ERR_OOM = -5
+# tp_dtype
+TP_F32 = 0
+TP_BF16 = 1
+# tp_layer
+TP_QKV = 0
+TP_MLP_UP = 1
+TP_ATTN_OUT = 2
+TP_MLP_DOWN = 3
+TP_BLOCK_OUT = 4
+
+EXPORTED = (
+    "tp_block_shard_create", "tp_block_shard_destroy", "tp_colwise_linear",
+    "tp_colwise_qkv_up", "tp_attn_heads", "tp_rowwise_linear_partial",
+    "tp_partial_reduce", "tp_status_string", "tp_last_error_detail",
+)
+
+
+class TpBlockConfig(ctypes.Structure):
+    _fields_ = [("tp_degree", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("hidden", ctypes.c_int64), ("num_heads", ctypes.c_int64),
+                ("head_dim", ctypes.c_int64), ("ffn", ctypes.c_int64),
+                ("dtype", ctypes.c_int)]
+
+
+_WEIGHT_FIELDS = ("w_q", "w_k", "w_v", "b_q", "b_k", "b_v", "w_o", "w_up", "b_up", "w_down")
+
+
+class TpBlockWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS]
+
+
+class TpError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)} ({detail})")
+        self.status = status
+        self.detail = detail
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library {LIB_PATH} is missing: build it with "
+                               "`python -m tensor_dit_transformer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.tp_block_shard_create.argtypes = [ctypes.POINTER(TpBlockConfig),
+                                            ctypes.POINTER(TpBlockWeights), ctypes.POINTER(vp)]
+        L.tp_block_shard_destroy.argtypes = [vp]
+        L.tp_block_shard_destroy.restype = None
+        L.tp_colwise_linear.argtypes = [vp, ctypes.c_int, i64, vp, i64, vp, i64, vp]
+        L.tp_colwise_qkv_up.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp]
+        L.tp_attn_heads.argtypes = [vp, i64, vp, i64, vp, i64, vp]
+        L.tp_rowwise_linear_partial.argtypes = [vp, ctypes.c_int, i64, vp, i64, vp, i64,
+                                                ctypes.c_int, vp]
+        L.tp_partial_reduce.argtypes = [ctypes.POINTER(vp), i32, i64, ctypes.POINTER(vp), i32,
+                                        i64, i64, vp, i64, vp]
+        for f in ("tp_block_shard_create", "tp_colwise_linear", "tp_colwise_qkv_up",
+                  "tp_attn_heads", "tp_rowwise_linear_partial", "tp_partial_reduce"):
+            getattr(L, f).restype = ctypes.c_int
+        L.tp_status_string.argtypes = [ctypes.c_int]
+        L.tp_status_string.restype = ctypes.c_char_p
+        L.tp_last_error_detail.argtypes = []
+        L.tp_last_error_detail.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().tp_status_string(status).decode()
+
+
+def tp_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def tp_last_error_detail() -> str:
+    return lib().tp_last_error_detail().decode()
+
+
+def _check(status: int) -> None:
+    if status != TP_OK:
+        raise TpError(status, tp_last_error_detail())
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _mat(t, name: str, rows: int = 0, cols: int = 0, dtype: Optional[int] = None):
+    """(device pointer, row stride in elements) of a 2-D row-major torch
+    tensor that holds at least rows x cols elements of the given dtype code."""
+    if dtype is not None and _dtype_code(t) != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, the shard's dtype code is {dtype}")
+    if t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, needs at least ({rows}, {cols})")
+    return t.data_ptr(), t.stride(0)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return TP_BF16
+    if t.dtype == torch.float32:
+        return TP_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+class TpBlockShard:
+    """Handle of a created shard (owns the rank's device weight slices)."""
+
+    def __init__(self, handle: int, cfg: TpBlockConfig):
+        self.handle = handle
+        self.tp_degree = cfg.tp_degree
+        self.rank = cfg.rank
+        self.hidden = cfg.hidden
+        self.num_heads = cfg.num_heads
+        self.head_dim = cfg.head_dim
+        self.ffn = cfg.ffn
+        self.dtype = cfg.dtype
+        P = cfg.tp_degree
+        self.d_r = cfg.hidden // P if cfg.num_heads > 0 else 0
+        self.f_r = cfg.ffn // P
+        self.heads_r = cfg.num_heads // P
+
+    def close(self) -> None:
+        if self.handle:
+            lib().tp_block_shard_destroy(self.handle)
+            self.handle = 0
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        import torch
+        torch.cuda.synchronize()
+        self.close()
+
+
+def make_config(tp_degree: int, rank: int, hidden: int, num_heads: int, head_dim: int,
+                ffn: int, dtype: int) -> TpBlockConfig:
+    return TpBlockConfig(tp_degree, rank, hidden, num_heads, head_dim, ffn, dtype)
+
+
+def _weight_shapes(cfg: TpBlockConfig):
+    D, HD, F = cfg.hidden, cfg.num_heads * cfg.head_dim, cfg.ffn
+    return {"w_q": (HD, D), "w_k": (HD, D), "w_v": (HD, D), "b_q": (HD,), "b_k": (HD,),
+            "b_v": (HD,), "w_o": (D, HD), "w_up": (F, D), "b_up": (F,), "w_down": (D, F)}
+
+
+def _host_weights(weights: Dict[str, np.ndarray], cfg: TpBlockConfig):
+    """TpBlockWeights pointing at contiguous host arrays (kept alive by the
+    returned list).  bf16 arrays are uint16 bit patterns."""
+    keep = []
+    w = TpBlockWeights()
+    want = np.uint16 if cfg.dtype == TP_BF16 else np.float32
+    shapes = _weight_shapes(cfg)
+    for name in _WEIGHT_FIELDS:
+        a = weights.get(name)
+        if a is None and name == "w_down":
+            a = weights.get("w_dn")
+        if a is None:
+            continue
+        a = np.ascontiguousarray(a)
+        if a.dtype != want:
+            raise ValueError(f"{name}: host weights must be {np.dtype(want).name} for this dtype")
+        if a.size != int(np.prod(shapes[name])):
+            raise ValueError(f"{name}: {a.size} elements, expected shape {shapes[name]}")
+        keep.append(a)
+        setattr(w, name, a.ctypes.data)
+    return w, keep
+
+
+# ------------------------------------------------------------------ entry points
+
+def tp_block_shard_create(cfg: TpBlockConfig, weights: Dict[str, np.ndarray]) -> TpBlockShard:
+    w, keep = _host_weights(weights, cfg)
+    out = ctypes.c_void_p()
+    st = lib().tp_block_shard_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(out))
+    del keep
+    _check(st)
+    return TpBlockShard(out.value, cfg)
+
+
+def tp_block_shard_destroy(shard: TpBlockShard) -> None:
+    shard.close()
+
+
+def tp_colwise_linear(shard: TpBlockShard, layer: int, tokens: int, x, y, stream=None) -> None:
+    n = {TP_QKV: 3 * shard.d_r, TP_MLP_UP: shard.f_r}.get(layer, 0)
+    xp, ldx = _mat(x, "x", tokens, shard.hidden, shard.dtype)
+    yp, ldy = _mat(y, "y", tokens, n, shard.dtype)
+    _check(lib().tp_colwise_linear(shard.handle, layer, tokens, xp, ldx, yp, ldy, _stream(stream)))
+
+
+def tp_colwise_qkv_up(shard: TpBlockShard, tokens: int, x, qkv, h, stream=None) -> None:
+    xp, ldx = _mat(x, "x", tokens, shard.hidden, shard.dtype)
+    qp, ldq = _mat(qkv, "qkv", tokens, 3 * shard.d_r, shard.dtype)
+    hp, ldh = _mat(h, "h", tokens, shard.f_r, shard.dtype)
+    _check(lib().tp_colwise_qkv_up(shard.handle, tokens, xp, ldx, qp, ldq, hp, ldh,
+                                   _stream(stream)))
+
+
+def tp_attn_heads(shard: TpBlockShard, tokens: int, qkv, o, stream=None) -> None:
+    qp, ldq = _mat(qkv, "qkv", tokens, 3 * shard.d_r, shard.dtype)
+    op, ldo = _mat(o, "o", tokens, shard.d_r, shard.dtype)
+    _check(lib().tp_attn_heads(shard.handle, tokens, qp, ldq, op, ldo, _stream(stream)))
+
+
+def tp_rowwise_linear_partial(shard: TpBlockShard, layer: int, tokens: int, x_local, partial,
+                              accumulate: bool = False, stream=None) -> None:
+    k = {TP_ATTN_OUT: shard.d_r, TP_MLP_DOWN: shard.f_r,
+         TP_BLOCK_OUT: shard.d_r + shard.f_r}.get(layer, 0)
+    xp, ldx = _mat(x_local, "x_local", tokens, k, shard.dtype)
+    pp, ldp = _mat(partial, "partial", tokens, shard.hidden, TP_F32)
+    _check(lib().tp_rowwise_linear_partial(shard.handle, layer, tokens, xp, ldx, pp, ldp,
+                                           1 if accumulate else 0, _stream(stream)))
+
+
+def tp_partial_reduce(partials: Sequence, biases: Sequence, out, stream=None) -> None:
+    """out = sum(partials) + sum(biases); partials [T, D] fp32 sharing one row
+    stride, biases fp32 [D]."""
+    if len(partials) == 0:
+        raise ValueError("no partials")
+    T, D = out.shape
+    ptrs = [_mat(p, "partial", T, D, TP_F32) for p in partials]
+    ldp = ptrs[0][1]
+    if any(ld != ldp for _, ld in ptrs):
+        raise ValueError("partials must share one row stride")
+    for b in biases:
+        if b.dim() != 1 or not b.is_cuda or b.stride(0) != 1 or b.shape[0] < D or _dtype_code(b) != TP_F32:
+            raise ValueError("biases must be contiguous fp32 1-D device tensors of length >= hidden")
+    P = (ctypes.c_void_p * max(1, len(partials)))(*[p for p, _ in ptrs])
+    B = (ctypes.c_void_p * max(1, len(biases)))(*[b.data_ptr() for b in biases])
+    op, ldo = _mat(out, "out", 0, 0, TP_F32)
+    _check(lib().tp_partial_reduce(P, len(partials), ldp, B if biases else None, len(biases),
+                                   T, D, op, ldo, _stream(stream)))

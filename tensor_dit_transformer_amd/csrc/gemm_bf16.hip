@@ -1,0 +1,235 @@
+// bf16 GEMM with fp32 accumulate on gfx950 matrix cores:
+//   C[M, N] = A[M, K] * B[N, K]^T  (+ bias, GELU-tanh, bf16 store | fp32 store | fp32 accumulate)
+//
+// This is the colwise projection (output features = weight dim 0) and the
+// rowwise partial projection (input features = weight dim 1) of the Diffusers
+// tensor-parallelism page, §"Colwise e rowwise": in both cases the rank's
+// weight slice is an nn.Linear [out, in] matrix, so both operands are
+// K-contiguous and the kernel is one "NT" GEMM with different epilogues.
+//
+// Design (gfx950, 64-wide waves, 160 KB LDS per CU):
+//   * 256 threads = 4 waves in a WM x WN grid; each wave owns a
+//     (BM/WM) x (BN/WN) block of C held in accumulation registers as
+//     32x32 tiles of v_mfma_f32_32x32x16_bf16.
+//   * K advances 64 elements (128 bytes per row) per tile.  A and B tiles are
+//     fetched with 16-byte global loads into registers one tile ahead, then
+//     written to a double-buffered LDS tile; one barrier per K tile.
+//   * LDS rows are 128 bytes; the 16-byte chunk of k-group kc of row r lives
+//     at chunk kc ^ (r & 7) ^ ((r >> 3) & 1), so the rows read by one
+//     ds_read_b128 phase fall in distinct banks.
+//   * Workgroup ids are renumbered so each of the 8 XCDs (own L2) walks a
+//     contiguous stretch of a grouped tile order (8 tile rows per group), and
+//     the A/B panels it streams are shared by its neighbours in L2.
+//   * Rows past M / N are clamped on load and masked on store; a K that is not
+//     a multiple of 64 zero-fills the chunks past K (K must be a multiple of 8).
+#include "tp_kernels.h"
+
+namespace tpk {
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kBK = 64;        // K elements per tile
+constexpr int kRowChunks = 8;  // 16-byte chunks per LDS tile row
+constexpr int kGroupM = 8;     // tile rows per group in the tile order
+
+__device__ __forceinline__ int swizzle(int row, int kc) {
+  return kc ^ (row & 7) ^ ((row >> 3) & 1);
+}
+
+// GELU, tanh form: 0.5 u (1 + tanh(z)) = u * sigmoid(2 z) = u / (1 + exp(-2 z)),
+// z = sqrt(2/pi) (u + 0.044715 u^3).
+__device__ __forceinline__ float gelu_tanh(float u) {
+  const float c = 0.7978845608028654f;
+  const float z = c * fmaf(0.044715f * u, u * u, u);
+  return u / (1.0f + __expf(-2.0f * z));
+}
+
+template <int BM, int BN, int WM, int WN, OutKind KIND, bool KTAIL>
+__global__ void __launch_bounds__(kThreads)
+gemm_bf16_nt(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
+  static_assert(WM * WN * 64 == kThreads, "4 waves");
+  constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+  constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
+  constexpr int A_LOADS = BM * kRowChunks / kThreads;
+  constexpr int B_LOADS = BN * kRowChunks / kThreads;
+  constexpr int BUF = (BM + BN) * kRowChunks;  // 16-byte chunks per stage
+  static_assert(TM >= 1 && TN >= 1 && A_LOADS >= 1 && B_LOADS >= 1, "tile shape");
+
+  __shared__ u32x4 smem[2 * BUF];
+
+  // ---- tile coordinates: XCD-contiguous renumbering, then grouped order
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, per = nb >> 3, rem = nb & 7;
+  const int id = xcd * per + min(xcd, rem) + (bid >> 3);
+  const int group = id / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = id - group * kGroupM * tiles_n;
+  const int m0 = (first_m + in_group % gm) * BM;
+  const int n0 = (in_group / gm) * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bf16* __restrict__ A = static_cast<const bf16*>(p.A);
+  const bf16* __restrict__ B = static_cast<const bf16*>(p.B);
+
+  // ---- global -> register staging: thread loads chunk kc of rows r0 + 32 i
+  const int ld_row = tid >> 3, ld_kc = tid & 7;
+  int64_t a_off[A_LOADS], b_off[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i)
+    a_off[i] = (int64_t)min(m0 + ld_row + 32 * i, p.M - 1) * p.lda + ld_kc * 8;
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i)
+    b_off[i] = (int64_t)min(n0 + ld_row + 32 * i, p.N - 1) * p.ldb + ld_kc * 8;
+  // the swizzle of rows ld_row + 32 i does not depend on i
+  const int st_base = ld_row * kRowChunks + swizzle(ld_row, ld_kc);
+
+  u32x4 ra[A_LOADS], rb[B_LOADS];
+  auto gload = [&](int kt) {
+    const int k = kt * kBK;
+    const bool in = !KTAIL || (k + ld_kc * 8 < p.K);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i)
+      ra[i] = in ? *reinterpret_cast<const u32x4*>(A + a_off[i] + k) : zero;
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i)
+      rb[i] = in ? *reinterpret_cast<const u32x4*>(B + b_off[i] + k) : zero;
+  };
+  auto sstore = [&](int buf) {
+    u32x4* sa = smem + buf * BUF;
+    u32x4* sb = sa + BM * kRowChunks;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) sa[st_base + 32 * kRowChunks * i] = ra[i];
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) sb[st_base + 32 * kRowChunks * i] = rb[i];
+  };
+
+  // ---- MFMA operand reads: lane holds row (lane & 31), k-group 2 s + (lane >> 5)
+  const int wm = wave / WN, wn = wave % WN;
+  const int a_row = wm * WTM + (lane & 31);
+  const int b_row = wn * WTN + (lane & 31);
+  const int khalf = lane >> 5;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  auto compute = [&](int buf) {
+    const u32x4* sa = smem + buf * BUF;
+    const u32x4* sb = sa + BM * kRowChunks;
+#pragma unroll
+    for (int s = 0; s < kBK / 16; ++s) {
+      const int kc = 2 * s + khalf;
+      bf16x8 a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        a[i] = __builtin_bit_cast(bf16x8, sa[(a_row + 32 * i) * kRowChunks + swizzle(a_row, kc)]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        b[j] = __builtin_bit_cast(bf16x8, sb[(b_row + 32 * j) * kRowChunks + swizzle(b_row, kc)]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  const int nk = (p.K + kBK - 1) / kBK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    if (more) gload(kt + 1);
+    compute(kt & 1);
+    if (more) sstore((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue.  32x32 accumulator layout: lane holds column (lane & 31)
+  // and rows 8 (e / 4) + 4 (lane >> 5) + (e % 4), e = 0..15.
+  const int col_l = lane & 31;
+  const int row_l = 4 * (lane >> 5);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + wn * WTN + 32 * j + col_l;
+    if (col >= p.N) continue;
+    float bias = 0.0f;
+    if constexpr (KIND != OutKind::F32_ACC) {
+      if (ep.bias) bias = ep.bias[col];
+    }
+    const bool gelu = col >= ep.gelu_from;
+    const bool second = col >= ep.split;
+    const int ocol = second ? col - ep.split : col;
+    const int64_t ld = second ? ep.ld1 : ep.ld0;
+    void* out = second ? ep.out1 : ep.out0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * WTM + 32 * i + 8 * (e >> 2) + row_l + (e & 3);
+        if (row >= p.M) continue;
+        const int64_t off = (int64_t)row * ld + ocol;
+        float v = acc[i][j][e];
+        if constexpr (KIND == OutKind::F32_ACC) {
+          float* o = static_cast<float*>(out) + off;
+          *o = *o + v;
+        } else {
+          v += bias;
+          if (gelu) v = gelu_tanh(v);
+          if constexpr (KIND == OutKind::BF16)
+            static_cast<bf16*>(out)[off] = static_cast<bf16>(v);
+          else
+            static_cast<float*>(out)[off] = v;
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_tile(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
+                       hipStream_t stream) {
+  const int tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
+  const dim3 grid(tm * tn), block(kThreads);
+  const bool ktail = (p.K % kBK) != 0;
+#define TPK_LAUNCH(K_, T_) \
+  hipLaunchKernelGGL((gemm_bf16_nt<BM, BN, WM, WN, K_, T_>), grid, block, 0, stream, p, ep, tm, tn)
+  switch (kind) {
+    case OutKind::BF16:
+      if (ktail) TPK_LAUNCH(OutKind::BF16, true); else TPK_LAUNCH(OutKind::BF16, false);
+      break;
+    case OutKind::F32_STORE:
+      if (ktail) TPK_LAUNCH(OutKind::F32_STORE, true); else TPK_LAUNCH(OutKind::F32_STORE, false);
+      break;
+    case OutKind::F32_ACC:
+      if (ktail) TPK_LAUNCH(OutKind::F32_ACC, true); else TPK_LAUNCH(OutKind::F32_ACC, false);
+      break;
+  }
+#undef TPK_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
+                            hipStream_t stream) {
+  // 256x256 tiles when they give at least one full wave of workgroups on the
+  // 256 CUs; 128x128 otherwise.
+  const long big = (long)((p.M + 255) / 256) * ((p.N + 255) / 256);
+  if (big >= 256) return launch_tile<256, 256, 2, 2>(p, ep, kind, stream);
+  return launch_tile<128, 128, 2, 2>(p, ep, kind, stream);
+}
+
+}  // namespace tpk

@@ -1,0 +1,383 @@
+// Host layer of the C ABI declared in include/tp_shard.h: argument
+// validation, the rank's weight-slice upload, and kernel launches on the
+// caller's stream.  Validation comes first everywhere and nothing is
+// enqueued on error ("raise instead of silently doing something else",
+// Diffusers TP page, §Limitações; "check before loading or splitting any
+// weight", §Restrições e verificação).
+#include "tp_shard.h"
+#include "tp_kernels.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+struct tp_block_shard {
+  tp_block_config cfg;
+  int device;
+  size_t es;        // element size of activations and weights
+  int64_t D, Dr, Fr, Hr, d;
+  bool attn, mlp;
+  int64_t n_col;    // rows of the packed colwise weight: 3 Dr (attention) + Fr (MLP)
+  int64_t up_row0;  // first row of W_up_r in it
+  int64_t k_row;    // columns of the packed rowwise weight: Dr (attention) + Fr (MLP)
+  int64_t dn_col0;  // first column of W_dn_r in it
+  void* w_col;      // [n_col, D]      = [W_q[R_r]; W_k[R_r]; W_v[R_r]; W_up[C_r]]
+  float* b_col;     // [n_col] fp32    = [b_q[R_r]; b_k[R_r]; b_v[R_r]; b_up[C_r]]
+  void* w_row;      // [D, k_row]      = [W_o[:, R_r] | W_dn[:, C_r]]
+};
+
+namespace {
+
+thread_local std::string g_detail;
+
+tp_status fail(tp_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return s;
+}
+
+tp_status hip_fail(hipError_t e, const char* what) {
+  return fail(e == hipErrorOutOfMemory ? TP_ERR_OOM : TP_ERR_HIP, "%s: %s", what,
+              hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A row-major device matrix argument: non-NULL, 16-byte aligned, ld >= width,
+// every row start 16-byte aligned.
+tp_status check_matrix(const char* name, const void* p, int64_t ld, int64_t width, size_t es) {
+  if (!p) return fail(TP_ERR_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(TP_ERR_ARG, "%s is not 16-byte aligned", name);
+  if (ld < width) return fail(TP_ERR_ARG, "ld of %s (%lld) < width %lld", name, (long long)ld,
+                              (long long)width);
+  if ((ld * (int64_t)es) % 16) return fail(TP_ERR_ARG, "ld of %s (%lld) is not a multiple of 16 bytes",
+                                           name, (long long)ld);
+  return TP_OK;
+}
+
+bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + b_bytes && pb < pa + a_bytes;
+}
+
+int64_t span_bytes(int64_t rows, int64_t ld, int64_t width, size_t es) {
+  return rows <= 0 ? 0 : ((rows - 1) * ld + width) * (int64_t)es;
+}
+
+tp_status check_shard(const tp_block_shard* s) {
+  if (!s) return fail(TP_ERR_ARG, "shard is NULL");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != s->device)
+    return fail(TP_ERR_ARG, "current device %d is not the shard's device %d", dev, s->device);
+  return TP_OK;
+}
+
+tp_status check_tokens(int64_t tokens) {
+  if (tokens < 0) return fail(TP_ERR_ARG, "tokens (%lld) < 0", (long long)tokens);
+  if (tokens > INT32_MAX) return fail(TP_ERR_UNSUPPORTED, "tokens (%lld) > 2^31-1", (long long)tokens);
+  return TP_OK;
+}
+
+void widen_bias(std::vector<float>& dst, int64_t at, const void* src, int64_t from, int64_t n,
+                tp_dtype dt) {
+  if (!src) return;  // NULL bias = zero
+  if (dt == TP_F32) {
+    std::memcpy(dst.data() + at, static_cast<const float*>(src) + from, n * sizeof(float));
+  } else {
+    const uint16_t* b = static_cast<const uint16_t*>(src) + from;
+    for (int64_t i = 0; i < n; ++i) {
+      const uint32_t bits = (uint32_t)b[i] << 16;  // exact bf16 -> fp32 widening
+      std::memcpy(&dst[at + i], &bits, 4);
+    }
+  }
+}
+
+void free_shard(tp_block_shard* s) {
+  if (!s) return;
+  if (s->w_col) (void)hipFree(s->w_col);
+  if (s->b_col) (void)hipFree(s->b_col);
+  if (s->w_row) (void)hipFree(s->w_row);
+  delete s;
+}
+
+tp_status launch(const tpk::GemmProblem& p, const tpk::GemmEpilogue& ep, tpk::OutKind kind,
+                 tp_dtype dt, hipStream_t stream) {
+  const hipError_t e = dt == TP_BF16 ? tpk::launch_gemm_bf16(p, ep, kind, stream)
+                                     : tpk::launch_gemm_f32(p, ep, kind, stream);
+  if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_block_weights* w,
+                                       tp_block_shard** out) {
+  if (!out) return fail(TP_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (!cfg || !w) return fail(TP_ERR_ARG, "config or weights is NULL");
+  if (cfg->dtype != TP_F32 && cfg->dtype != TP_BF16)
+    return fail(TP_ERR_ARG, "unknown dtype %d", (int)cfg->dtype);
+  const int64_t P = cfg->tp_degree, r = cfg->rank, D = cfg->hidden, H = cfg->num_heads,
+                d = cfg->head_dim, F = cfg->ffn;
+  if (P < 1 || r < 0 || r >= P)
+    return fail(TP_ERR_ARG, "rank %lld not in [0, tp_degree=%lld)", (long long)r, (long long)P);
+  if (D <= 0 || H < 0 || F < 0) return fail(TP_ERR_ARG, "sizes must be positive");
+  if (H == 0 && F == 0) return fail(TP_ERR_ARG, "neither attention (num_heads) nor MLP (ffn)");
+  if (H > 0 && d <= 0) return fail(TP_ERR_ARG, "head_dim must be positive");
+  if (H > 0) {
+    if (H * d != D)
+      return fail(TP_ERR_DIVISIBILITY, "num_heads*head_dim = %lld != hidden %lld",
+                  (long long)(H * d), (long long)D);
+    if (H % P)
+      return fail(TP_ERR_DIVISIBILITY, "tp_degree %lld does not divide num_heads %lld",
+                  (long long)P, (long long)H);
+    if (D % P)
+      return fail(TP_ERR_DIVISIBILITY, "tp_degree %lld does not divide the Q/K/V blocks (%lld)",
+                  (long long)P, (long long)D);
+  }
+  if (F % P)
+    return fail(TP_ERR_DIVISIBILITY, "tp_degree %lld does not divide ffn %lld", (long long)P,
+                (long long)F);
+  const int64_t Dr = H > 0 ? D / P : 0, Fr = F / P;
+  if (D % 8 || Dr % 8 || Fr % 8)
+    return fail(TP_ERR_UNSUPPORTED, "hidden, hidden/tp and ffn/tp must be multiples of 8");
+  if (H > 0 && (!w->w_q || !w->w_k || !w->w_v || !w->w_o))
+    return fail(TP_ERR_ARG, "attention configured but w_q/w_k/w_v/w_o missing");
+  if (F > 0 && (!w->w_up || !w->w_down))
+    return fail(TP_ERR_ARG, "MLP configured but w_up/w_down missing");
+
+  tp_block_shard* s = new tp_block_shard();
+  s->cfg = *cfg;
+  s->es = cfg->dtype == TP_BF16 ? 2 : 4;
+  s->D = D; s->Dr = Dr; s->Fr = Fr; s->Hr = H / P; s->d = d;
+  s->attn = H > 0; s->mlp = F > 0;
+  s->up_row0 = 3 * Dr;
+  s->n_col = 3 * Dr + Fr;
+  s->dn_col0 = Dr;
+  s->k_row = Dr + Fr;
+  hipError_t e = hipGetDevice(&s->device);
+  if (e != hipSuccess) { free_shard(s); return hip_fail(e, "hipGetDevice"); }
+
+  const size_t es = s->es;
+  if ((e = hipMalloc(&s->w_col, (size_t)(s->n_col * D) * es)) != hipSuccess ||
+      (e = hipMalloc(reinterpret_cast<void**>(&s->b_col), (size_t)s->n_col * sizeof(float))) != hipSuccess ||
+      (e = hipMalloc(&s->w_row, (size_t)(D * s->k_row) * es)) != hipSuccess) {
+    free_shard(s);
+    return hip_fail(e, "hipMalloc of the weight slices");
+  }
+
+  // Colwise slices: contiguous blocks of dim-0 rows, one per packed block.
+  std::vector<float> bias((size_t)s->n_col, 0.0f);
+  char* wc = static_cast<char*>(s->w_col);
+  const size_t row_bytes = (size_t)D * es;
+  auto put_rows = [&](const void* src, int64_t src_row0, int64_t nrows, int64_t dst_row0) {
+    return hipMemcpy(wc + dst_row0 * row_bytes,
+                     static_cast<const char*>(src) + src_row0 * row_bytes, nrows * row_bytes,
+                     hipMemcpyHostToDevice);
+  };
+  if (s->attn) {
+    const void* ws[3] = {w->w_q, w->w_k, w->w_v};
+    const void* bs[3] = {w->b_q, w->b_k, w->b_v};
+    for (int b = 0; b < 3 && e == hipSuccess; ++b) {
+      e = put_rows(ws[b], r * Dr, Dr, b * Dr);
+      widen_bias(bias, b * Dr, bs[b], r * Dr, Dr, cfg->dtype);
+    }
+  }
+  if (e == hipSuccess && s->mlp) {
+    e = put_rows(w->w_up, r * Fr, Fr, s->up_row0);
+    widen_bias(bias, s->up_row0, w->b_up, r * Fr, Fr, cfg->dtype);
+  }
+  if (e == hipSuccess)
+    e = hipMemcpy(s->b_col, bias.data(), bias.size() * sizeof(float), hipMemcpyHostToDevice);
+  // Rowwise slices: dim-1 column blocks, copied as strided 2-D regions.
+  char* wr = static_cast<char*>(s->w_row);
+  const size_t dpitch = (size_t)s->k_row * es;
+  if (e == hipSuccess && s->attn)
+    e = hipMemcpy2D(wr, dpitch, static_cast<const char*>(w->w_o) + r * Dr * es, (size_t)(H * d) * es,
+                    (size_t)Dr * es, (size_t)D, hipMemcpyHostToDevice);
+  if (e == hipSuccess && s->mlp)
+    e = hipMemcpy2D(wr + s->dn_col0 * es, dpitch, static_cast<const char*>(w->w_down) + r * Fr * es,
+                    (size_t)F * es, (size_t)Fr * es, (size_t)D, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    free_shard(s);
+    return hip_fail(e, "weight slice upload");
+  }
+  *out = s;
+  return TP_OK;
+}
+
+TP_API void tp_block_shard_destroy(tp_block_shard* shard) { free_shard(shard); }
+
+TP_API tp_status tp_colwise_linear(tp_block_shard* s, tp_layer layer, int64_t tokens, const void* x,
+                                   int64_t ldx, void* y, int64_t ldy, void* stream) {
+  tp_status st = check_shard(s);
+  if (st != TP_OK) return st;
+  int64_t row0, n;
+  int gelu_from;
+  if (layer == TP_QKV) {
+    if (!s->attn) return fail(TP_ERR_ARG, "TP_QKV: shard has no attention layers");
+    row0 = 0; n = 3 * s->Dr; gelu_from = (int)n;
+  } else if (layer == TP_MLP_UP) {
+    if (!s->mlp) return fail(TP_ERR_ARG, "TP_MLP_UP: shard has no MLP layers");
+    row0 = s->up_row0; n = s->Fr; gelu_from = 0;
+  } else {
+    return fail(TP_ERR_ARG, "layer %d is not colwise (TP_QKV or TP_MLP_UP)", (int)layer);
+  }
+  if ((st = check_tokens(tokens)) != TP_OK) return st;
+  if ((st = check_matrix("x", x, ldx, s->D, s->es)) != TP_OK) return st;
+  if ((st = check_matrix("y", y, ldy, n, s->es)) != TP_OK) return st;
+  if (tokens == 0) return TP_OK;
+  const tpk::GemmProblem p{x, ldx, static_cast<const char*>(s->w_col) + row0 * s->D * s->es, s->D,
+                           (int)tokens, (int)n, (int)s->D};
+  const tpk::GemmEpilogue ep{s->b_col + row0, gelu_from, (int)n, y, ldy, nullptr, 0};
+  return launch(p, ep, s->cfg.dtype == TP_BF16 ? tpk::OutKind::BF16 : tpk::OutKind::F32_STORE,
+                s->cfg.dtype, static_cast<hipStream_t>(stream));
+}
+
+TP_API tp_status tp_colwise_qkv_up(tp_block_shard* s, int64_t tokens, const void* x, int64_t ldx,
+                                   void* qkv, int64_t ldqkv, void* h, int64_t ldh, void* stream) {
+  tp_status st = check_shard(s);
+  if (st != TP_OK) return st;
+  if (!s->attn || !s->mlp) return fail(TP_ERR_ARG, "tp_colwise_qkv_up needs attention and MLP");
+  if ((st = check_tokens(tokens)) != TP_OK) return st;
+  if ((st = check_matrix("x", x, ldx, s->D, s->es)) != TP_OK) return st;
+  if ((st = check_matrix("qkv", qkv, ldqkv, 3 * s->Dr, s->es)) != TP_OK) return st;
+  if ((st = check_matrix("h", h, ldh, s->Fr, s->es)) != TP_OK) return st;
+  if (tokens == 0) return TP_OK;
+  if (overlap(qkv, span_bytes(tokens, ldqkv, 3 * s->Dr, s->es), h, span_bytes(tokens, ldh, s->Fr, s->es)))
+    return fail(TP_ERR_ARG, "qkv and h overlap");
+  const int split = (int)(3 * s->Dr);
+  const tpk::GemmProblem p{x, ldx, s->w_col, s->D, (int)tokens, (int)s->n_col, (int)s->D};
+  const tpk::GemmEpilogue ep{s->b_col, split, split, qkv, ldqkv, h, ldh};
+  return launch(p, ep, s->cfg.dtype == TP_BF16 ? tpk::OutKind::BF16 : tpk::OutKind::F32_STORE,
+                s->cfg.dtype, static_cast<hipStream_t>(stream));
+}
+
+TP_API tp_status tp_attn_heads(tp_block_shard* s, int64_t tokens, const void* qkv, int64_t ldqkv,
+                               void* o, int64_t ldo, void* stream) {
+  tp_status st = check_shard(s);
+  if (st != TP_OK) return st;
+  if (!s->attn) return fail(TP_ERR_ARG, "shard has no attention layers");
+  if (s->cfg.dtype != TP_BF16) return fail(TP_ERR_UNSUPPORTED, "attention is built for bf16 only");
+  if (s->d != 128) return fail(TP_ERR_UNSUPPORTED, "attention is built for head_dim 128 only");
+  if ((st = check_tokens(tokens)) != TP_OK) return st;
+  if ((st = check_matrix("qkv", qkv, ldqkv, 3 * s->Dr, s->es)) != TP_OK) return st;
+  if ((st = check_matrix("o", o, ldo, s->Dr, s->es)) != TP_OK) return st;
+  if (tokens == 0) return TP_OK;
+  if (overlap(qkv, span_bytes(tokens, ldqkv, 3 * s->Dr, s->es), o, span_bytes(tokens, ldo, s->Dr, s->es)))
+    return fail(TP_ERR_ARG, "o overlaps qkv");
+  const hipError_t e = tpk::launch_attn_fwd_bf16_d128(qkv, ldqkv, o, ldo, (int)tokens, (int)s->Hr,
+                                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return TP_OK;
+}
+
+TP_API tp_status tp_rowwise_linear_partial(tp_block_shard* s, tp_layer layer, int64_t tokens,
+                                           const void* x_local, int64_t ldx, float* partial,
+                                           int64_t ldp, int accumulate, void* stream) {
+  tp_status st = check_shard(s);
+  if (st != TP_OK) return st;
+  int64_t col0, k;
+  if (layer == TP_ATTN_OUT) {
+    if (!s->attn) return fail(TP_ERR_ARG, "TP_ATTN_OUT: shard has no attention layers");
+    col0 = 0; k = s->Dr;
+  } else if (layer == TP_MLP_DOWN) {
+    if (!s->mlp) return fail(TP_ERR_ARG, "TP_MLP_DOWN: shard has no MLP layers");
+    col0 = s->dn_col0; k = s->Fr;
+  } else if (layer == TP_BLOCK_OUT) {
+    if (!s->attn || !s->mlp) return fail(TP_ERR_ARG, "TP_BLOCK_OUT needs attention and MLP");
+    col0 = 0; k = s->k_row;
+  } else {
+    return fail(TP_ERR_ARG, "layer %d is not rowwise", (int)layer);
+  }
+  if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_ARG, "accumulate must be 0 or 1");
+  if ((st = check_tokens(tokens)) != TP_OK) return st;
+  if ((st = check_matrix("x_local", x_local, ldx, k, s->es)) != TP_OK) return st;
+  if ((st = check_matrix("partial", partial, ldp, s->D, sizeof(float))) != TP_OK) return st;
+  if (tokens == 0) return TP_OK;
+  if (overlap(x_local, span_bytes(tokens, ldx, k, s->es), partial,
+              span_bytes(tokens, ldp, s->D, sizeof(float))))
+    return fail(TP_ERR_ARG, "partial overlaps x_local");
+  const tpk::GemmProblem p{x_local, ldx, static_cast<const char*>(s->w_row) + col0 * s->es, s->k_row,
+                           (int)tokens, (int)s->D, (int)k};
+  const tpk::GemmEpilogue ep{nullptr, (int)s->D, (int)s->D, partial, ldp, nullptr, 0};
+  return launch(p, ep, accumulate ? tpk::OutKind::F32_ACC : tpk::OutKind::F32_STORE, s->cfg.dtype,
+                static_cast<hipStream_t>(stream));
+}
+
+TP_API tp_status tp_partial_reduce(const float* const* partials, int32_t n_partials, int64_t ldp,
+                                   const float* const* biases, int32_t n_biases, int64_t tokens,
+                                   int64_t hidden, float* out, int64_t ldo, void* stream) {
+  if (!partials) return fail(TP_ERR_ARG, "partials is NULL");
+  if (n_partials < 1) return fail(TP_ERR_ARG, "n_partials (%d) < 1", n_partials);
+  if (n_partials > tpk::kMaxReducePartials)
+    return fail(TP_ERR_UNSUPPORTED, "n_partials (%d) > %d", n_partials, tpk::kMaxReducePartials);
+  if (n_biases < 0) return fail(TP_ERR_ARG, "n_biases (%d) < 0", n_biases);
+  if (n_biases > tpk::kMaxReduceBiases)
+    return fail(TP_ERR_UNSUPPORTED, "n_biases (%d) > %d", n_biases, tpk::kMaxReduceBiases);
+  if (n_biases > 0 && !biases) return fail(TP_ERR_ARG, "biases is NULL");
+  tp_status st = check_tokens(tokens);
+  if (st != TP_OK) return st;
+  if (hidden <= 0 || hidden % 4) return fail(TP_ERR_ARG, "hidden (%lld) must be a positive multiple of 4",
+                                            (long long)hidden);
+  if (tokens * (hidden / 4) >= ((int64_t)1 << 31))
+    return fail(TP_ERR_UNSUPPORTED, "tokens*hidden/4 >= 2^31");
+  tpk::ReduceArgs a{};
+  for (int i = 0; i < n_partials; ++i) {
+    if ((st = check_matrix("partials[i]", partials[i], ldp, hidden, sizeof(float))) != TP_OK) return st;
+    a.partials[i] = partials[i];
+  }
+  for (int i = 0; i < n_biases; ++i) {
+    if (!biases[i]) return fail(TP_ERR_ARG, "biases[%d] is NULL", i);
+    if (!aligned16(biases[i])) return fail(TP_ERR_ARG, "biases[%d] is not 16-byte aligned", i);
+    a.biases[i] = biases[i];
+  }
+  if ((st = check_matrix("out", out, ldo, hidden, sizeof(float))) != TP_OK) return st;
+  if (tokens == 0) return TP_OK;
+  const int64_t ob = span_bytes(tokens, ldo, hidden, sizeof(float));
+  for (int i = 0; i < n_partials; ++i) {
+    const bool same = partials[i] == out && ldp == ldo;
+    if (overlap(out, ob, partials[i], span_bytes(tokens, ldp, hidden, sizeof(float))) && !(i == 0 && same))
+      return fail(TP_ERR_ARG, "out overlaps partials[%d] (only exact aliasing of partials[0] is allowed)", i);
+  }
+  for (int i = 0; i < n_biases; ++i)
+    if (overlap(out, ob, biases[i], hidden * (int64_t)sizeof(float)))
+      return fail(TP_ERR_ARG, "out overlaps biases[%d]", i);
+  a.n_partials = n_partials;
+  a.n_biases = n_biases;
+  a.rows = tokens;
+  a.cols = hidden;
+  a.ldp = ldp;
+  a.ldo = ldo;
+  a.out = out;
+  const hipError_t e = tpk::launch_partial_reduce(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "reduce launch");
+  return TP_OK;
+}
+
+TP_API const char* tp_status_string(tp_status status) {
+  switch (status) {
+    case TP_OK: return "TP_OK";
+    case TP_ERR_ARG: return "TP_ERR_ARG: invalid argument";
+    case TP_ERR_DIVISIBILITY: return "TP_ERR_DIVISIBILITY: tp_degree does not divide a sharded dimension";
+    case TP_ERR_UNSUPPORTED: return "TP_ERR_UNSUPPORTED: combination not built";
+    case TP_ERR_HIP: return "TP_ERR_HIP: HIP runtime error";
+    case TP_ERR_OOM: return "TP_ERR_OOM: device allocation failed";
+  }
+  return "unknown tp_status";
+}
+
+TP_API const char* tp_last_error_detail(void) { return g_detail.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Internal interface between the host layer (shard.hip) and the gfx950
+// kernels.  Not part of the public ABI (include/tp_shard.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace tpk {
+
+// What the GEMM epilogue does with each fp32 accumulator.
+enum class OutKind : int {
+  BF16 = 0,       // (+bias, GELU on a column range) -> bf16 store
+  F32_STORE = 1,  // (+bias, GELU on a column range) -> fp32 store
+  F32_ACC = 2,    // fp32 read-add-write (rowwise partial accumulate), no bias
+};
+
+// C[M, N] = A[M, K] * B[N, K]^T: both operands K-contiguous (x in [T, K],
+// weights in the nn.Linear [out, in] layout).
+struct GemmProblem {
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  int M, N, K;
+};
+
+// Output columns n < split go to out0[:, n], columns n >= split to
+// out1[:, n - split] (two tensors written by one launch: the packed
+// QKV+up colwise projection).  Columns n >= gelu_from get GELU-tanh after
+// the bias.  bias is fp32 [N] or nullptr.
+struct GemmEpilogue {
+  const float* bias;
+  int gelu_from;
+  int split;
+  void* out0;
+  int64_t ld0;
+  void* out1;
+  int64_t ld1;
+};
+
+hipError_t launch_gemm_bf16(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
+                            hipStream_t stream);
+hipError_t launch_gemm_f32(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
+                           hipStream_t stream);
+
+// Non-causal multi-head attention, bf16 in/out, head_dim 128, fp32 softmax.
+// qkv: [T, 3*Dr] (Q | K | V, head j at columns j*128 of each block);
+// o: [T, Dr].
+hipError_t launch_attn_fwd_bf16_d128(const void* qkv, int64_t ldqkv, void* o, int64_t ldo,
+                                     int T, int heads, hipStream_t stream);
+
+constexpr int kMaxReducePartials = 16;
+constexpr int kMaxReduceBiases = 4;
+
+struct ReduceArgs {
+  const float* partials[kMaxReducePartials];
+  const float* biases[kMaxReduceBiases];
+  int n_partials;
+  int n_biases;
+  int64_t rows;
+  int64_t cols;      // multiple of 4
+  int64_t ldp;
+  int64_t ldo;
+  float* out;
+};
+
+hipError_t launch_partial_reduce(const ReduceArgs& a, hipStream_t stream);
+
+}  // namespace tpk

@@ -1,0 +1,185 @@
+"""The C-ABI library without a GPU: it loads, exports exactly the symbols the
+header declares, and rejects invalid requests before any HIP call (so these
+run on a host with no device).  Validation order and codes follow the
+Diffusers TP page, §Restrições e verificação (tp_degree divides the heads and
+every packed block, checked before any weight is touched) and §Limitações
+(an error, never a silent fallback)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+import tensor_dit_transformer_amd as tp
+from tensor_dit_transformer_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_shard.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tp.LIB_PATH):
+        from tensor_dit_transformer_amd import build
+        build.build(verbose=False)
+    return tp.lib()
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^TP_API[^(]*?\b(tp_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    syms = header_symbols()
+    assert syms == sorted(binding.EXPORTED)
+
+
+def test_library_exports_exactly_the_header_symbols(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", tp.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines()
+                       if l.split() and l.split()[-2] in ("T", "W") and not l.split()[-1].startswith("_")})
+    assert exported == header_symbols()
+    for s in header_symbols():
+        assert hasattr(L, s)
+
+
+def _create(L, cfg, weights=None):
+    w = tp.TpBlockWeights()
+    keep = []
+    for k, a in (weights or {}).items():
+        keep.append(a)
+        setattr(w, k, a.ctypes.data)
+    out = ctypes.c_void_p(12345)
+    st = L.tp_block_shard_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(out))
+    return st, out.value
+
+
+def _tiny_weights(D, H, d, F, dtype=np.uint16):
+    HD = H * d
+    w = {}
+    if H:
+        for k in ("w_q", "w_k", "w_v"):
+            w[k] = np.zeros((HD, D), dtype)
+        w["w_o"] = np.zeros((D, HD), dtype)
+    if F:
+        w["w_up"] = np.zeros((F, D), dtype)
+        w["w_down"] = np.zeros((D, F), dtype)
+    return w
+
+
+@pytest.mark.parametrize("P,r,D,H,d,F,want", [
+    (5, 0, 24 * 8, 24, 8, 0, tp.TP_ERR_DIVISIBILITY),     # P does not divide the heads
+    (4, 0, 24 * 8, 24, 8, 1022, tp.TP_ERR_DIVISIBILITY),  # ... nor the FFN width
+    (2, 0, 100, 4, 8, 0, tp.TP_ERR_DIVISIBILITY),         # heads * head_dim != hidden
+    (4, 4, 32, 4, 8, 64, tp.TP_ERR_ARG),                  # rank out of range
+    (4, -1, 32, 4, 8, 64, tp.TP_ERR_ARG),
+    (0, 0, 32, 4, 8, 64, tp.TP_ERR_ARG),                  # tp_degree < 1
+    (1, 0, 32, 0, 0, 0, tp.TP_ERR_ARG),                   # neither attention nor MLP
+    (1, 0, 0, 0, 0, 64, tp.TP_ERR_ARG),                   # hidden <= 0
+    (2, 0, 36, 0, 0, 64, tp.TP_ERR_UNSUPPORTED),          # hidden not a multiple of 8
+    (4, 0, 64, 0, 0, 40, tp.TP_ERR_UNSUPPORTED),          # ffn / tp not a multiple of 8
+])
+def test_create_rejects_before_touching_weights(L, P, r, D, H, d, F, want):
+    # No weights at all: the checks that fail must come before any weight is read.
+    st, out = _create(L, tp.make_config(P, r, D, H, d, F, tp.TP_BF16))
+    assert st == want, tp.tp_last_error_detail()
+    assert out is None
+    assert tp.tp_last_error_detail()
+
+
+def test_create_rejects_missing_weights_and_nulls(L):
+    st, out = _create(L, tp.make_config(2, 0, 32, 4, 8, 64, tp.TP_BF16))
+    assert st == tp.TP_ERR_ARG and out is None and "missing" in tp.tp_last_error_detail()
+    w = tp.TpBlockWeights()
+    assert L.tp_block_shard_create(None, ctypes.byref(w), ctypes.byref(ctypes.c_void_p())) == tp.TP_ERR_ARG
+    cfg = tp.make_config(2, 0, 32, 4, 8, 64, tp.TP_BF16)
+    assert L.tp_block_shard_create(ctypes.byref(cfg), None, ctypes.byref(ctypes.c_void_p())) == tp.TP_ERR_ARG
+    assert L.tp_block_shard_create(ctypes.byref(cfg), ctypes.byref(w), None) == tp.TP_ERR_ARG
+    cfg.dtype = 7
+    st, _ = _create(L, cfg, _tiny_weights(32, 4, 8, 64))
+    assert st == tp.TP_ERR_ARG
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 5, 6, 8, 12, 24])
+@pytest.mark.parametrize("H,F", [(24, 24 * 8 * 4), (24, 1000), (12, 0), (0, 96)])
+def test_create_agrees_with_oracle_constraints(L, P, H, F):
+    """The library's accept/reject decision matches the oracle's constraint
+    check (sizes chosen so every accepted case also meets the 8-alignment)."""
+    d = 8
+    D = H * d if H else 192
+    try:
+        O.check_config(P, 0, D, H, d, F)
+        oracle_kind = None
+    except O.ShardConfigError as e:
+        oracle_kind = e.kind
+    st, out = _create(L, tp.make_config(P, 0, D, H, d, F, tp.TP_BF16), _tiny_weights(D, H, d, F))
+    if out:
+        L.tp_block_shard_destroy(out)
+    if oracle_kind == "divisibility":
+        assert st == tp.TP_ERR_DIVISIBILITY
+    elif oracle_kind == "argument":
+        assert st == tp.TP_ERR_ARG
+    else:
+        # accepted: either created (device present) or failed in the HIP runtime,
+        # or a multiple-of-8 requirement of this library
+        assert st in (tp.TP_OK, tp.TP_ERR_HIP, tp.TP_ERR_UNSUPPORTED, tp.TP_ERR_OOM)
+        if st == tp.TP_ERR_UNSUPPORTED:
+            assert (D // P) % 8 or (F // P) % 8
+
+
+def test_calls_reject_null_shard(L):
+    vp = ctypes.c_void_p(0x10000)
+    assert L.tp_colwise_linear(None, tp.TP_QKV, 8, vp, 64, vp, 64, None) == tp.TP_ERR_ARG
+    assert L.tp_colwise_qkv_up(None, 8, vp, 64, vp, 64, vp, 64, None) == tp.TP_ERR_ARG
+    assert L.tp_attn_heads(None, 8, vp, 64, vp, 64, None) == tp.TP_ERR_ARG
+    assert L.tp_rowwise_linear_partial(None, tp.TP_BLOCK_OUT, 8, vp, 64, vp, 64, 0, None) == tp.TP_ERR_ARG
+    L.tp_block_shard_destroy(None)  # ignored
+
+
+def _reduce(L, parts, n_p, ldp, biases, n_b, T, D, out, ldo):
+    P = (ctypes.c_void_p * max(1, len(parts)))(*parts)
+    B = (ctypes.c_void_p * max(1, len(biases)))(*biases) if biases is not None else None
+    return L.tp_partial_reduce(P, n_p, ldp, B, n_b, T, D, out, ldo, None)
+
+
+def test_reduce_validation_without_device(L):
+    a, b, c, o = 0x100000, 0x200000, 0x300000, 0x400000   # never dereferenced
+    ok = dict(parts=[a, b], n_p=2, ldp=64, biases=[c], n_b=1, T=0, D=64, out=o, ldo=64)
+    assert _reduce(L, **ok) == tp.TP_OK                           # tokens == 0: no-op
+    assert _reduce(L, **{**ok, "n_p": 0}) == tp.TP_ERR_ARG
+    assert _reduce(L, **{**ok, "n_p": 17}) == tp.TP_ERR_UNSUPPORTED
+    assert _reduce(L, **{**ok, "n_b": 5}) == tp.TP_ERR_UNSUPPORTED
+    assert _reduce(L, **{**ok, "n_b": -1}) == tp.TP_ERR_ARG
+    assert _reduce(L, **{**ok, "biases": None}) == tp.TP_ERR_ARG
+    assert _reduce(L, **{**ok, "T": -1}) == tp.TP_ERR_ARG
+    assert _reduce(L, **{**ok, "D": 62, "ldp": 64, "ldo": 64}) == tp.TP_ERR_ARG  # hidden % 4
+    assert _reduce(L, **{**ok, "parts": [a + 8, b]}) == tp.TP_ERR_ARG            # misaligned
+    assert _reduce(L, **{**ok, "parts": [0, b]}) == tp.TP_ERR_ARG                # NULL
+    assert _reduce(L, **{**ok, "ldp": 60}) == tp.TP_ERR_ARG                      # ld < width
+    assert _reduce(L, **{**ok, "ldo": 66}) == tp.TP_ERR_ARG                      # 16-byte rows
+    assert _reduce(L, **{**ok, "out": 0}) == tp.TP_ERR_ARG
+    # overlap: out on top of partials[1] is rejected; exact alias of partials[0] is allowed
+    live = {**ok, "T": 4}
+    assert _reduce(L, **{**live, "out": b}) == tp.TP_ERR_ARG
+    assert _reduce(L, **{**live, "out": c - 64}) == tp.TP_ERR_ARG                # covers the bias
+    assert "overlap" in tp.tp_last_error_detail()
+
+
+def test_status_strings(L):
+    for code in (tp.TP_OK, tp.TP_ERR_ARG, tp.TP_ERR_DIVISIBILITY, tp.TP_ERR_UNSUPPORTED,
+                 tp.TP_ERR_HIP, tp.TP_ERR_OOM):
+        assert tp.tp_status_string(code).startswith("TP_")
+    assert tp.tp_status_string(42) == "unknown tp_status"
+
+
+def test_binding_raises_with_detail(L):
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_block_shard_create(tp.make_config(5, 0, 192, 24, 8, 0, tp.TP_BF16),
+                                 _tiny_weights(192, 24, 8, 0))
+    assert e.value.status == tp.TP_ERR_DIVISIBILITY
+    assert "divide" in str(e.value)

@@ -1,0 +1,283 @@
+"""GPU parity: every output of the C ABI (qkv_r, o_r, h_r, partial_r and the
+reduced y) against the float64 CPU oracle on the same seeded inputs, at the
+tolerance max|gpu - ref| / max|ref| <= 1e-4 (fp32) or 2e-2 (bf16).
+
+The check recipe is the Diffusers TP page's own (§Restrições e verificação):
+run the same seeded inputs unsharded and under tensor parallelism and compare
+numerically, since a misplaced colwise/rowwise still runs.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import tensor_dit_transformer_amd as tp
+import tp_harness as H
+import tp_inputs
+from tp_inputs import Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def full_oracle(w: Workload, inp):
+    vals = inp.values
+    bf16 = w.dtype == "bf16"
+    ranks = [O.rank_forward(vals["x"], vals, w.tp_degree, r, w.num_heads, w.head_dim, bf16)
+             for r in range(w.tp_degree)]
+    y = O.partial_reduce([r["p_block"] for r in ranks], O.rowwise_bias(vals))
+    return ranks, y
+
+
+def run_all_ranks(w: Workload, inp, fused=True):
+    shards = H.create_shards(w, inp)
+    x = H.to_device(inp, "x")
+    T = w.tokens
+    outs = []
+    partials = []
+    for s in shards:
+        buf = H.RankBuffers(s, T)
+        H.run_rank(s, x, buf, fused=fused)
+        partials.append(buf.partial)
+        outs.append(buf)
+    y = torch.empty((T, w.hidden), dtype=torch.float32, device="cuda")
+    tp.tp_partial_reduce(partials, H.rowwise_biases(w, inp), y)
+    torch.cuda.synchronize()
+    return shards, outs, y
+
+
+def close_all(shards):
+    torch.cuda.synchronize()
+    for s in shards:
+        s.close()
+
+
+def check_rank(w, buf, ref, tol, what=""):
+    errs = {}
+    if buf.qkv is not None:
+        errs["qkv_r"] = H.rel_err(H.as_f64(buf.qkv), ref["qkv_r"])
+        errs["o_r"] = H.rel_err(H.as_f64(buf.o), ref["o_r"])
+    if buf.h is not None:
+        errs["h_r"] = H.rel_err(H.as_f64(buf.h), ref["h_r"])
+    errs["partial_r"] = H.rel_err(H.as_f64(buf.partial), ref["p_block"])
+    say(what, {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= tol, f"{what} {k}: {v:.3e} > {tol}"
+
+
+# ------------------------------------------------------------------ small/mid, full compare
+
+def test_c1_fp32_mlp_both_ranks_reduce_equals_unsharded():
+    w = tp_inputs.C1
+    inp = tp_inputs.make_inputs(w, seed=0)
+    ranks, y_ref = full_oracle(w, inp)
+    unsharded = O.block_unsharded(inp["x"], inp.values, 0, 0, bf16=False)["y"]
+    shards, outs, y = run_all_ranks(w, inp)
+    for r, (buf, ref) in enumerate(zip(outs, ranks)):
+        check_rank(w, buf, ref, H.TOL["f32"], f"C1 rank {r}")
+    e = H.rel_err(H.as_f64(y), unsharded)
+    say("C1 y vs unsharded", e)
+    assert e <= H.TOL["f32"]
+    assert H.rel_err(H.as_f64(y), y_ref) <= H.TOL["f32"]
+    close_all(shards)
+
+
+MID = Workload("mid_block_T777_D512_H4_F2048_P2", 777, 512, 4, 128, 2048, 2, "bf16")
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_mid_bf16_block_ragged_all_outputs(fused):
+    w = MID
+    inp = tp_inputs.make_inputs(w, seed=3)
+    ranks, y_ref = full_oracle(w, inp)
+    shards, outs, y = run_all_ranks(w, inp, fused=fused)
+    for r, (buf, ref) in enumerate(zip(outs, ranks)):
+        check_rank(w, buf, ref, H.TOL["bf16"], f"MID rank {r} fused={fused}")
+    unsharded = O.block_unsharded(inp["x"], inp.values, w.num_heads, w.head_dim, bf16=True)["y"]
+    e = H.rel_err(H.as_f64(y), unsharded)
+    say("MID y vs unsharded", e)
+    assert e <= H.TOL["bf16"]
+    close_all(shards)
+
+
+def test_fused_qkv_up_is_bitwise_equal_to_separate_calls():
+    w = MID
+    inp = tp_inputs.make_inputs(w, seed=4)
+    shards, a, _ = run_all_ranks(w, inp, fused=True)
+    close_all(shards)
+    shards, b, _ = run_all_ranks(w, inp, fused=False)
+    for x, z in zip(a, b):
+        assert torch.equal(x.qkv, z.qkv)
+        assert torch.equal(x.oh, z.oh)
+    close_all(shards)
+
+
+def test_block_out_equals_attn_out_plus_mlp_down_accumulate():
+    w = MID
+    inp = tp_inputs.make_inputs(w, seed=5)
+    shards, outs, _ = run_all_ranks(w, inp)
+    s, buf = shards[1], outs[1]
+    T = w.tokens
+    p2 = torch.empty_like(buf.partial)
+    tp.tp_rowwise_linear_partial(s, tp.TP_ATTN_OUT, T, buf.o, p2)
+    tp.tp_rowwise_linear_partial(s, tp.TP_MLP_DOWN, T, buf.h, p2, accumulate=True)
+    torch.cuda.synchronize()
+    assert H.rel_err(H.as_f64(p2), H.as_f64(buf.partial)) < 1e-5
+    close_all(shards)
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 129, 300])
+def test_small_and_ragged_token_counts(T):
+    w = Workload(f"small_T{T}", T, 256, 2, 128, 512, 2, "bf16")
+    inp = tp_inputs.make_inputs(w, seed=T)
+    ranks, y_ref = full_oracle(w, inp)
+    shards, outs, y = run_all_ranks(w, inp)
+    for r, (buf, ref) in enumerate(zip(outs, ranks)):
+        check_rank(w, buf, ref, H.TOL["bf16"], f"T={T} rank {r}")
+    assert H.rel_err(H.as_f64(y), y_ref) <= H.TOL["bf16"]
+    if T == 1:  # one token attends to itself: o = v exactly (softmax weight 1)
+        Dr = shards[0].d_r
+        assert torch.equal(outs[0].o, outs[0].qkv[:, 2 * Dr:])
+    close_all(shards)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_k_not_multiple_of_tile_and_single_rank(dtype):
+    # MLP-only, P = 1 (the shard is the whole layer), K = 264 and 520: both
+    # GEMMs take the zero-filled K-tail path.
+    w = Workload(f"ktail_{dtype}", 200, 264, 0, 0, 520, 1, dtype)
+    inp = tp_inputs.make_inputs(w, seed=11)
+    ranks, y_ref = full_oracle(w, inp)
+    unsharded = O.block_unsharded(inp["x"], inp.values, 0, 0, bf16=dtype == "bf16")["y"]
+    shards, outs, y = run_all_ranks(w, inp)
+    check_rank(w, outs[0], ranks[0], H.TOL[dtype], f"ktail {dtype}")
+    assert H.rel_err(H.as_f64(y), unsharded) <= H.TOL[dtype]
+    close_all(shards)
+
+
+def test_zero_tokens_is_a_no_op():
+    w = Workload("zero", 8, 256, 2, 128, 512, 2, "bf16")
+    inp = tp_inputs.make_inputs(w, seed=1)
+    shards = H.create_shards(w, inp)
+    x = H.to_device(inp, "x")
+    buf = H.RankBuffers(shards[0], 8)
+    for t in (buf.qkv, buf.oh, buf.partial):
+        t.fill_(7)
+    tp.tp_colwise_qkv_up(shards[0], 0, x, buf.qkv, buf.h)
+    tp.tp_colwise_linear(shards[0], tp.TP_QKV, 0, x, buf.qkv)
+    tp.tp_attn_heads(shards[0], 0, buf.qkv, buf.o)
+    tp.tp_rowwise_linear_partial(shards[0], tp.TP_BLOCK_OUT, 0, buf.oh, buf.partial)
+    import ctypes
+    parts = (ctypes.c_void_p * 1)(buf.partial.data_ptr())
+    st = tp.lib().tp_partial_reduce(parts, 1, 256, None, 0, 0, 256, buf.partial.data_ptr(), 256, None)
+    assert st == tp.TP_OK
+    torch.cuda.synchronize()
+    for t in (buf.qkv, buf.oh, buf.partial):
+        assert bool((t.float() == 7).all())
+    close_all(shards)
+
+
+def test_reduce_fp32_exact_rank_order_and_aliasing():
+    rng = np.random.default_rng(9)
+    T, D, P = 1000, 768, 3
+    parts = [rng.standard_normal((T, D)).astype(np.float32) for _ in range(P)]
+    bias = [rng.standard_normal(D).astype(np.float32) * 0.01 for _ in range(2)]
+    ref = O.partial_reduce(parts, bias[0].astype(np.float64) + bias[1])
+    dp = [torch.from_numpy(p).cuda() for p in parts]
+    db = [torch.from_numpy(b).cuda() for b in bias]
+    out = torch.empty((T, D), device="cuda")
+    tp.tp_partial_reduce(dp, db, out)
+    torch.cuda.synchronize()
+    assert H.rel_err(H.as_f64(out), ref) < 1e-6
+    # the fp32 rank-order sum is reproduced exactly by numpy in float32
+    f32 = ((parts[0] + parts[1]) + parts[2]) + bias[0] + bias[1]
+    assert np.array_equal(out.cpu().numpy(), f32)
+    # strided partials and output, and in-place into partials[0]
+    big = torch.zeros((T, D + 64), device="cuda")
+    big[:, :D] = dp[0]
+    tp.tp_partial_reduce([big[:, :D]], db[:1], big[:, :D])
+    torch.cuda.synchronize()
+    assert np.array_equal(big[:, :D].cpu().numpy(), parts[0] + bias[0])
+    assert bool((big[:, D:] == 0).all())
+
+
+def test_deterministic_repeats():
+    w = MID
+    inp = tp_inputs.make_inputs(w, seed=6)
+    shards, first, y0 = run_all_ranks(w, inp)
+    x = H.to_device(inp, "x")
+    for _ in range(5):
+        for s, b0 in zip(shards, first):
+            b = H.RankBuffers(s, w.tokens)
+            H.run_rank(s, x, b)
+            torch.cuda.synchronize()
+            assert torch.equal(b.qkv, b0.qkv) and torch.equal(b.oh, b0.oh)
+            assert torch.equal(b.partial, b0.partial)
+    close_all(shards)
+
+
+def test_side_stream_gives_identical_results():
+    w = MID
+    inp = tp_inputs.make_inputs(w, seed=7)
+    shards, outs, y = run_all_ranks(w, inp)
+    x = H.to_device(inp, "x")
+    st = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        b = H.RankBuffers(shards[0], w.tokens)
+        H.run_rank(shards[0], x, b)
+    st.synchronize()
+    assert torch.equal(b.partial, outs[0].partial)
+    close_all(shards)
+
+
+def test_call_errors_enqueue_nothing():
+    w = MID
+    inp = tp_inputs.make_inputs(w, seed=8, tokens=64)
+    shards = H.create_shards(dataclass_tokens(w, 64), inp)
+    s = shards[0]
+    x = H.to_device(inp, "x")
+    buf = H.RankBuffers(s, 64)
+    buf.partial.fill_(3)
+    with pytest.raises(tp.TpError) as e:             # colwise call with a rowwise layer
+        tp.tp_colwise_linear(s, tp.TP_BLOCK_OUT, 64, x, buf.qkv)
+    assert e.value.status == tp.TP_ERR_ARG
+    raw = torch.empty(64 * 512 + 8, dtype=torch.bfloat16, device="cuda")
+    mis = raw[1:1 + 64 * 512].view(64, 512)          # 2-byte offset: misaligned
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_colwise_linear(s, tp.TP_QKV, 64, mis, buf.qkv)
+    assert e.value.status == tp.TP_ERR_ARG
+    narrow = torch.empty((64, 16), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):                  # the binding checks shapes
+        tp.tp_rowwise_linear_partial(s, tp.TP_BLOCK_OUT, 64, narrow, buf.partial)
+    st = tp.lib().tp_rowwise_linear_partial(s.handle, tp.TP_BLOCK_OUT, 64, narrow.data_ptr(), 16,
+                                            buf.partial.data_ptr(), buf.partial.stride(0), 0, None)
+    assert st == tp.TP_ERR_ARG                       # ld (16) < K_r
+    with pytest.raises(tp.TpError) as e:             # o overlapping qkv
+        tp.tp_attn_heads(s, 64, buf.qkv, buf.qkv[:, :s.d_r])
+    assert e.value.status == tp.TP_ERR_ARG
+    with pytest.raises(tp.TpError) as e:             # tokens < 0
+        tp.tp_attn_heads(s, -1, buf.qkv, buf.o)
+    assert e.value.status == tp.TP_ERR_ARG
+    torch.cuda.synchronize()
+    assert bool((buf.partial == 3).all())
+    f32 = tp_inputs.Workload("f32attn", 64, 256, 2, 128, 0, 1, "f32")
+    i32 = tp_inputs.make_inputs(f32, seed=1)
+    s32 = H.create_shards(f32, i32)[0]
+    b32 = H.RankBuffers(s32, 64)
+    with pytest.raises(tp.TpError) as e:             # fp32 attention is not built
+        tp.tp_attn_heads(s32, 64, b32.qkv, b32.o)
+    assert e.value.status == tp.TP_ERR_UNSUPPORTED
+    close_all(shards + [s32])
+
+
+def dataclass_tokens(w, T):
+    import dataclasses
+    return dataclasses.replace(w, tokens=T)

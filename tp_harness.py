@@ -1,0 +1,98 @@
+"""Harness shared by the GPU tests, the smoke check and the benchmark: upload
+seeded inputs, create the P rank shards through the C ABI, and run one rank's
+hot path (all through tensor_dit_transformer_amd; no arithmetic here)."""
+from __future__ import annotations
+
+from typing import Dict, List
+
+import numpy as np
+import torch
+
+import tensor_dit_transformer_amd as tp
+import tp_inputs
+
+
+def to_device(inp: tp_inputs.Inputs, name: str) -> torch.Tensor:
+    if inp.bits is not None:
+        return torch.from_numpy(inp.bits[name].view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(inp.values[name])).cuda()
+
+
+def host_weights(inp: tp_inputs.Inputs) -> Dict[str, np.ndarray]:
+    src = inp.bits if inp.bits is not None else inp.values
+    out = {k: v for k, v in src.items() if k != "x"}
+    if "w_dn" in out:
+        out["w_down"] = out.pop("w_dn")
+    return out
+
+
+def create_shards(w: tp_inputs.Workload, inp: tp_inputs.Inputs, ranks=None) -> List[tp.TpBlockShard]:
+    dt = tp.TP_BF16 if w.dtype == "bf16" else tp.TP_F32
+    hw = host_weights(inp)
+    ranks = range(w.tp_degree) if ranks is None else ranks
+    return [tp.tp_block_shard_create(
+        tp.make_config(w.tp_degree, r, w.hidden, w.num_heads, w.head_dim, w.ffn, dt), hw)
+        for r in ranks]
+
+
+def rowwise_biases(w: tp_inputs.Workload, inp: tp_inputs.Inputs) -> List[torch.Tensor]:
+    """fp32 device copies of the rowwise biases (exact widening of bf16)."""
+    out = []
+    for k in ("b_o", "b_dn"):
+        if k in inp.values:
+            out.append(torch.from_numpy(np.ascontiguousarray(inp.values[k], dtype=np.float32)).cuda())
+    return out
+
+
+class RankBuffers:
+    """Activation buffers of one rank: qkv [T, 3Dr], oh = [o_r | h_r]
+    [T, Dr + Fr], partial fp32 [T, D]."""
+
+    def __init__(self, shard: tp.TpBlockShard, T: int, partial: torch.Tensor = None):
+        dt = torch.bfloat16 if shard.dtype == tp.TP_BF16 else torch.float32
+        Dr, Fr, D = shard.d_r, shard.f_r, shard.hidden
+        self.qkv = torch.empty((T, 3 * Dr), dtype=dt, device="cuda") if Dr else None
+        self.oh = torch.empty((T, Dr + Fr), dtype=dt, device="cuda")
+        self.o = self.oh[:, :Dr] if Dr else None
+        self.h = self.oh[:, Dr:] if Fr else None
+        self.partial = partial if partial is not None else torch.empty((T, D), dtype=torch.float32,
+                                                                      device="cuda")
+
+
+def run_rank(shard: tp.TpBlockShard, x: torch.Tensor, buf: RankBuffers, fused: bool = True) -> None:
+    """One rank's hot path: colwise projection(s), attention, rowwise partial."""
+    T = x.shape[0]
+    attn, mlp = shard.d_r > 0, shard.f_r > 0
+    if attn and mlp:
+        if fused:
+            tp.tp_colwise_qkv_up(shard, T, x, buf.qkv, buf.h)
+        else:
+            tp.tp_colwise_linear(shard, tp.TP_QKV, T, x, buf.qkv)
+            tp.tp_colwise_linear(shard, tp.TP_MLP_UP, T, x, buf.h)
+        tp.tp_attn_heads(shard, T, buf.qkv, buf.o)
+        tp.tp_rowwise_linear_partial(shard, tp.TP_BLOCK_OUT, T, buf.oh, buf.partial)
+    elif attn:
+        tp.tp_colwise_linear(shard, tp.TP_QKV, T, x, buf.qkv)
+        tp.tp_attn_heads(shard, T, buf.qkv, buf.o)
+        tp.tp_rowwise_linear_partial(shard, tp.TP_ATTN_OUT, T, buf.o, buf.partial)
+    else:
+        tp.tp_colwise_linear(shard, tp.TP_MLP_UP, T, x, buf.h)
+        tp.tp_rowwise_linear_partial(shard, tp.TP_MLP_DOWN, T, buf.h, buf.partial)
+
+
+def as_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def rel_err(got, ref) -> float:
+    """max |got - ref| / max |ref|, the parity metric."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
