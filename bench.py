@@ -1,0 +1,258 @@
+"""Benchmark of the tensor-parallel DiT block shard on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+for every simulated rank r = 0..P-1 of the full block (T=16384 tokens,
+hidden 6144, 48 heads x 128, ffn 18432, tp_degree 4),
+    fused colwise QKV + MLP-up (bias, GELU-tanh)   -> qkv_r, h_r
+    attention over the rank's 12 heads              -> o_r
+    packed rowwise out over [o_r | h_r]             -> fp32 partial_r
+and then the partial reduce (+ rowwise biases) that stands in for the
+boundary AllReduce.  Inputs and weights are resident in HBM before timing.
+
+Prints one JSON line: value = algorithmic TFLOP/s of the step (GEMM
+2*M*N*K + attention 4*T^2*d per head, all ranks) / step time; "roofline"
+for the kernel with the largest share of step time, from HIP events around
+each launch on the stream it runs on; "cpu_baseline" = the float64 oracle
+timed on the host cores on a bounded sample (rank 0's shard of the same
+block on the first 12288 tokens).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "tensor_dit_transformer_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str, source: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if absent or taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    e = t.get(kernel_key)
+    if not e or e.get("source_sha") != kernel_source_hash(source):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(tokens_sample: int = 12288):
+    """The oracle, as it stands, on rank 0 of the tp_degree-4 full block for
+    the first `tokens_sample` tokens (a shorter sequence of the same block)."""
+    import numpy as np
+    import oracle as O
+    import tp_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    w = tp_inputs.C5_P4
+    inp = tp_inputs.make_inputs(w, seed=0, tokens=tokens_sample)
+    t0 = time.perf_counter()
+    O.rank_forward(inp["x"], inp.values, w.tp_degree, 0, w.num_heads, w.head_dim, bf16=True)
+    dt = time.perf_counter() - t0
+    T, D, P = tokens_sample, w.hidden, w.tp_degree
+    Dr, Fr, Hr = D // P, w.ffn // P, w.num_heads // P
+    flops = 2 * T * D * (3 * Dr + Fr) + 4 * T * T * w.head_dim * Hr + 2 * T * (Dr + Fr) * D
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rank 0 of 4 of the full block (hidden 6144, 48 heads, ffn 18432) on "
+                      f"the first {T} tokens: {flops / 1e9:.0f} GFLOP fp64 in {dt:.1f} s",
+            "seconds": round(dt, 2), "cpu_count": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="block_bf16_T16384_D6144_H48_F18432_P4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the shard's ranks are "
+              "simulated one after another on a single MI355X; there is no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tensor_dit_transformer_amd as tp
+    import tp_harness as H
+    import tp_inputs
+
+    w = tp_inputs.WORKLOADS[args.workload]
+    T, D, P, d = w.tokens, w.hidden, w.tp_degree, w.head_dim
+    Dr = D // P if w.has_attn else 0
+    Fr = w.ffn // P
+    Hr = w.num_heads // P
+
+    log(f"[bench] generating inputs for {w.name}")
+    t0 = time.time()
+    inp = tp_inputs.make_inputs(w, seed=0)
+    shards = H.create_shards(w, inp)
+    x = H.to_device(inp, "x")
+    biases = H.rowwise_biases(w, inp)
+    del inp
+    partials = [torch.empty((T, D), dtype=torch.float32, device="cuda") for _ in range(P)]
+    bufs = H.RankBuffers(shards[0], T, partial=partials[0])
+    y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    log(f"[bench] setup {time.time() - t0:.1f} s")
+
+    # kernels of a step, with algorithmic work per launch
+    kernels = {}
+    if w.has_attn and w.has_mlp:
+        kernels["colwise_qkv_up"] = ("gemm_bf16.hip", 2 * T * D * (3 * Dr + Fr), "mfma")
+        kernels["attention"] = ("attn_fwd.hip", 4 * T * T * d * Hr, "mfma")
+        kernels["rowwise_block_out"] = ("gemm_bf16.hip", 2 * T * (Dr + Fr) * D, "mfma")
+    elif w.has_attn:
+        kernels["colwise_qkv"] = ("gemm_bf16.hip", 2 * T * D * 3 * Dr, "mfma")
+        kernels["attention"] = ("attn_fwd.hip", 4 * T * T * d * Hr, "mfma")
+        kernels["rowwise_attn_out"] = ("gemm_bf16.hip", 2 * T * Dr * D, "mfma")
+    else:
+        kernels["colwise_mlp_up"] = ("gemm_bf16.hip", 2 * T * D * Fr, "mfma")
+        kernels["rowwise_mlp_down"] = ("gemm_bf16.hip", 2 * T * Fr * D, "mfma")
+    reduce_bytes = (P + 1) * T * D * 4 + len(biases) * D * 4
+    kernels["partial_reduce"] = ("partial_reduce.hip", reduce_bytes, "hbm")
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        def mark(name, fn):
+            if ev is None:
+                fn()
+                return
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev.setdefault(name, []).append((a, b))
+
+        for r, s in enumerate(shards):
+            bufs.partial = partials[r]
+            if w.has_attn and w.has_mlp:
+                mark("colwise_qkv_up", lambda: tp.tp_colwise_qkv_up(s, T, x, bufs.qkv, bufs.h))
+                mark("attention", lambda: tp.tp_attn_heads(s, T, bufs.qkv, bufs.o))
+                mark("rowwise_block_out", lambda: tp.tp_rowwise_linear_partial(
+                    s, tp.TP_BLOCK_OUT, T, bufs.oh, bufs.partial))
+            elif w.has_attn:
+                mark("colwise_qkv", lambda: tp.tp_colwise_linear(s, tp.TP_QKV, T, x, bufs.qkv))
+                mark("attention", lambda: tp.tp_attn_heads(s, T, bufs.qkv, bufs.o))
+                mark("rowwise_attn_out", lambda: tp.tp_rowwise_linear_partial(
+                    s, tp.TP_ATTN_OUT, T, bufs.o, bufs.partial))
+            else:
+                mark("colwise_mlp_up", lambda: tp.tp_colwise_linear(s, tp.TP_MLP_UP, T, x, bufs.h))
+                mark("rowwise_mlp_down", lambda: tp.tp_rowwise_linear_partial(
+                    s, tp.TP_MLP_DOWN, T, bufs.h, bufs.partial))
+        mark("partial_reduce", lambda: tp.tp_partial_reduce(partials, biases, y))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    ev = {}
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        step(ev)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu_ms = g0.elapsed_time(g1)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+
+    step_flops = sum(k[1] for n, k in kernels.items() if k[2] == "mfma") * P
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    per_kernel = {}
+    for name, (src, work, bound) in kernels.items():
+        times = [a.elapsed_time(b) for a, b in ev[name]]
+        avg_ms = sum(times) / len(times)
+        per_launch = work
+        if bound == "mfma":
+            ach = per_launch / (avg_ms * 1e-3) / 1e12
+            per_kernel[name] = {"avg_ms": round(avg_ms, 4), "launches_per_step": len(times) // args.steps,
+                                "tflops": round(ach, 1), "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                                "step_share": 0.0}
+        else:
+            ach = per_launch / (avg_ms * 1e-3) / 1e9
+            per_kernel[name] = {"avg_ms": round(avg_ms, 4), "launches_per_step": len(times) // args.steps,
+                                "gbs": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4),
+                                "step_share": 0.0}
+        per_kernel[name]["step_share"] = round(avg_ms * per_kernel[name]["launches_per_step"]
+                                               / ms_per_step, 4)
+    dom = max(per_kernel, key=lambda n: per_kernel[n]["step_share"])
+    src, work, bound = kernels[dom]
+    k = per_kernel[dom]
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": k["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": k["frac"]}
+    else:
+        roof = {"bound": "hbm", "achieved": k["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": k["frac"]}
+    roof["kernel"] = dom
+    roof["traffic"] = load_traffic(dom, src)
+
+    torch.cuda.synchronize()
+    for s in shards:
+        s.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle sample")
+        cpu = cpu_baseline()
+        log(f"[bench] oracle: {cpu['sample']}")
+
+    out = {
+        "metric": "TFLOP/s per TP-rank DiT block shard (bf16) + % of MI355X MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) activations, N(0,0.02) weights, N(0,0.01) biases, bf16 RNE",
+        "mfma_peak_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "config": {"workload": w.name, "tokens": T, "hidden": D, "num_heads": w.num_heads,
+                   "head_dim": d, "ffn": w.ffn, "tp_degree": P, "ranks_per_step": P,
+                   "step": "per rank: fused colwise QKV+up, attention, packed rowwise out; then partial reduce"},
+        "roofline": roof,
+        "kernels": per_kernel,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
