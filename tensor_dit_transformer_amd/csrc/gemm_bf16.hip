@@ -198,6 +198,168 @@ gemm_bf16_nt(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
   }
 }
 
+// 256x256 tile, 8 waves (2 per SIMD, so one wave's LDS reads and epilogue
+// overlap the other's MFMAs) in a 2 x 4 grid of 128x64 wave tiles.  A and B
+// tiles go global -> LDS directly (global_load_lds_dwordx4: each wave
+// instruction fills 1 KB = 8 tile rows), so no registers stage them and no
+// ds_write is issued.  Needs K % 64 == 0 (no zero-fill on this path).
+template <OutKind KIND>
+__global__ void __launch_bounds__(512)
+gemm_bf16_nt_256x256_8w(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
+  constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
+  constexpr int WTM = BM / WM, WTN = BN / WN;   // 128 x 64
+  constexpr int TM = WTM / 32, TN = WTN / 32;   // 4 x 2 MFMA tiles
+  constexpr int BUF = (BM + BN) * kRowChunks;   // 16-byte chunks per stage
+  constexpr int NWAVES = 8;
+  constexpr int A_INSTR = BM * kRowChunks / 64 / NWAVES;  // 4 wave loads of 1 KB
+  constexpr int B_INSTR = BN * kRowChunks / 64 / NWAVES;
+
+  __shared__ u32x4 smem[2 * BUF];
+
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, per = nb >> 3, rem = nb & 7;
+  const int id = xcd * per + min(xcd, rem) + (bid >> 3);
+  const int group = id / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = id - group * kGroupM * tiles_n;
+  const int m0 = (first_m + in_group % gm) * BM;
+  const int n0 = (in_group / gm) * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bf16* __restrict__ A = static_cast<const bf16*>(p.A);
+  const bf16* __restrict__ B = static_cast<const bf16*>(p.B);
+
+  // Wave instruction i fills chunks c0 = (wave * A_INSTR + i) * 64 .. + 63 of
+  // the stage, i.e. tile rows 8 (wave * A_INSTR + i) + (lane >> 3); lane
+  // writes physical chunk (lane & 7) of its row, which holds logical k-group
+  // (lane & 7) ^ swizzle-of-row.
+  int64_t a_off[A_INSTR], b_off[B_INSTR];
+#pragma unroll
+  for (int i = 0; i < A_INSTR; ++i) {
+    const int row = 8 * (wave * A_INSTR + i) + (lane >> 3);
+    const int kc = swizzle(row, lane & 7);
+    a_off[i] = (int64_t)min(m0 + row, p.M - 1) * p.lda + kc * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_INSTR; ++i) {
+    const int row = 8 * (wave * B_INSTR + i) + (lane >> 3);
+    const int kc = swizzle(row, lane & 7);
+    b_off[i] = (int64_t)min(n0 + row, p.N - 1) * p.ldb + kc * 8;
+  }
+  auto issue = [&](int kt, int buf) {
+    const int k = kt * kBK;
+    u32x4* sa = smem + buf * BUF;
+    u32x4* sb = sa + BM * kRowChunks;
+#pragma unroll
+    for (int i = 0; i < A_INSTR; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(A + a_off[i] + k),
+          (void __attribute__((address_space(3)))*)(sa + (wave * A_INSTR + i) * 64), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_INSTR; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(B + b_off[i] + k),
+          (void __attribute__((address_space(3)))*)(sb + (wave * B_INSTR + i) * 64), 16, 0, 0);
+  };
+
+  const int wm = wave / WN, wn = wave % WN;
+  const int a_row = wm * WTM + (lane & 31);
+  const int b_row = wn * WTN + (lane & 31);
+  const int khalf = lane >> 5;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int nk = p.K / kBK;
+  issue(0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
+    const u32x4* sa = smem + buf * BUF;
+    const u32x4* sb = sa + BM * kRowChunks;
+#pragma unroll
+    for (int s = 0; s < kBK / 16; ++s) {
+      const int kc = 2 * s + khalf;
+      bf16x8 a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        a[i] = __builtin_bit_cast(bf16x8, sa[(a_row + 32 * i) * kRowChunks + swizzle(a_row, kc)]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        b[j] = __builtin_bit_cast(bf16x8, sb[(b_row + 32 * j) * kRowChunks + swizzle(b_row, kc)]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();  // waits for this wave's LDS-DMA loads, then for every wave
+  }
+
+  const int col_l = lane & 31;
+  const int row_l = 4 * (lane >> 5);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + wn * WTN + 32 * j + col_l;
+    if (col >= p.N) continue;
+    float bias = 0.0f;
+    if constexpr (KIND != OutKind::F32_ACC) {
+      if (ep.bias) bias = ep.bias[col];
+    }
+    const bool gelu = col >= ep.gelu_from;
+    const bool second = col >= ep.split;
+    const int ocol = second ? col - ep.split : col;
+    const int64_t ld = second ? ep.ld1 : ep.ld0;
+    void* out = second ? ep.out1 : ep.out0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * WTM + 32 * i + 8 * (e >> 2) + row_l + (e & 3);
+        if (row >= p.M) continue;
+        const int64_t off = (int64_t)row * ld + ocol;
+        float v = acc[i][j][e];
+        if constexpr (KIND == OutKind::F32_ACC) {
+          float* o = static_cast<float*>(out) + off;
+          *o = *o + v;
+        } else {
+          v += bias;
+          if (gelu) v = gelu_tanh(v);
+          if constexpr (KIND == OutKind::BF16)
+            static_cast<bf16*>(out)[off] = static_cast<bf16>(v);
+          else
+            static_cast<float*>(out)[off] = v;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_256x256_8w(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
+                             hipStream_t stream) {
+  const int tm = (p.M + 255) / 256, tn = (p.N + 255) / 256;
+  const dim3 grid(tm * tn), block(512);
+  switch (kind) {
+    case OutKind::BF16:
+      hipLaunchKernelGGL(gemm_bf16_nt_256x256_8w<OutKind::BF16>, grid, block, 0, stream, p, ep, tm, tn);
+      break;
+    case OutKind::F32_STORE:
+      hipLaunchKernelGGL(gemm_bf16_nt_256x256_8w<OutKind::F32_STORE>, grid, block, 0, stream, p, ep, tm, tn);
+      break;
+    case OutKind::F32_ACC:
+      hipLaunchKernelGGL(gemm_bf16_nt_256x256_8w<OutKind::F32_ACC>, grid, block, 0, stream, p, ep, tm, tn);
+      break;
+  }
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_tile(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
                        hipStream_t stream) {
@@ -228,6 +390,7 @@ hipError_t launch_gemm_bf16(const GemmProblem& p, const GemmEpilogue& ep, OutKin
   // 256x256 tiles when they give at least one full wave of workgroups on the
   // 256 CUs; 128x128 otherwise.
   const long big = (long)((p.M + 255) / 256) * ((p.N + 255) / 256);
+  if (big >= 256 && p.K % kBK == 0) return launch_256x256_8w(p, ep, kind, stream);
   if (big >= 256) return launch_tile<256, 256, 2, 2>(p, ep, kind, stream);
   return launch_tile<128, 128, 2, 2>(p, ep, kind, stream);
 }

@@ -1,0 +1,179 @@
+"""GPU parity at the workloads' full sizes.
+
+C2 (MLP shard), C3 (attention shard) and C4 (wide block shard) are compared
+element by element with the float64 oracle.  The full block (T=16384,
+hidden 6144, 48 heads, ffn 18432, tp_degree 4 and 2) runs in exactly the
+launch configuration the benchmark times; there the oracle computes sampled
+outputs one by one (each output row depends on its own input row, plus all
+keys/values for attention), every kernel is also fed a seeded full-size input
+and checked on sampled rows (reduce: every element), and the reduced outputs
+of the tp_degree-4 and tp_degree-2 runs must agree (a property of the
+colwise/rowwise split at any size, Diffusers TP page §Colwise e rowwise)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import tensor_dit_transformer_amd as tp
+import tp_harness as H
+import tp_inputs
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _run(w, inp, ranks):
+    shards = H.create_shards(w, inp, ranks=ranks)
+    x = H.to_device(inp, "x")
+    outs = []
+    for s in shards:
+        b = H.RankBuffers(s, w.tokens)
+        H.run_rank(s, x, b)
+        outs.append(b)
+    torch.cuda.synchronize()
+    return shards, outs
+
+
+def _close(shards):
+    torch.cuda.synchronize()
+    for s in shards:
+        s.close()
+
+
+def _check(buf, ref, what):
+    errs = {}
+    if buf.qkv is not None:
+        errs["qkv_r"] = H.rel_err(H.as_f64(buf.qkv), ref["qkv_r"])
+        errs["o_r"] = H.rel_err(H.as_f64(buf.o), ref["o_r"])
+    if buf.h is not None:
+        errs["h_r"] = H.rel_err(H.as_f64(buf.h), ref["h_r"])
+    errs["partial_r"] = H.rel_err(H.as_f64(buf.partial), ref["p_block"])
+    say(what, {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= H.TOL["bf16"], f"{what} {k}: {v:.3e}"
+
+
+@pytest.mark.parametrize("name,ranks", [
+    ("mlp_bf16_T4608_D3072_F12288_P4", (0, 3)),
+    ("attn_bf16_T4608_D3072_H24_P4", (0, 3)),
+    ("block_bf16_T4608_D6144_H48_F18432_P4", (0,)),
+])
+def test_one_rank_shards_full_compare(name, ranks):
+    w = tp_inputs.WORKLOADS[name]
+    inp = tp_inputs.make_inputs(w, seed=0)
+    say(f"[{name}] inputs ready")
+    shards, outs = _run(w, inp, ranks)
+    for r, b in zip(ranks, outs):
+        ref = O.rank_forward(inp["x"], inp.values, w.tp_degree, r, w.num_heads, w.head_dim, bf16=True)
+        _check(b, ref, f"{name} rank {r}")
+    _close(shards)
+
+
+def test_full_block_bench_configuration():
+    w4, w2 = tp_inputs.C5_P4, tp_inputs.C5_P2
+    inp = tp_inputs.make_inputs(w4, seed=0)
+    v = inp.values
+    T, D, d, HD = w4.tokens, w4.hidden, w4.head_dim, w4.num_heads * w4.head_dim
+    rows = tp_inputs.sample_rows(T, 24, seed=1)
+    xr = v["x"][rows]
+    x64 = v["x"].astype(np.float64)
+    x = H.to_device(inp, "x")
+    say("[C5] inputs ready")
+    ys = {}
+    for w in (w4, w2):
+        P = w.tp_degree
+        shards = H.create_shards(w, inp)
+        partials = [torch.empty((T, D), dtype=torch.float32, device="cuda") for _ in range(P)]
+        for r, s in enumerate(shards):
+            b = H.RankBuffers(s, T, partial=partials[r])
+            H.run_rank(s, x, b)
+            torch.cuda.synchronize()
+            R, C = O.colwise_range(HD, P, r), O.colwise_range(w.ffn, P, r)
+            w_qkv = np.concatenate([v["w_q"][R], v["w_k"][R], v["w_v"][R]])
+            b_qkv = np.concatenate([v["b_q"][R], v["b_k"][R], v["b_v"][R]])
+            e_qkv = H.rel_err(H.as_f64(b.qkv[rows]), O.colwise_rows_sampled(xr, w_qkv, b_qkv))
+            e_h = H.rel_err(H.as_f64(b.h[rows]),
+                            O.colwise_rows_sampled(xr, v["w_up"][C], v["b_up"][C], gelu=True))
+            # one sampled head of this rank: its K and V over all tokens
+            j = (5 * r + 3) % s.heads_r
+            g = slice(R.start + j * d, R.start + (j + 1) * d)
+            k = O.to_bf16_rne(O.linear(x64, v["w_k"][g], v["b_k"][g]))
+            vv = O.to_bf16_rne(O.linear(x64, v["w_v"][g], v["b_v"][g]))
+            q = O.to_bf16_rne(O.linear(xr, v["w_q"][g], v["b_q"][g]))
+            o_ref = O.to_bf16_rne(O.attention_rows(q, k, vv, 1, d))
+            e_o = H.rel_err(H.as_f64(b.o[rows, j * d:(j + 1) * d]), o_ref)
+            say(f"[C5 P={P}] rank {r}: qkv {e_qkv:.2e} h {e_h:.2e} o(head {j}) {e_o:.2e}")
+            for e in (e_qkv, e_h, e_o):
+                assert e <= H.TOL["bf16"]
+            del b
+        y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+        tp.tp_partial_reduce(partials, H.rowwise_biases(w, inp), y)
+        torch.cuda.synchronize()
+        ys[P] = y
+        del partials
+        _close(shards)
+    e = H.rel_err(H.as_f64(ys[2]), H.as_f64(ys[4]))
+    say(f"[C5] y(P=2) vs y(P=4): {e:.2e}")
+    assert e <= 1e-5
+
+
+def test_full_size_kernels_on_seeded_inputs():
+    """Each kernel of the full block, at its full-size launch, on a seeded
+    input the oracle can check directly."""
+    w = tp_inputs.C5_P4
+    inp = tp_inputs.make_inputs(w, seed=0)
+    v = inp.values
+    T, D, d, P = w.tokens, w.hidden, w.head_dim, w.tp_degree
+    HD = w.num_heads * d
+    rows = tp_inputs.sample_rows(T, 24, seed=2)
+    r = 2
+    s = H.create_shards(w, inp, ranks=(r,))[0]
+    Dr, Fr, Hr = s.d_r, s.f_r, s.heads_r
+
+    # attention over a seeded packed qkv (std 1.5, like the projections' output)
+    qkv_v, qkv_b = tp_inputs.random_matrix((T, 3 * Dr), seed=31, std=1.5)
+    qkv = torch.from_numpy(qkv_b.view(np.int16)).view(torch.bfloat16).cuda()
+    o = torch.empty((T, Dr), dtype=torch.bfloat16, device="cuda")
+    tp.tp_attn_heads(s, T, qkv, o)
+    torch.cuda.synchronize()
+    q64 = qkv_v.astype(np.float64)
+    o_ref = O.to_bf16_rne(O.attention_rows(q64[rows, :Dr], q64[:, Dr:2 * Dr], q64[:, 2 * Dr:], Hr, d))
+    e_o = H.rel_err(H.as_f64(o[rows]), o_ref)
+    say(f"[C5 kernels] attention (12 heads, T=16384): {e_o:.2e}")
+    assert e_o <= H.TOL["bf16"]
+    del qkv, o, q64
+
+    # packed rowwise out over a seeded [o | h]
+    xl_v, xl_b = tp_inputs.random_matrix((T, Dr + Fr), seed=32)
+    xl = torch.from_numpy(xl_b.view(np.int16)).view(torch.bfloat16).cuda()
+    part = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    tp.tp_rowwise_linear_partial(s, tp.TP_BLOCK_OUT, T, xl, part)
+    torch.cuda.synchronize()
+    w_blk = np.concatenate([v["w_o"][:, O.rowwise_range(HD, P, r)],
+                            v["w_dn"][:, O.rowwise_range(w.ffn, P, r)]], axis=1)
+    ref = O.linear(xl_v[rows], w_blk)
+    e_p = H.rel_err(H.as_f64(part[rows]), ref)
+    say(f"[C5 kernels] block out (K=6144, N=6144): {e_p:.2e}")
+    assert e_p <= H.TOL["bf16"]
+    del xl, w_blk
+    torch.cuda.synchronize()
+    s.close()
+
+    # partial reduce over seeded fp32 partials, every element
+    parts = [tp_inputs.random_matrix((T, D), seed=40 + i, dtype="f32")[0] for i in range(P)]
+    biases = [v["b_o"], v["b_dn"]]
+    dp = [torch.from_numpy(p).cuda() for p in parts]
+    db = [torch.from_numpy(np.ascontiguousarray(b, dtype=np.float32)).cuda() for b in biases]
+    y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    tp.tp_partial_reduce(dp, db, y)
+    torch.cuda.synchronize()
+    ref = O.partial_reduce(parts, O.rowwise_bias({"b_o": biases[0], "b_dn": biases[1]}))
+    e_y = H.rel_err(H.as_f64(y), ref)
+    say(f"[C5 kernels] reduce (4 x 16384 x 6144): {e_y:.2e}")
+    assert e_y <= 1e-6

@@ -162,6 +162,37 @@ def test_k_not_multiple_of_tile_and_single_rank(dtype):
     close_all(shards)
 
 
+# Shapes large enough (>= 256 output tiles of 256 x 256, K % 64 == 0) for the
+# 8-wave direct-to-LDS GEMM, with a ragged token count.
+BIG_FUSED = Workload("big_fused_T2125_D1024_H8_F16384_P2", 2125, 1024, 8, 128, 16384, 2, "bf16")
+
+
+def test_large_fused_colwise_and_attention_paths():
+    w = BIG_FUSED   # fused QKV+up: N = 3*512 + 8192 = 9728 -> 9 x 38 tiles
+    inp = tp_inputs.make_inputs(w, seed=21)
+    ranks, y_ref = full_oracle(w, inp)
+    shards, outs, y = run_all_ranks(w, inp)
+    for r, (buf, ref) in enumerate(zip(outs, ranks)):
+        check_rank(w, buf, ref, H.TOL["bf16"], f"BIG_FUSED rank {r}")
+    assert H.rel_err(H.as_f64(y), y_ref) <= H.TOL["bf16"]
+    close_all(shards)
+
+
+def test_large_rowwise_store_and_accumulate_paths():
+    # MLP-only, P = 1, hidden 8192: the down projection is N = 8192 -> 9 x 32 tiles
+    w = Workload("big_down_T2125_D8192_F1024_P1", 2125, 8192, 0, 0, 1024, 1, "bf16")
+    inp = tp_inputs.make_inputs(w, seed=22)
+    ranks, y_ref = full_oracle(w, inp)
+    shards, outs, y = run_all_ranks(w, inp)
+    check_rank(w, outs[0], ranks[0], H.TOL["bf16"], "BIG_DOWN")
+    p2 = torch.zeros_like(outs[0].partial)
+    tp.tp_rowwise_linear_partial(shards[0], tp.TP_MLP_DOWN, w.tokens, outs[0].h, p2, accumulate=True)
+    tp.tp_rowwise_linear_partial(shards[0], tp.TP_MLP_DOWN, w.tokens, outs[0].h, p2, accumulate=True)
+    torch.cuda.synchronize()
+    assert H.rel_err(H.as_f64(p2), 2 * ranks[0]["p_block"]) <= H.TOL["bf16"]
+    close_all(shards)
+
+
 def test_zero_tokens_is_a_no_op():
     w = Workload("zero", 8, 256, 2, 128, 512, 2, "bf16")
     inp = tp_inputs.make_inputs(w, seed=1)
