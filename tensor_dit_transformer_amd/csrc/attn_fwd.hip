@@ -8,7 +8,8 @@
 // of the packed qkv tensor [T, 3*Dr].
 //
 // Design:
-//   * grid = (ceil(T/128), heads); 4 waves per workgroup, 32 queries per wave.
+//   * grid = (ceil(T/128), heads); 4 waves per workgroup, 32 queries per wave,
+//     <= 256 VGPRs so two workgroups share a CU (two waves per SIMD).
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (A = a 32-key slab of K from LDS, B = the
 //     wave's Q^T held in registers for the whole kernel).  In the 32x32
@@ -22,10 +23,12 @@
 //   * K and V tiles of 64 keys are fetched one tile ahead into registers and
 //     written to a double-buffered LDS (padded rows, conflict-free reads);
 //     one barrier per tile.
-//   * Softmax runs in the exp2 domain: s * log2(e)/sqrt(d), running max m,
-//     running sum l, rescale by exp2(m_old - m_new).  Keys past T get -inf
-//     (only the last tile); query rows past T are clamped on load and not
-//     stored.
+//   * Softmax runs in the exp2 domain with few vector instructions per
+//     score: one FMA (scale folded in) and one exp2; the row sum is a bf16
+//     dot2 over the packed weights; the accumulator is rescaled by
+//     exp2(m_old - m_new) only when a row max outgrows the reference by 8
+//     (log2 units).  Keys past T get -inf (last tile only); query rows past T
+//     are clamped on load and not stored.
 #include "tp_kernels.h"
 
 namespace tpk {
@@ -49,7 +52,91 @@ __device__ __forceinline__ int vt_pos(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-__global__ void __launch_bounds__(256)
+// Slack (log2 domain) the running max may trail the true row max before the
+// accumulator is rescaled.  Softmax is invariant to the reference value, so
+// this only lets the unnormalised weights grow to at most 2^8; it skips almost
+// every O rescale once the first tiles have set the max.
+constexpr float kRescaleSlack = 8.0f;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <bool MASKED>
+__device__ __forceinline__ void attn_tile(const bf16* __restrict__ sKb, const bf16* __restrict__ sVb,
+                                          const bf16x8 (&qf)[kD / 16], f32x16 (&acc_o)[kD / 32],
+                                          float& m_ref, float& l_run, int key0, int T,
+                                          float scale_log2, int l32, int half) {
+  // S^T for keys 32 c .. 32 c + 31 of the tile (raw scores)
+  f32x16 s[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[c][e] = 0.0f;
+    const bf16* kb = sKb + (32 * c + l32) * kKPitch + 8 * half;
+#pragma unroll
+    for (int st = 0; st < kD / 16; ++st) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + 16 * st);
+      s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[c], 0, 0, 0);
+    }
+  }
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = key0 + 32 * c + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (key >= T) s[c][e] = -INFINITY;
+      }
+  }
+  // tile max of this lane's 32 scores, then of the other half-wave's 32
+  float mloc = s[0][0];
+#pragma unroll
+  for (int e = 1; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s[0][e], s[0][e + 1]));
+#pragma unroll
+  for (int e = 0; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s[1][e], s[1][e + 1]));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;
+  // rescale only when some row's max outgrew the reference by the slack
+  if (__builtin_amdgcn_ballot_w64(mloc > m_ref + kRescaleSlack)) {
+    const float m_new = fmaxf(m_ref, mloc);
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+    m_ref = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc_o[t][e] *= alpha;
+  }
+  // p = exp2(s * log2(e)/sqrt(d) - m_ref), packed to bf16 for the PV product;
+  // the row sum adds the bf16 values the product actually uses
+  bf16x8 pb[2][2];
+  const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[c][e], scale_log2, -m_ref));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[c][e + 1], scale_log2, -m_ref));
+      const bf16x2 pp = {static_cast<bf16>(p0), static_cast<bf16>(p1)};
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+      pb[c][e >> 3][e & 7] = pp[0];
+      pb[c][e >> 3][(e & 7) + 1] = pp[1];
+    }
+  // O^T += V^T P^T over the tile's 4 steps of 16 keys
+#pragma unroll
+  for (int t = 0; t < kD / 32; ++t) {
+    const bf16* vb = sVb + (32 * t + l32) * kVPitch + 8 * half;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vb + 32 * c + 16 * u);
+        acc_o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c][u], acc_o[t], 0, 0, 0);
+      }
+  }
+}
+
+// Two workgroups per CU (<= 256 VGPRs per wave): each SIMD runs two waves, so
+// one wave's softmax arithmetic overlaps the other's matrix instructions.
+__global__ void __launch_bounds__(256, 2)
 attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict__ o,
                    int64_t ldo, int T, int heads, float scale_log2) {
   __shared__ bf16 sK[2][kBKV * kKPitch];
@@ -120,9 +207,10 @@ attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict
   for (int t = 0; t < kD / 32; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc_o[t][e] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_ref = -INFINITY, l_run = 0.0f;
 
   const int nkt = (T + kBKV - 1) / kBKV;
+  const int nfull = T / kBKV;  // tiles with every key valid
   gload(0);
   sstore(0);
   __syncthreads();
@@ -130,69 +218,10 @@ attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict
     const int buf = kt & 1;
     const bool more = kt + 1 < nkt;
     if (more) gload(kt + 1);
-
-    // S^T for keys 32 c .. 32 c + 31 of this tile
-    f32x16 s[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[c][e] = 0.0f;
-      const bf16* kb = &sK[buf][(32 * c + l32) * kKPitch + 8 * half];
-#pragma unroll
-      for (int st = 0; st < kD / 16; ++st) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + 16 * st);
-        s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[c], 0, 0, 0);
-      }
-    }
-
-    // online softmax for query l32; this lane holds 32 of the tile's 64 keys
-    const int k0 = kt * kBKV;
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = s[c][e] * scale_log2;
-        if (k0 + kBKV > T) {
-          const int key = k0 + 32 * c + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (key >= T) v = -INFINITY;
-        }
-        s[c][e] = v;
-        mloc = fmaxf(mloc, v);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.0f;
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(s[c][e] - m_new);
-        psum += pv;
-        pb[c][e >> 3][e & 7] = static_cast<bf16>(pv);
-      }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int t = 0; t < kD / 32; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc_o[t][e] *= alpha;
-
-    // O^T += V^T P^T over the tile's 4 steps of 16 keys
-#pragma unroll
-    for (int t = 0; t < kD / 32; ++t) {
-      const bf16* vb = &sVt[buf][(32 * t + l32) * kVPitch + 8 * half];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(vb + 32 * c + 16 * u);
-          acc_o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c][u], acc_o[t], 0, 0, 0);
-        }
-    }
-
+    if (kt < nfull)
+      attn_tile<false>(sK[buf], sVt[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, scale_log2, l32, half);
+    else
+      attn_tile<true>(sK[buf], sVt[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, scale_log2, l32, half);
     if (more) sstore(buf ^ 1);
     __syncthreads();
   }
