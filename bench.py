@@ -90,6 +90,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="block_bf16_T16384_D6144_H48_F18432_P4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before warmup, run a plain 512 MiB device-to-device copy twice so a "
+                         "counter run can scale FETCH_SIZE / WRITE_SIZE by a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the shard's ranks are "
@@ -137,6 +140,13 @@ def main():
     kernels["partial_reduce"] = ("partial_reduce.hip", reduce_bytes, "hbm")
 
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev=None):
         def mark(name, fn):

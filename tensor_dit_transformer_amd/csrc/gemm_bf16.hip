@@ -276,6 +276,27 @@ gemm_bf16_nt_256x256_8w(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // Operand fragments are double-buffered in registers: the reads for k-step
+  // s + 1 are issued before the MFMAs of step s, so LDS latency hides behind
+  // matrix work within each wave.
+  bf16x8 fa[2][TM], fb[2][TN];
+  auto read_frags = [&](const u32x4* sa, const u32x4* sb, int s, int slot) {
+    const int kc = 2 * s + khalf;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      fa[slot][i] = __builtin_bit_cast(bf16x8, sa[(a_row + 32 * i) * kRowChunks + swizzle(a_row, kc)]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      fb[slot][j] = __builtin_bit_cast(bf16x8, sb[(b_row + 32 * j) * kRowChunks + swizzle(b_row, kc)]);
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+  };
+
   const int nk = p.K / kBK;
   issue(0, 0);
   __syncthreads();
@@ -284,21 +305,15 @@ gemm_bf16_nt_256x256_8w(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n
     if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
     const u32x4* sa = smem + buf * BUF;
     const u32x4* sb = sa + BM * kRowChunks;
+    read_frags(sa, sb, 0, 0);
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
-      const int kc = 2 * s + khalf;
-      bf16x8 a[TM], b[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        a[i] = __builtin_bit_cast(bf16x8, sa[(a_row + 32 * i) * kRowChunks + swizzle(a_row, kc)]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        b[j] = __builtin_bit_cast(bf16x8, sb[(b_row + 32 * j) * kRowChunks + swizzle(b_row, kc)]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      // fences keep the compiler from sinking the next step's reads below
+      // this step's MFMAs (or merging the two fragment sets)
+      if (s + 1 < kBK / 16) read_frags(sa, sb, s + 1, (s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(s & 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();  // waits for this wave's LDS-DMA loads, then for every wave
   }
@@ -342,19 +357,198 @@ gemm_bf16_nt_256x256_8w(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n
   }
 }
 
+// Ping-pong variant of the 256x256 8-wave tile.  Waves 0-3 (group 0) own C
+// rows 0-127 and waves 4-7 (group 1) rows 128-255.  The groups run one phase
+// apart, separated by workgroup barriers: while one group reads a whole K
+// tile of operand fragments from LDS into registers (24 x 16 bytes per
+// lane), the other issues the 32 MFMAs of the tile it read in the previous
+// phase.  Phase 2k: group 0 reads tile k, group 1 multiplies tile k-1;
+// phase 2k+1: group 0 multiplies tile k, group 1 reads tile k.  Tile k+1 is
+// fetched global -> LDS (half by each group) at the start of phase 2k into
+// the stage that held tile k-1, and waited for at the end of phase 2k+1.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <OutKind KIND, int GROUP_SHIFT>
+__global__ void __launch_bounds__(512)
+gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
+  constexpr int BM = 256, BN = 256;
+  constexpr int TM = 4, TN = 2;                 // 128 x 64 per wave
+  constexpr int KS = kBK / 16;                  // 4 MFMA k-steps per tile
+  constexpr int BUF = (BM + BN) * kRowChunks;   // 16-byte chunks per stage
+
+  __shared__ u32x4 smem[2 * BUF];
+
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, per = nb >> 3, rem = nb & 7;
+  const int id = xcd * per + min(xcd, rem) + (bid >> 3);
+  const int group = id / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = id - group * kGroupM * tiles_n;
+  const int m0 = (first_m + in_group % gm) * BM;
+  const int n0 = (in_group / gm) * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  // group of a wave: GROUP_SHIFT 2 -> waves 0-3 / 4-7, 0 -> even / odd waves
+  const int g = GROUP_SHIFT == 2 ? (wave >> 2) : (wave & 1);
+  const int q = GROUP_SHIFT == 2 ? (wave & 3) : (wave >> 1);
+  const bf16* __restrict__ A = static_cast<const bf16*>(p.A);
+  const bf16* __restrict__ B = static_cast<const bf16*>(p.B);
+
+  // global -> LDS: group g fetches A rows and B rows [128 g, 128 g + 128);
+  // wave instruction i of wave q covers 8 rows from 128 g + 32 q + 8 i.
+  int a_off[4], b_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 128 * g + 32 * q + 8 * i + (lane >> 3);
+    const int kc = swizzle(row, lane & 7);
+    a_off[i] = min(m0 + row, p.M - 1) * (int)p.lda + kc * 8;
+    b_off[i] = min(n0 + row, p.N - 1) * (int)p.ldb + kc * 8;
+  }
+  const int dst0 = (128 * g + 32 * q) * kRowChunks;
+  auto issue = [&](int kt) {
+    const int k = kt * kBK;
+    u32x4* sa = smem + (kt & 1) * BUF;
+    u32x4* sb = sa + BM * kRowChunks;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(A + a_off[i] + k),
+          (void __attribute__((address_space(3)))*)(sa + dst0 + 64 * i), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(B + b_off[i] + k),
+          (void __attribute__((address_space(3)))*)(sb + dst0 + 64 * i), 16, 0, 0);
+  };
+
+  const int a_row = 128 * g + (lane & 31);
+  const int b_row = 64 * q + (lane & 31);
+  const int khalf = lane >> 5;
+  bf16x8 fa[KS][TM], fb[KS][TN];
+  auto read_tile = [&](int kt) {
+    const u32x4* sa = smem + (kt & 1) * BUF;
+    const u32x4* sb = sa + BM * kRowChunks;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int kc = 2 * s + khalf;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[s][i] = __builtin_bit_cast(bf16x8, sa[(a_row + 32 * i) * kRowChunks + swizzle(a_row, kc)]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fb[s][j] = __builtin_bit_cast(bf16x8, sb[(b_row + 32 * j) * kRowChunks + swizzle(b_row, kc)]);
+    }
+  };
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  auto multiply = [&]() {
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+  };
+
+  const int nk = p.K / kBK;
+  issue(0);
+  wait_vmem();
+  wg_barrier();
+  if (g == 0) {
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool more = kt + 1 < nk;
+      if (more) issue(kt + 1);
+      read_tile(kt);
+      wg_barrier();                       // end of phase 2 kt
+      multiply();
+      if (more) wait_vmem();
+      wg_barrier();                       // end of phase 2 kt + 1
+    }
+    wg_barrier();
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool more = kt + 1 < nk;
+      if (more) issue(kt + 1);
+      if (kt > 0) multiply();             // tile kt - 1
+      wg_barrier();                       // end of phase 2 kt
+      read_tile(kt);
+      if (more) wait_vmem();
+      wg_barrier();                       // end of phase 2 kt + 1
+    }
+    multiply();
+    wg_barrier();
+  }
+
+  const int col_l = lane & 31;
+  const int row_l = 4 * (lane >> 5);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + 64 * q + 32 * j + col_l;
+    if (col >= p.N) continue;
+    float bias = 0.0f;
+    if constexpr (KIND != OutKind::F32_ACC) {
+      if (ep.bias) bias = ep.bias[col];
+    }
+    const bool gelu = col >= ep.gelu_from;
+    const bool second = col >= ep.split;
+    const int ocol = second ? col - ep.split : col;
+    const int64_t ld = second ? ep.ld1 : ep.ld0;
+    void* out = second ? ep.out1 : ep.out0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + 128 * g + 32 * i + 8 * (e >> 2) + row_l + (e & 3);
+        if (row >= p.M) continue;
+        const int64_t off = (int64_t)row * ld + ocol;
+        float v = acc[i][j][e];
+        if constexpr (KIND == OutKind::F32_ACC) {
+          float* o = static_cast<float*>(out) + off;
+          *o = *o + v;
+        } else {
+          v += bias;
+          if (gelu) v = gelu_tanh(v);
+          if constexpr (KIND == OutKind::BF16)
+            static_cast<bf16*>(out)[off] = static_cast<bf16>(v);
+          else
+            static_cast<float*>(out)[off] = v;
+        }
+      }
+    }
+  }
+}
+
 hipError_t launch_256x256_8w(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
                              hipStream_t stream) {
   const int tm = (p.M + 255) / 256, tn = (p.N + 255) / 256;
   const dim3 grid(tm * tn), block(512);
   switch (kind) {
     case OutKind::BF16:
-      hipLaunchKernelGGL(gemm_bf16_nt_256x256_8w<OutKind::BF16>, grid, block, 0, stream, p, ep, tm, tn);
+      hipLaunchKernelGGL((gemm_bf16_nt_pingpong<OutKind::BF16, 2>), grid, block, 0, stream, p, ep, tm, tn);
       break;
     case OutKind::F32_STORE:
-      hipLaunchKernelGGL(gemm_bf16_nt_256x256_8w<OutKind::F32_STORE>, grid, block, 0, stream, p, ep, tm, tn);
+      hipLaunchKernelGGL((gemm_bf16_nt_pingpong<OutKind::F32_STORE, 2>), grid, block, 0, stream, p, ep, tm, tn);
       break;
     case OutKind::F32_ACC:
-      hipLaunchKernelGGL(gemm_bf16_nt_256x256_8w<OutKind::F32_ACC>, grid, block, 0, stream, p, ep, tm, tn);
+      hipLaunchKernelGGL((gemm_bf16_nt_pingpong<OutKind::F32_ACC, 2>), grid, block, 0, stream, p, ep, tm, tn);
       break;
   }
   return hipGetLastError();
@@ -390,7 +584,10 @@ hipError_t launch_gemm_bf16(const GemmProblem& p, const GemmEpilogue& ep, OutKin
   // 256x256 tiles when they give at least one full wave of workgroups on the
   // 256 CUs; 128x128 otherwise.
   const long big = (long)((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (big >= 256 && p.K % kBK == 0) return launch_256x256_8w(p, ep, kind, stream);
+  // the 8-wave kernel indexes operands with 32-bit element offsets
+  const bool fits32 = (int64_t)p.M * p.lda < ((int64_t)1 << 31) &&
+                      (int64_t)p.N * p.ldb < ((int64_t)1 << 31);
+  if (big >= 256 && p.K % kBK == 0 && fits32) return launch_256x256_8w(p, ep, kind, stream);
   if (big >= 256) return launch_tile<256, 256, 2, 2>(p, ep, kind, stream);
   return launch_tile<128, 128, 2, 2>(p, ep, kind, stream);
 }
