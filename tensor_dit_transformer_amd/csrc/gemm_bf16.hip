@@ -364,8 +364,9 @@ gemm_bf16_nt_256x256_8w(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n
 // lane), the other issues the 32 MFMAs of the tile it read in the previous
 // phase.  Phase 2k: group 0 reads tile k, group 1 multiplies tile k-1;
 // phase 2k+1: group 0 multiplies tile k, group 1 reads tile k.  Tile k+1 is
-// fetched global -> LDS (half by each group) at the start of phase 2k into
-// the stage that held tile k-1, and waited for at the end of phase 2k+1.
+// fetched global -> LDS during phase 2k into the stage that held tile k-1
+// (group 0 after its LDS reads, group 1 spread through its MFMAs) and waited
+// for at the end of phase 2k+1.
 __device__ __forceinline__ void wg_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
@@ -406,31 +407,28 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
   const bf16* __restrict__ A = static_cast<const bf16*>(p.A);
   const bf16* __restrict__ B = static_cast<const bf16*>(p.B);
 
-  // global -> LDS: group g fetches A rows and B rows [128 g, 128 g + 128);
-  // wave instruction i of wave q covers 8 rows from 128 g + 32 q + 8 i.
-  int a_off[4], b_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 128 * g + 32 * q + 8 * i + (lane >> 3);
-    const int kc = swizzle(row, lane & 7);
-    a_off[i] = min(m0 + row, p.M - 1) * (int)p.lda + kc * 8;
-    b_off[i] = min(n0 + row, p.N - 1) * (int)p.ldb + kc * 8;
-  }
-  const int dst0 = (128 * g + 32 * q) * kRowChunks;
-  auto issue = [&](int kt) {
+  // global -> LDS.  Wave q's instruction pair i (one for A, one for B)
+  // covers 8 rows from 64 q + 8 i; group 0 fetches i < 4, group 1 i >= 4.
+  // Rows 64 q + 8 i + (lane >> 3): the swizzle depends only on i & 1.
+  const int row0 = 64 * q + (lane >> 3);
+  const int kc_even = swizzle(row0, lane & 7) * 8, kc_odd = swizzle(row0 + 8, lane & 7) * 8;
+  auto issue = [&](int kt, int first, int count) {
     const int k = kt * kBK;
     u32x4* sa = smem + (kt & 1) * BUF;
     u32x4* sb = sa + BM * kRowChunks;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i) {
+      if (i < first || i >= first + count) continue;
+      const int kc = (i & 1) ? kc_odd : kc_even;
+      const int a_off = min(m0 + row0 + 8 * i, p.M - 1) * (int)p.lda + kc + k;
+      const int b_off = min(n0 + row0 + 8 * i, p.N - 1) * (int)p.ldb + kc + k;
       __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(A + a_off[i] + k),
-          (void __attribute__((address_space(3)))*)(sa + dst0 + 64 * i), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+          (const void __attribute__((address_space(1)))*)(A + a_off),
+          (void __attribute__((address_space(3)))*)(sa + (64 * q + 8 * i) * kRowChunks), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(B + b_off[i] + k),
-          (void __attribute__((address_space(3)))*)(sb + dst0 + 64 * i), 16, 0, 0);
+          (const void __attribute__((address_space(1)))*)(B + b_off),
+          (void __attribute__((address_space(3)))*)(sb + (64 * q + 8 * i) * kRowChunks), 16, 0, 0);
+    }
   };
 
   const int a_row = 128 * g + (lane & 31);
@@ -458,27 +456,37 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  auto multiply = [&]() {
+  // The MFMAs of one tile; with load_kt >= 0, this wave's half of that
+  // tile's global -> LDS loads is issued one row block after each k-step, so
+  // a load that waits at issue holds up at most 8 MFMAs.
+  auto multiply = [&](int load_kt) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+      if (load_kt >= 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(load_kt, 4 + s, 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
 
   const int nk = p.K / kBK;
-  issue(0);
+  issue(0, 4 * g, 4);                     // first tile: each group half of it
   wait_vmem();
   wg_barrier();
   if (g == 0) {
     for (int kt = 0; kt < nk; ++kt) {
       const bool more = kt + 1 < nk;
-      if (more) issue(kt + 1);
       read_tile(kt);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) issue(kt + 1, 0, 4);      // group 0's half, after its LDS reads
       wg_barrier();                       // end of phase 2 kt
-      multiply();
+      multiply(-1);
       if (more) wait_vmem();
       wg_barrier();                       // end of phase 2 kt + 1
     }
@@ -486,14 +494,14 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
   } else {
     for (int kt = 0; kt < nk; ++kt) {
       const bool more = kt + 1 < nk;
-      if (more) issue(kt + 1);
-      if (kt > 0) multiply();             // tile kt - 1
+      if (kt > 0) multiply(more ? kt + 1 : -1);   // tile kt - 1, loading tile kt + 1
+      else if (more) issue(kt + 1, 4, 4);
       wg_barrier();                       // end of phase 2 kt
       read_tile(kt);
       if (more) wait_vmem();
       wg_barrier();                       // end of phase 2 kt + 1
     }
-    multiply();
+    multiply(-1);
     wg_barrier();
   }
 
