@@ -17,12 +17,13 @@
 //     of its query are lane-local (plus one exchange with lane ^ 32).
 //   * Output is accumulated transposed too, O^T += V^T P^T: the bf16 P^T
 //     B-operand is the score accumulator itself, converted in registers; the
-//     A-operand is V^T, stored in LDS key-contiguous with the key order
-//     inside every 16 keys permuted (bits 2 and 3 swapped) so that the 8
-//     keys a lane needs are one 16-byte read.
-//   * K and V tiles of 64 keys are fetched one tile ahead into registers and
-//     written to a double-buffered LDS (padded rows, conflict-free reads);
-//     one barrier per tile.
+//     V^T A-operand is read from row-major V with the transposing LDS read
+//     ds_read_b64_tr_b16 (in each 16-lane group, source lane 4 r + c points
+//     at V[k + r][d + 4 c] and lane i receives V[k + e][d + i], e = 0..3).
+//   * K and V tiles of 64 keys go global -> LDS directly
+//     (global_load_lds_dwordx4), one tile ahead, into a double-buffered LDS
+//     with 256-byte rows and an XOR chunk swizzle that keeps both the K reads
+//     and the transposed V reads conflict-free; one barrier per tile.
 //   * Softmax runs in the exp2 domain with few vector instructions per
 //     score: one FMA (scale folded in) and one exp2; the row sum is a bf16
 //     dot2 over the packed weights; the accumulator is rescaled by
@@ -39,18 +40,20 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;            // head dim
 constexpr int kBQ = 128;           // queries per workgroup
 constexpr int kBKV = 64;           // keys per tile
-constexpr int kKPitch = kD + 8;    // bf16 per K row in LDS (272 bytes)
-constexpr int kVPitch = kBKV + 8;  // bf16 per V^T row in LDS (144 bytes)
+constexpr int kRowChunks = kD / 8; // 16-byte chunks per K or V row (256 bytes)
 
-// Position of key k (0..63) in a V^T row: swap bits 2 and 3.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
+// LDS position of 16-byte chunk c of K/V tile row r: c ^ f(r), with f a
+// bijection on 16 consecutive rows (conflict-free K reads: 16 rows, one
+// chunk) that also gives 4 aligned rows distinct values of one parity
+// (conflict-free transposed V reads: 4 rows, two adjacent chunks).
+__device__ __forceinline__ int swz(int r) { return ((r << 1) | ((r >> 3) & 1)) & 15; }
 
 // Slack (log2 domain) the running max may trail the true row max before the
 // accumulator is rescaled.  Softmax is invariant to the reference value, so
@@ -61,20 +64,23 @@ constexpr float kRescaleSlack = 8.0f;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <bool MASKED>
-__device__ __forceinline__ void attn_tile(const bf16* __restrict__ sKb, const bf16* __restrict__ sVb,
+__device__ __forceinline__ void attn_tile(const u32x4* __restrict__ sK, const u32x4* __restrict__ sV,
                                           const bf16x8 (&qf)[kD / 16], f32x16 (&acc_o)[kD / 32],
                                           float& m_ref, float& l_run, int key0, int T,
-                                          float scale_log2, int l32, int half) {
-  // S^T for keys 32 c .. 32 c + 31 of the tile (raw scores)
+                                          float scale_log2, int lane) {
+  const int half = lane >> 5, l32 = lane & 31;
+  // S^T for keys 32 c .. 32 c + 31 of the tile (raw scores): A = K rows
   f32x16 s[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[c][e] = 0.0f;
-    const bf16* kb = sKb + (32 * c + l32) * kKPitch + 8 * half;
+    const int row = 32 * c + l32;
+    const u32x4* kb = sK + row * kRowChunks;
+    const int f = swz(row);
 #pragma unroll
     for (int st = 0; st < kD / 16; ++st) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + 16 * st);
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, kb[(2 * st + half) ^ f]);
       s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[c], 0, 0, 0);
     }
   }
@@ -120,16 +126,34 @@ __device__ __forceinline__ void attn_tile(const bf16* __restrict__ sKb, const bf
       pb[c][e >> 3][e & 7] = pp[0];
       pb[c][e >> 3][(e & 7) + 1] = pp[1];
     }
-  // O^T += V^T P^T over the tile's 4 steps of 16 keys
+  // O^T += V^T P^T.  The P^T operand element j of this lane is key
+  // 8 (j / 4) + 4 half + (j % 4) of each 16-key step; the V^T operand is read
+  // transposed from row-major V: in each 16-lane group, source lane 4 r + cc
+  // points at V[key0 + r][d0 + 4 cc], and lane i of the group receives
+  // V[key0 + e][d0 + i], e = 0..3 -- keys 4 half .. + 3 (first read) and
+  // 8 + 4 half .. + 3 (second read), dim = 32 t + (lane & 31).
+  const int gi = lane & 15, r = gi >> 2, cc = gi & 3;
+  const int keyA = 4 * half + r, keyB = keyA + 8;
+  const int fA = swz(keyA), fB = swz(keyB);
+  const int dsub = 16 * ((lane >> 4) & 1) + 4 * cc;      // dim within the 32-dim tile
+  const int off8 = (dsub & 7) * 2;                        // byte offset in the chunk
 #pragma unroll
   for (int t = 0; t < kD / 32; ++t) {
-    const bf16* vb = sVb + (32 * t + l32) * kVPitch + 8 * half;
+    const int lchunk = (32 * t + dsub) >> 3;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vb + 32 * c + 16 * u);
-        acc_o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c][u], acc_o[t], 0, 0, 0);
+        const int kb = 32 * c + 16 * u;
+        const char* pa = reinterpret_cast<const char*>(sV + (kb + keyA) * kRowChunks + (lchunk ^ fA)) + off8;
+        const char* pbp = reinterpret_cast<const char*>(sV + (kb + keyB) * kRowChunks + (lchunk ^ fB)) + off8;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(pa));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(pbp));
+        const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc_o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pb[c][u],
+                                                          acc_o[t], 0, 0, 0);
       }
   }
 }
@@ -139,10 +163,11 @@ __device__ __forceinline__ void attn_tile(const bf16* __restrict__ sKb, const bf
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict__ o,
                    int64_t ldo, int T, int heads, float scale_log2) {
-  __shared__ bf16 sK[2][kBKV * kKPitch];
-  __shared__ bf16 sVt[2][kD * kVPitch];
+  __shared__ u32x4 sK[2][kBKV * kRowChunks];
+  __shared__ u32x4 sV[2][kBKV * kRowChunks];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int head = blockIdx.y;
   const int q0 = blockIdx.x * kBQ + wave * 32;
   const int Dr = heads * kD;
@@ -160,45 +185,22 @@ attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict
       qf[s] = *reinterpret_cast<const bf16x8*>(Qg + row * ldqkv + 16 * s + 8 * half);
   }
 
-  // K tile loader: chunk (row (tid >> 4) + 16 i, 16-byte column tid & 15)
-  const int k_row = tid >> 4, k_c = tid & 15;
-  // V tile loader: key pair (tid & 31), dim chunk (tid >> 5) + 8 i
-  const int v_pair = tid & 31, v_c = tid >> 5;
-  u32x4 rk[4];
-  u32x4 rv[2][2];
-
-  auto gload = [&](int kt) {
+  // K and V tiles go global -> LDS directly: wave instruction i fills 1 KB =
+  // tile rows 4 (4 wave + i) .. + 3; lane writes physical chunk lane & 15 of
+  // row + (lane >> 4), which holds logical chunk (lane & 15) ^ swz(row).
+  auto issue = [&](int kt, int buf) {
     const int k0 = kt * kBKV;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t row = min(k0 + k_row + 16 * i, T - 1);
-      rk[i] = *reinterpret_cast<const u32x4*>(Kg + row * ldqkv + 8 * k_c);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = v_c + 8 * i;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int64_t row = min(k0 + 2 * v_pair + t, T - 1);
-        rv[i][t] = *reinterpret_cast<const u32x4*>(Vg + row * ldqkv + 8 * c);
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&sK[buf][(k_row + 16 * i) * kKPitch + 8 * k_c]) = rk[i];
-    const int pos = vt_pos(2 * v_pair);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = v_c + 8 * i;
-      const u16x8 a = __builtin_bit_cast(u16x8, rv[i][0]);
-      const u16x8 b = __builtin_bit_cast(u16x8, rv[i][1]);
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const unsigned int w = (unsigned int)a[jj] | ((unsigned int)b[jj] << 16);
-        *reinterpret_cast<unsigned int*>(&sVt[buf][(8 * c + jj) * kVPitch + pos]) = w;
-      }
+      const int rr = 4 * (4 * wave + i) + (lane >> 4);
+      const int c = (lane & 15) ^ swz(rr);
+      const int64_t row = min(k0 + rr, T - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(Kg + row * ldqkv + 8 * c),
+          (void __attribute__((address_space(3)))*)(&sK[buf][64 * (4 * wave + i)]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(Vg + row * ldqkv + 8 * c),
+          (void __attribute__((address_space(3)))*)(&sV[buf][64 * (4 * wave + i)]), 16, 0, 0);
     }
   };
 
@@ -211,19 +213,16 @@ attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict
 
   const int nkt = (T + kBKV - 1) / kBKV;
   const int nfull = T / kBKV;  // tiles with every key valid
-  gload(0);
-  sstore(0);
+  issue(0, 0);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) gload(kt + 1);
+    if (kt + 1 < nkt) issue(kt + 1, buf ^ 1);
     if (kt < nfull)
-      attn_tile<false>(sK[buf], sVt[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, scale_log2, l32, half);
+      attn_tile<false>(sK[buf], sV[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, scale_log2, lane);
     else
-      attn_tile<true>(sK[buf], sVt[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, scale_log2, l32, half);
-    if (more) sstore(buf ^ 1);
-    __syncthreads();
+      attn_tile<true>(sK[buf], sV[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, scale_log2, lane);
+    __syncthreads();  // tile kt + 1 landed (this wave's DMA) and every wave is done with buf
   }
 
   // normalise and store: lane holds query q0 + l32, dims 32 t + 8 (e/4) + 4 half + (e%4)

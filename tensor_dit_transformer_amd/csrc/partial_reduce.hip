@@ -4,10 +4,10 @@
 //   out[r, c] = ((p_0[r, c] + p_1[r, c]) + ... + p_{P-1}[r, c]) + b_0[c] + ...
 // in fp32, rank order fixed, so the result is deterministic.
 //
-// Pure HBM streaming (0.2 FLOP/byte): every thread moves UNROLL float4
-// (16-byte) elements spaced one workgroup apart, so each load instruction is
-// fully coalesced and every thread has P * UNROLL independent loads in
-// flight.  Partials are read and the output written with non-temporal hints:
+// Pure HBM streaming (0.2 FLOP/byte): one float4 (16-byte) element per
+// thread and many small workgroups; each thread has its P loads in flight at
+// once.  (Measured at 4 x 16384 x 6144: one element per thread streams
+// ~6.6 TB/s alone, two ~6.5, four ~6.0, eight collapse.)  Partials are read and the output written with non-temporal hints:
 // none of it is reused, so it should not displace L2 / MALL contents.
 #include "tp_kernels.h"
 
@@ -16,7 +16,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 1;
 
 template <bool CONTIG>
 __global__ void __launch_bounds__(kThreads) partial_reduce_kernel(ReduceArgs a) {
