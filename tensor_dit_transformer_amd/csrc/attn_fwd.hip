@@ -8,8 +8,9 @@
 // of the packed qkv tensor [T, 3*Dr].
 //
 // Design:
-//   * grid = (ceil(T/128), heads); 4 waves per workgroup, 32 queries per wave,
-//     <= 256 VGPRs so two workgroups share a CU (two waves per SIMD).
+//   * 32 queries per wave; 4-wave workgroups (two per CU) or, for long
+//     sequences, 8-wave workgroups sharing each K/V tile among 256 queries;
+//     <= 256 VGPRs so two waves share each SIMD.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (A = a 32-key slab of K from LDS, B = the
 //     wave's Q^T held in registers for the whole kernel).  In the 32x32
@@ -45,7 +46,6 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;            // head dim
-constexpr int kBQ = 128;           // queries per workgroup
 constexpr int kBKV = 64;           // keys per tile
 constexpr int kRowChunks = kD / 8; // 16-byte chunks per K or V row (256 bytes)
 
@@ -63,11 +63,15 @@ constexpr float kRescaleSlack = 8.0f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-template <bool MASKED>
+// One 64-key tile for one wave.  dma(j), j = 0..7, issues this wave's share
+// of the next tile's global -> LDS loads; the calls are spread over the
+// tile's 32 MFMAs (one per 4) so a load that waits at issue delays only a
+// few MFMAs instead of the whole tile.
+template <bool MASKED, class Dma>
 __device__ __forceinline__ void attn_tile(const u32x4* __restrict__ sK, const u32x4* __restrict__ sV,
                                           const bf16x8 (&qf)[kD / 16], f32x16 (&acc_o)[kD / 32],
                                           float& m_ref, float& l_run, int key0, int T,
-                                          float scale_log2, int lane) {
+                                          float scale_log2, int lane, Dma&& dma) {
   const int half = lane >> 5, l32 = lane & 31;
   // S^T for keys 32 c .. 32 c + 31 of the tile (raw scores): A = K rows
   f32x16 s[2];
@@ -82,6 +86,11 @@ __device__ __forceinline__ void attn_tile(const u32x4* __restrict__ sK, const u3
     for (int st = 0; st < kD / 16; ++st) {
       const bf16x8 ka = __builtin_bit_cast(bf16x8, kb[(2 * st + half) ^ f]);
       s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[c], 0, 0, 0);
+      if ((st & 3) == 3) {
+        __builtin_amdgcn_sched_barrier(0);
+        dma(2 * c + (st >> 2));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   if constexpr (MASKED) {
@@ -155,21 +164,30 @@ __device__ __forceinline__ void attn_tile(const u32x4* __restrict__ sK, const u3
         acc_o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pb[c][u],
                                                           acc_o[t], 0, 0, 0);
       }
+    __builtin_amdgcn_sched_barrier(0);
+    dma(4 + t);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Two workgroups per CU (<= 256 VGPRs per wave): each SIMD runs two waves, so
-// one wave's softmax arithmetic overlaps the other's matrix instructions.
-__global__ void __launch_bounds__(256, 2)
+// NW waves x 32 queries per workgroup.  NW = 4: two workgroups per CU;
+// NW = 8: one.  Either way <= 256 VGPRs per wave and two waves per SIMD, so
+// one wave's softmax arithmetic overlaps another's matrix instructions.  The
+// 8-wave form shares each K/V tile among 256 queries, halving the tile
+// traffic per query; it is used when the sequence gives enough workgroups.
+template <int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
 attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict__ o,
                    int64_t ldo, int T, int heads, float scale_log2) {
+  constexpr int BQ = 32 * NW;
+  constexpr int PER_WAVE = 32 / NW;     // 1 KB K/V loads per wave per tile
   __shared__ u32x4 sK[2][kBKV * kRowChunks];
   __shared__ u32x4 sV[2][kBKV * kRowChunks];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int head = blockIdx.y;
-  const int q0 = blockIdx.x * kBQ + wave * 32;
+  const int q0 = blockIdx.x * BQ + wave * 32;
   const int Dr = heads * kD;
   const bf16* Qg = qkv + head * kD;
   const bf16* Kg = qkv + Dr + head * kD;
@@ -185,23 +203,19 @@ attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict
       qf[s] = *reinterpret_cast<const bf16x8*>(Qg + row * ldqkv + 16 * s + 8 * half);
   }
 
-  // K and V tiles go global -> LDS directly: wave instruction i fills 1 KB =
-  // tile rows 4 (4 wave + i) .. + 3; lane writes physical chunk lane & 15 of
-  // row + (lane >> 4), which holds logical chunk (lane & 15) ^ swz(row).
-  auto issue = [&](int kt, int buf) {
-    const int k0 = kt * kBKV;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 4 * (4 * wave + i) + (lane >> 4);
-      const int c = (lane & 15) ^ swz(rr);
-      const int64_t row = min(k0 + rr, T - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(Kg + row * ldqkv + 8 * c),
-          (void __attribute__((address_space(3)))*)(&sK[buf][64 * (4 * wave + i)]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(Vg + row * ldqkv + 8 * c),
-          (void __attribute__((address_space(3)))*)(&sV[buf][64 * (4 * wave + i)]), 16, 0, 0);
-    }
+  // K and V tiles go global -> LDS directly.  Load n (0..31) of a tile fills
+  // 1 KB = tile rows 4 (n & 15) .. + 3 of K (n < 16) or V; lane writes
+  // physical chunk lane & 15 of its row, which holds logical chunk
+  // (lane & 15) ^ swz(row).  Wave w issues loads w * PER_WAVE .. + PER_WAVE-1.
+  auto load = [&](int kt, int buf, int n) {
+    const int blk = n & 15;
+    const int rr = 4 * blk + (lane >> 4);
+    const int c = (lane & 15) ^ swz(rr);
+    const int64_t row = min(kt * kBKV + rr, T - 1);
+    const bf16* src = (n < 16 ? Kg : Vg) + row * ldqkv + 8 * c;
+    u32x4* dst = (n < 16 ? sK[buf] : sV[buf]) + 64 * blk;
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                     (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
   };
 
   f32x16 acc_o[kD / 32];
@@ -213,15 +227,25 @@ attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict
 
   const int nkt = (T + kBKV - 1) / kBKV;
   const int nfull = T / kBKV;  // tiles with every key valid
-  issue(0, 0);
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) load(0, 0, wave * PER_WAVE + j);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nkt) issue(kt + 1, buf ^ 1);
+    const bool more = kt + 1 < nkt;
+    // slot j of 8 in the tile carries load j * PER_WAVE / 8 ... spread evenly
+    auto dma = [&](int j) {
+      if (!more) return;
+      if constexpr (PER_WAVE == 8) {
+        load(kt + 1, buf ^ 1, wave * 8 + j);
+      } else {
+        if ((j & 1) == 0) load(kt + 1, buf ^ 1, wave * PER_WAVE + (j >> 1));
+      }
+    };
     if (kt < nfull)
-      attn_tile<false>(sK[buf], sV[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, scale_log2, lane);
+      attn_tile<false>(sK[buf], sV[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, scale_log2, lane, dma);
     else
-      attn_tile<true>(sK[buf], sV[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, scale_log2, lane);
+      attn_tile<true>(sK[buf], sV[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, scale_log2, lane, dma);
     __syncthreads();  // tile kt + 1 landed (this wave's DMA) and every wave is done with buf
   }
 
@@ -248,10 +272,18 @@ attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict
 hipError_t launch_attn_fwd_bf16_d128(const void* qkv, int64_t ldqkv, void* o, int64_t ldo,
                                      int T, int heads, hipStream_t stream) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kD);
-  const dim3 grid((T + kBQ - 1) / kBQ, heads), block(256);
-  hipLaunchKernelGGL(attn_fwd_bf16_d128, grid, block, 0, stream,
-                     static_cast<const bf16*>(qkv), ldqkv, static_cast<bf16*>(o), ldo, T, heads,
-                     scale_log2);
+  // 8-wave workgroups when they still give at least two per CU's worth of
+  // work (256 CUs), 4-wave ones otherwise.
+  const long wg8 = (long)((T + 255) / 256) * heads;
+  if (wg8 >= 512) {
+    const dim3 grid((T + 255) / 256, heads), block(512);
+    hipLaunchKernelGGL(attn_fwd_bf16_d128<8>, grid, block, 0, stream, static_cast<const bf16*>(qkv),
+                       ldqkv, static_cast<bf16*>(o), ldo, T, heads, scale_log2);
+  } else {
+    const dim3 grid((T + 127) / 128, heads), block(256);
+    hipLaunchKernelGGL(attn_fwd_bf16_d128<4>, grid, block, 0, stream, static_cast<const bf16*>(qkv),
+                       ldqkv, static_cast<bf16*>(o), ldo, T, heads, scale_log2);
+  }
   return hipGetLastError();
 }
 

@@ -193,6 +193,29 @@ def test_large_rowwise_store_and_accumulate_paths():
     close_all(shards)
 
 
+@pytest.mark.parametrize("T,heads", [(5500, 24), (4608, 6)])
+def test_attention_long_sequences_both_workgroup_shapes(T, heads):
+    """T=5500 x 24 heads takes the 256-query (8-wave) workgroups with a
+    ragged last tile; 4608 x 6 takes the 128-query ones.  Seeded packed qkv,
+    oracle on sampled query rows (each against all keys)."""
+    w = Workload(f"attn_T{T}_H{heads}", T, heads * 128, heads, 128, 0, 1, "bf16")
+    inp = tp_inputs.make_inputs(w, seed=12, tokens=8)      # weights only matter for create
+    s = H.create_shards(dataclass_tokens(w, 8), inp)[0]
+    Dr = s.d_r
+    qkv_v, qkv_b = tp_inputs.random_matrix((T, 3 * Dr), seed=13, std=1.5)
+    qkv = torch.from_numpy(qkv_b.view(np.int16)).view(torch.bfloat16).cuda()
+    o = torch.empty((T, Dr), dtype=torch.bfloat16, device="cuda")
+    tp.tp_attn_heads(s, T, qkv, o)
+    torch.cuda.synchronize()
+    rows = tp_inputs.sample_rows(T, 40, seed=14)
+    q64 = qkv_v.astype(np.float64)
+    ref = O.to_bf16_rne(O.attention_rows(q64[rows, :Dr], q64[:, Dr:2 * Dr], q64[:, 2 * Dr:], heads, 128))
+    e = H.rel_err(H.as_f64(o[rows]), ref)
+    say(f"attention T={T} heads={heads}: {e:.2e}")
+    assert e <= H.TOL["bf16"]
+    close_all([s])
+
+
 def test_zero_tokens_is_a_no_op():
     w = Workload("zero", 8, 256, 2, 128, 512, 2, "bf16")
     inp = tp_inputs.make_inputs(w, seed=1)
