@@ -8,9 +8,11 @@
 // of the packed qkv tensor [T, 3*Dr].
 //
 // Design:
-//   * 32 queries per wave; 4-wave workgroups (two per CU) or, for long
-//     sequences, 8-wave workgroups sharing each K/V tile among 256 queries;
-//     <= 256 VGPRs so two waves share each SIMD.
+//   * 32 queries per wave, <= 256 VGPRs so two waves share each SIMD.  Short
+//     sequences: 4-wave workgroups, two per CU.  Long sequences: the
+//     software-pipelined form below, 8-wave workgroups sharing each K/V tile
+//     among 256 queries, in which each wave overlaps the next tile's score
+//     MFMAs with this tile's softmax.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (A = a 32-key slab of K from LDS, B = the
 //     wave's Q^T held in registers for the whole kernel).  In the 32x32
@@ -267,17 +269,246 @@ attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined form.  One wave per SIMD (4 waves, up to 512 registers
+// per lane), NQ sub-tiles of 32 queries per wave (K and V operands are read
+// once per wave and feed NQ MFMAs).  Within key tile j a wave issues the
+// score MFMAs of tile j+1 in the same straight-line block as the softmax of
+// tile j, interleaved about one MFMA per seven vector instructions, so the
+// matrix core and the vector ALU work at the same time inside one wave; then
+// the PV MFMAs of tile j.  Four LDS stages: iteration j reads K of tile j+1
+// and V of tile j, and fetches tile j+3 into the stage tile j-1 used, so
+// every tile's loads have two iterations to land.  Loads past the last tile
+// re-fetch the last tile (harmless, keeps the block branch-free), and the
+// scores computed in the final iteration are discarded.
+template <int N>
+__device__ __forceinline__ void barrier_keep_newest_loads() {
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int NQ, int NW>
+__global__ void __launch_bounds__(64 * NW, 1)
+attn_fwd_pipe(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict__ o, int64_t ldo,
+              int T, int heads, float scale_log2) {
+  constexpr int NSTAGE = 4;
+  constexpr int BQ = NW * 32 * NQ;
+  constexpr int PER_WAVE = 32 / NW;   // 1 KB loads per wave per tile
+  __shared__ u32x4 sK[NSTAGE][kBKV * kRowChunks];
+  __shared__ u32x4 sV[NSTAGE][kBKV * kRowChunks];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int head = blockIdx.y;
+  const int q0 = blockIdx.x * BQ + wave * 32 * NQ;
+  const int Dr = heads * kD;
+  const bf16* Qg = qkv + head * kD;
+  const bf16* Kg = qkv + Dr + head * kD;
+  const bf16* Vg = qkv + 2 * Dr + head * kD;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  bf16x8 qf[NQ][kD / 16];
+#pragma unroll
+  for (int a = 0; a < NQ; ++a) {
+    const int64_t row = min(q0 + 32 * a + l32, T - 1);
+#pragma unroll
+    for (int st = 0; st < kD / 16; ++st)
+      qf[a][st] = *reinterpret_cast<const bf16x8*>(Qg + row * ldqkv + 16 * st + 8 * half);
+  }
+
+  const int nkt = (T + kBKV - 1) / kBKV;
+  // Load n (0..31) of tile kt: K rows (n < 16) or V rows 4 (n & 15) .. + 3;
+  // wave w issues loads PER_WAVE w .. PER_WAVE (w + 1) - 1.
+  auto load_tile = [&](int kt) {
+    const int buf = kt % NSTAGE;
+    const int tt = min(kt, nkt - 1);
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int n = PER_WAVE * wave + j;
+      const int blk = n & 15;
+      const int rr = 4 * blk + (lane >> 4);
+      const int c = (lane & 15) ^ swz(rr);
+      const int64_t row = min(tt * kBKV + rr, T - 1);
+      const bf16* src = (n < 16 ? Kg : Vg) + row * ldqkv + 8 * c;
+      u32x4* dst = (n < 16 ? sK[buf] : sV[buf]) + 64 * blk;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                       (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
+    }
+  };
+
+  auto scores = [&](const u32x4* __restrict__ sKb, f32x16 (&s)[NQ][2]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int a = 0; a < NQ; ++a)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[a][c][e] = 0.0f;
+      const int row = 32 * c + l32;
+      const u32x4* kb = sKb + row * kRowChunks;
+      const int f = swz(row);
+#pragma unroll
+      for (int st = 0; st < kD / 16; ++st) {
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, kb[(2 * st + half) ^ f]);
+#pragma unroll
+        for (int a = 0; a < NQ; ++a)
+          s[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[a][st], s[a][c], 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc_o[NQ][kD / 32];
+#pragma unroll
+  for (int a = 0; a < NQ; ++a)
+#pragma unroll
+    for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc_o[a][t][e] = 0.0f;
+  float m_ref[NQ], l_run[NQ];
+#pragma unroll
+  for (int a = 0; a < NQ; ++a) { m_ref[a] = -INFINITY; l_run[a] = 0.0f; }
+
+  // V^T operand addressing (see attn_tile): per lane constants
+  const int gi = lane & 15, r = gi >> 2, cc = gi & 3;
+  const int keyA = 4 * half + r, keyB = keyA + 8;
+  const int fA = swz(keyA), fB = swz(keyB);
+  const int dsub = 16 * ((lane >> 4) & 1) + 4 * cc;
+  const int off8 = (dsub & 7) * 2;
+  const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
+
+  // One key tile: s_cur holds raw scores of tile kt; issues scores of kt + 1.
+  auto step = [&](int kt, f32x16 (&s_cur)[NQ][2], f32x16 (&s_nxt)[NQ][2]) {
+    if (kt * kBKV + kBKV > T) {  // last, partial tile: mask keys past T
+#pragma unroll
+      for (int a = 0; a < NQ; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kt * kBKV + 32 * c + 8 * (e >> 2) + 4 * half + (e & 3);
+            if (key >= T) s_cur[a][c][e] = -INFINITY;
+          }
+    }
+    load_tile(kt + 3);
+    scores(sK[(kt + 1) % NSTAGE], s_nxt);
+    bf16x8 pb[NQ][2][2];
+    float alpha[NQ];
+    bool rescale = false;
+#pragma unroll
+    for (int a = 0; a < NQ; ++a) {
+      float mloc = s_cur[a][0][0];
+#pragma unroll
+      for (int e = 1; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s_cur[a][0][e], s_cur[a][0][e + 1]));
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s_cur[a][1][e], s_cur[a][1][e + 1]));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;
+      const bool need = __builtin_amdgcn_ballot_w64(mloc > m_ref[a] + kRescaleSlack) != 0;
+      const float m_new = need ? fmaxf(m_ref[a], mloc) : m_ref[a];
+      alpha[a] = __builtin_amdgcn_exp2f(m_ref[a] - m_new);
+      m_ref[a] = m_new;
+      rescale |= need;
+      float l = l_run[a] * alpha[a];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[a][c][e], scale_log2, -m_new));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[a][c][e + 1], scale_log2, -m_new));
+          const bf16x2 pp = {static_cast<bf16>(p0), static_cast<bf16>(p1)};
+          l = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l, false);
+          pb[a][c][e >> 3][e & 7] = pp[0];
+          pb[a][c][e >> 3][(e & 7) + 1] = pp[1];
+        }
+      l_run[a] = l;
+    }
+    // interleave: the loads and K reads first, then one score MFMA per ~7
+    // vector instructions of the softmax
+    __builtin_amdgcn_sched_group_barrier(0x020, PER_WAVE, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+    for (int i = 0; i < 16 * NQ; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    }
+    if (rescale) {
+#pragma unroll
+      for (int a = 0; a < NQ; ++a)
+#pragma unroll
+        for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc_o[a][t][e] *= alpha[a];
+    }
+    // O^T += V^T P^T for tile kt
+    const u32x4* sVb = sV[kt % NSTAGE];
+#pragma unroll
+    for (int t = 0; t < kD / 32; ++t) {
+      const int lchunk = (32 * t + dsub) >> 3;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int kb = 32 * c + 16 * u;
+          const char* pa = reinterpret_cast<const char*>(sVb + (kb + keyA) * kRowChunks + (lchunk ^ fA)) + off8;
+          const char* pbp = reinterpret_cast<const char*>(sVb + (kb + keyB) * kRowChunks + (lchunk ^ fB)) + off8;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(pa));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(pbp));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int a = 0; a < NQ; ++a)
+            acc_o[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[a][c][u], acc_o[a][t], 0, 0, 0);
+        }
+    }
+    barrier_keep_newest_loads<PER_WAVE>();
+  };
+
+  load_tile(0);
+  load_tile(1);
+  load_tile(2);
+  __syncthreads();
+  f32x16 sa[NQ][2], sb[NQ][2];
+  scores(sK[0], sa);
+  int kt = 0;
+  for (; kt + 1 < nkt; kt += 2) {
+    step(kt, sa, sb);
+    step(kt + 1, sb, sa);
+  }
+  if (kt < nkt) step(kt, sa, sb);
+
+#pragma unroll
+  for (int a = 0; a < NQ; ++a) {
+    const float l_tot = l_run[a] + __shfl_xor(l_run[a], 32);
+    const float inv = 1.0f / l_tot;
+    const int q = q0 + 32 * a + l32;
+    if (q < T) {
+      bf16* orow = o + (int64_t)q * ldo + head * kD;
+#pragma unroll
+      for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(acc_o[a][t][4 * g + e] * inv);
+          *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * half) = v;
+        }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16_d128(const void* qkv, int64_t ldqkv, void* o, int64_t ldo,
                                      int T, int heads, hipStream_t stream) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kD);
-  // 8-wave workgroups when they still give at least two per CU's worth of
-  // work (256 CUs), 4-wave ones otherwise.
+  // Long sequences: the software-pipelined form in 256-query workgroups
+  // (one per CU), when that still gives two workgroups per CU over the
+  // launch; otherwise 128-query workgroups, two per CU.
   const long wg8 = (long)((T + 255) / 256) * heads;
   if (wg8 >= 512) {
     const dim3 grid((T + 255) / 256, heads), block(512);
-    hipLaunchKernelGGL(attn_fwd_bf16_d128<8>, grid, block, 0, stream, static_cast<const bf16*>(qkv),
+    hipLaunchKernelGGL((attn_fwd_pipe<1, 8>), grid, block, 0, stream, static_cast<const bf16*>(qkv),
                        ldqkv, static_cast<bf16*>(o), ldo, T, heads, scale_log2);
   } else {
     const dim3 grid((T + 127) / 128, heads), block(256);
