@@ -502,11 +502,11 @@ attn_fwd_pipe(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict__ o,
 hipError_t launch_attn_fwd_bf16_d128(const void* qkv, int64_t ldqkv, void* o, int64_t ldo,
                                      int T, int heads, hipStream_t stream) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kD);
-  // Long sequences: the software-pipelined form in 256-query workgroups
-  // (one per CU), when that still gives two workgroups per CU over the
-  // launch; otherwise 128-query workgroups, two per CU.
+  // Long sequences: the software-pipelined form in 256-query workgroups (one
+  // per CU), when they cover at least three quarters of the 256 CUs;
+  // otherwise 128-query workgroups, two per CU.
   const long wg8 = (long)((T + 255) / 256) * heads;
-  if (wg8 >= 512) {
+  if (wg8 >= 192) {
     const dim3 grid((T + 255) / 256, heads), block(512);
     hipLaunchKernelGGL((attn_fwd_pipe<1, 8>), grid, block, 0, stream, static_cast<const bf16*>(qkv),
                        ldqkv, static_cast<bf16*>(o), ldo, T, heads, scale_log2);

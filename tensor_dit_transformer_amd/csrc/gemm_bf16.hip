@@ -589,13 +589,14 @@ hipError_t launch_tile(const GemmProblem& p, const GemmEpilogue& ep, OutKind kin
 
 hipError_t launch_gemm_bf16(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
                             hipStream_t stream) {
-  // 256x256 tiles when they give at least one full wave of workgroups on the
-  // 256 CUs; 128x128 otherwise.
+  // 256x256 tiles when they fill at least half the 256 CUs (the 8-wave
+  // kernel beats four times as many 128x128 tiles even then); 128x128
+  // otherwise.
   const long big = (long)((p.M + 255) / 256) * ((p.N + 255) / 256);
   // the 8-wave kernel indexes operands with 32-bit element offsets
   const bool fits32 = (int64_t)p.M * p.lda < ((int64_t)1 << 31) &&
                       (int64_t)p.N * p.ldb < ((int64_t)1 << 31);
-  if (big >= 256 && p.K % kBK == 0 && fits32) return launch_256x256_8w(p, ep, kind, stream);
+  if (big >= 128 && p.K % kBK == 0 && fits32) return launch_256x256_8w(p, ep, kind, stream);
   if (big >= 256) return launch_tile<256, 256, 2, 2>(p, ep, kind, stream);
   return launch_tile<128, 128, 2, 2>(p, ep, kind, stream);
 }
