@@ -13,14 +13,19 @@ tensor" and its v0.43.0 Chinese twin "张量并行"; cited below as [TP page]):
   partial sum.  The pair is always colwise then rowwise, with one AllReduce at
   the block boundary.  Colwise Q/K/V give each rank a subset of heads.
 * §"Projeções fundidas" (融合投影): a packed Linear is sharded block by block,
-  never by one plain slice across the concatenation.
+  never by one plain slice across the concatenation; blocks [1, 1] for a
+  SwiGLU gate/up projection with equal halves, [1, 1, 1, 3, 3] for a fused
+  Q, K, V, gate, up projection at mlp_ratio 3, and stored row blocks
+  [inner_dim, mlp_hidden_dim] for a rowwise output projection over the
+  concatenated attention output and MLP hidden (the single-stream block).
 * §"Restrições e verificação" (约束与验证): tp_degree divides the head count;
   every packed block is divisible by tp_degree on its own; both are checked
   before any weight is touched.
 
 Readings where the pages are silent (all stated again in the design notes):
 * attention is softmax(Q K^T / sqrt(d)) V per head, non-causal, no mask;
-* the MLP activation is GELU with the tanh approximation;
+* the MLP activation is GELU with the tanh approximation, or SwiGLU
+  silu(gate) * up with gate the first half of the packed gate/up output;
 * a rank owns the contiguous head block [r*H/P, (r+1)*H/P) and the contiguous
   feature blocks [r*N/P, (r+1)*N/P) of each sharded dimension;
 * the rowwise bias is added once, after the partial sum;
@@ -42,7 +47,9 @@ __all__ = [
     "attention_head", "attention_heads", "check_config", "colwise_range",
     "rowwise_range", "packed_colwise_rows", "shard_weights", "rank_forward",
     "block_unsharded", "partial_reduce", "rowwise_bias",
-    "attention_rows", "colwise_rows_sampled",
+    "attention_rows", "colwise_rows_sampled", "silu", "swiglu", "MLP_ACTS",
+    "mlp_hidden", "packed_rowwise_cols", "single_stream_block",
+    "single_stream_rank", "single_stream_as_block",
 ]
 
 
@@ -98,6 +105,23 @@ def gelu_tanh(u) -> np.ndarray:
     0.5 * u * (1 + tanh(sqrt(2/pi) * (u + 0.044715 u^3)))."""
     u = np.asarray(u, dtype=np.float64)
     return 0.5 * u * (1.0 + np.tanh(_GELU_C * (u + _GELU_A * u * u * u)))
+
+
+def silu(u) -> np.ndarray:
+    """SiLU (swish): u * sigmoid(u) = u / (1 + exp(-u))."""
+    u = np.asarray(u, dtype=np.float64)
+    return u / (1.0 + np.exp(-u))
+
+
+def swiglu(gate, up) -> np.ndarray:
+    """SwiGLU combination of a gate and an up projection: silu(gate) * up."""
+    return silu(gate) * np.asarray(up, dtype=np.float64)
+
+
+# MLP activations: "gelu_tanh" (W_up is [F, D]) or "swiglu" (W_up packs the
+# gate and up projections as [W_gate; W_up], [2F, D], the [1, 1] packed
+# projection of [TP page, §Projeções fundidas]).
+MLP_ACTS = ("gelu_tanh", "swiglu")
 
 
 def softmax_rows(s) -> np.ndarray:
@@ -190,13 +214,31 @@ def packed_colwise_rows(block_sizes: Sequence[int], tp_degree: int, rank: int) -
     return np.concatenate(rows)
 
 
+def packed_rowwise_cols(block_sizes: Sequence[int], tp_degree: int, rank: int) -> np.ndarray:
+    """[TP page, §Projeções fundidas] dim-1 column indices a rank takes from
+    a rowwise Linear whose input is the concatenation of blocks of the given
+    absolute sizes (the stored packed row blocks, e.g. [inner_dim,
+    mlp_hidden_dim] for an output projection over attention output and MLP
+    hidden): its own slice of every block, in block order."""
+    cols: List[np.ndarray] = []
+    start = 0
+    for size in block_sizes:
+        if size % tp_degree:
+            raise ShardConfigError("divisibility", f"packed block {size} not divisible by {tp_degree}")
+        s = rowwise_range(size, tp_degree, rank)
+        cols.append(np.arange(start + s.start, start + s.stop))
+        start += size
+    return np.concatenate(cols)
+
+
 def shard_weights(wts: Dict[str, np.ndarray], tp_degree: int, rank: int,
-                  num_heads: int, head_dim: int) -> Dict[str, np.ndarray]:
+                  num_heads: int, head_dim: int, mlp_act: str = "gelu_tanh") -> Dict[str, np.ndarray]:
     """One rank's weight slices.  Colwise (dim 0): the packed Q|K|V weight with
-    blocks [1, 1, 1] and the MLP up-projection.  Rowwise (dim 1): the attention
-    out-projection and the MLP down-projection.  Rowwise biases are not
-    sharded (added once after the sum).  [TP page, §Colwise e rowwise;
-    §Projeções fundidas]"""
+    blocks [1, 1, 1] and the MLP up-projection (for SwiGLU the packed
+    [W_gate; W_up] with blocks [1, 1], so the slice is [gate_r; up_r]).
+    Rowwise (dim 1): the attention out-projection and the MLP
+    down-projection.  Rowwise biases are not sharded (added once after the
+    sum).  [TP page, §Colwise e rowwise; §Projeções fundidas]"""
     out: Dict[str, np.ndarray] = {}
     f64 = lambda a: np.asarray(a, dtype=np.float64)
     if "w_q" in wts:
@@ -208,12 +250,29 @@ def shard_weights(wts: Dict[str, np.ndarray], tp_degree: int, rank: int,
         out["b_qkv"] = b_qkv[rows]
         out["w_o"] = f64(wts["w_o"])[:, rowwise_range(HD, tp_degree, rank)]
     if "w_up" in wts:
-        F = wts["w_up"].shape[0]
-        c = colwise_range(F, tp_degree, rank)
-        out["w_up"] = f64(wts["w_up"])[c]
-        out["b_up"] = f64(wts["b_up"])[c]
+        F = wts["w_dn"].shape[1]
+        if mlp_act == "swiglu":
+            rows = packed_colwise_rows([F, F], tp_degree, rank)
+        else:
+            c = colwise_range(F, tp_degree, rank)
+            rows = np.arange(c.start, c.stop)
+        out["w_up"] = f64(wts["w_up"])[rows]
+        out["b_up"] = f64(wts["b_up"])[rows]
         out["w_dn"] = f64(wts["w_dn"])[:, rowwise_range(F, tp_degree, rank)]
     return out
+
+
+def mlp_hidden(x, w_up, b_up, mlp_act: str) -> np.ndarray:
+    """The MLP hidden activation from an (unsharded or colwise-sharded) up
+    projection: gelu_tanh(x W^T + b), or for SwiGLU with W = [W_gate; W_up]
+    (equal halves) silu(x W_gate^T + b_gate) * (x W_up^T + b_up)."""
+    u = linear(x, w_up, b_up)
+    if mlp_act == "swiglu":
+        n = u.shape[1] // 2
+        return swiglu(u[:, :n], u[:, n:])
+    if mlp_act != "gelu_tanh":
+        raise ValueError(mlp_act)
+    return gelu_tanh(u)
 
 
 # --------------------------------------------------------------------------
@@ -221,12 +280,14 @@ def shard_weights(wts: Dict[str, np.ndarray], tp_degree: int, rank: int,
 # --------------------------------------------------------------------------
 
 def rank_forward(x, wts: Dict[str, np.ndarray], tp_degree: int, rank: int,
-                 num_heads: int, head_dim: int, bf16: bool) -> Dict[str, np.ndarray]:
+                 num_heads: int, head_dim: int, bf16: bool,
+                 mlp_act: str = "gelu_tanh") -> Dict[str, np.ndarray]:
     """Everything rank ``rank`` computes, in order:
 
     qkv_r   = x W_qkv_r^T + b_qkv_r                  colwise  [T, 3*D_r]
     o_r     = attention over the rank's H/P heads     [T, D_r]
     h_r     = gelu_tanh(x W_up_r^T + b_up_r)          colwise  [T, F_r]
+              (SwiGLU: silu(x G_r^T + b_g) * (x U_r^T + b_u))
     p_attn  = o_r W_o_r^T                            rowwise partial [T, D]
     p_mlp   = h_r W_dn_r^T                           rowwise partial [T, D]
     p_block = p_attn + p_mlp                          (= [o_r | h_r] [W_o_r | W_dn_r]^T)
@@ -235,7 +296,7 @@ def rank_forward(x, wts: Dict[str, np.ndarray], tp_degree: int, rank: int,
     With ``bf16`` the stored activations qkv_r, o_r, h_r are rounded to
     bfloat16 (inputs are assumed bf16-representable already)."""
     rnd = to_bf16_rne if bf16 else (lambda a: np.asarray(a, dtype=np.float64))
-    s = shard_weights(wts, tp_degree, rank, num_heads, head_dim)
+    s = shard_weights(wts, tp_degree, rank, num_heads, head_dim, mlp_act)
     x = np.asarray(x, dtype=np.float64)
     res: Dict[str, np.ndarray] = {}
     parts = []
@@ -249,7 +310,7 @@ def rank_forward(x, wts: Dict[str, np.ndarray], tp_degree: int, rank: int,
         res["p_attn"] = linear(o, s["w_o"])
         parts.append(res["p_attn"])
     if "w_up" in s:
-        h = rnd(gelu_tanh(linear(x, s["w_up"], s["b_up"])))
+        h = rnd(mlp_hidden(x, s["w_up"], s["b_up"], mlp_act))
         res["h_r"] = h
         res["p_mlp"] = linear(h, s["w_dn"])
         parts.append(res["p_mlp"])
@@ -280,7 +341,7 @@ def partial_reduce(partials: Sequence[np.ndarray], bias=None) -> np.ndarray:
 
 
 def block_unsharded(x, wts: Dict[str, np.ndarray], num_heads: int, head_dim: int,
-                    bf16: bool) -> Dict[str, np.ndarray]:
+                    bf16: bool, mlp_act: str = "gelu_tanh") -> Dict[str, np.ndarray]:
     """The same block on one device, no sharding: the result tensor parallelism
     must reproduce.  [TP page, §Restrições e verificação: compare single-device
     output with the tensor-parallel output.]"""
@@ -297,7 +358,7 @@ def block_unsharded(x, wts: Dict[str, np.ndarray], num_heads: int, head_dim: int
         res["y_attn"] = linear(o, wts["w_o"], wts["b_o"])
         ys.append(res["y_attn"])
     if "w_up" in wts:
-        g = rnd(gelu_tanh(linear(x, wts["w_up"], wts["b_up"])))
+        g = rnd(mlp_hidden(x, wts["w_up"], wts["b_up"], mlp_act))
         res["g"] = g
         res["y_mlp"] = linear(g, wts["w_dn"], wts["b_dn"])
         ys.append(res["y_mlp"])
@@ -306,15 +367,94 @@ def block_unsharded(x, wts: Dict[str, np.ndarray], num_heads: int, head_dim: int
 
 
 # --------------------------------------------------------------------------
+# Single-stream block with fused projections [TP page, §Projeções fundidas]
+#
+# One input Linear W_in [3 HD + 2 F, D] packs Q, K, V, gate and up (blocks
+# [1, 1, 1, 3, 3] when F = 3 D); one output Linear W_out [D, HD + F] reads the
+# concatenation [attention output | SwiGLU hidden] (row blocks [HD, F]).
+# --------------------------------------------------------------------------
+
+def _single_stream_parts(u, sizes, num_heads_local, head_dim, rnd):
+    """Split the fused projection output by block sizes and run both halves
+    (attention over the heads present, SwiGLU over gate/up).  The stored
+    activations are q, k, v (the attention input), o and h; gate and up are
+    only the SwiGLU's operands."""
+    q_w, k_w, v_w, g_w, u_w = sizes
+    edges = np.cumsum([0, q_w, k_w, v_w, g_w, u_w])
+    q, k, v, gate, up = (u[:, edges[i]:edges[i + 1]] for i in range(5))
+    qkv = rnd(np.concatenate([q, k, v], axis=1))
+    q, k, v = qkv[:, :q_w], qkv[:, q_w:q_w + k_w], qkv[:, q_w + k_w:]
+    o = rnd(attention_heads(q, k, v, num_heads_local, head_dim))
+    h = rnd(swiglu(gate, up))
+    return qkv, o, h
+
+
+def single_stream_block(x, w_in, b_in, w_out, b_out, num_heads: int, head_dim: int,
+                        ffn: int, bf16: bool) -> Dict[str, np.ndarray]:
+    """The unsharded single-stream block: u = x W_in^T + b_in split into
+    q, k, v, gate, up; o = attention over all heads; h = silu(gate) * up;
+    y = [o | h] W_out^T + b_out.  With bf16 the stored activations q, k, v,
+    o, h are rounded to bfloat16."""
+    rnd = to_bf16_rne if bf16 else (lambda a: np.asarray(a, dtype=np.float64))
+    HD = num_heads * head_dim
+    u = linear(x, w_in, b_in)
+    qkv, o, h = _single_stream_parts(u, (HD, HD, HD, ffn, ffn), num_heads, head_dim, rnd)
+    y = linear(np.concatenate([o, h], axis=1), w_out, b_out)
+    return {"qkv": qkv, "o": o, "h": h, "y": y}
+
+
+def single_stream_rank(x, w_in, b_in, w_out, tp_degree: int, rank: int, num_heads: int,
+                       head_dim: int, ffn: int, bf16: bool) -> Dict[str, np.ndarray]:
+    """One rank of the single-stream block under PackedColwiseParallel on
+    W_in (its slice of each of the five blocks) and PackedRowwiseParallel on
+    W_out (its slice of each of the two row blocks): the rank's fused
+    q/k/v slice qkv_r, its heads' attention o_r, its SwiGLU hidden h_r and
+    its fp32 partial [o_r | h_r] W_out_r^T (no bias: added once after the
+    sum)."""
+    check_config(tp_degree, rank, num_heads * head_dim, num_heads, head_dim, ffn)
+    rnd = to_bf16_rne if bf16 else (lambda a: np.asarray(a, dtype=np.float64))
+    HD = num_heads * head_dim
+    rows = packed_colwise_rows([HD, HD, HD, ffn, ffn], tp_degree, rank)
+    cols = packed_rowwise_cols([HD, ffn], tp_degree, rank)
+    w_in = np.asarray(w_in, dtype=np.float64)
+    u = linear(x, w_in[rows], np.asarray(b_in, dtype=np.float64)[rows])
+    Dr, Fr = HD // tp_degree, ffn // tp_degree
+    qkv, o, h = _single_stream_parts(u, (Dr, Dr, Dr, Fr, Fr), num_heads // tp_degree, head_dim, rnd)
+    w_out_r = np.asarray(w_out, dtype=np.float64)[:, cols]
+    return {"qkv_r": qkv, "o_r": o, "h_r": h,
+            "partial": linear(np.concatenate([o, h], axis=1), w_out_r)}
+
+
+def single_stream_as_block(w_in, b_in, w_out, b_out, num_heads: int, head_dim: int,
+                           ffn: int) -> Dict[str, np.ndarray]:
+    """The single-stream weights in the separate-projection form of the block
+    (w_q, w_k, w_v, w_up = [W_gate; W_up], w_o, w_dn) with the output bias
+    carried as b_o and a zero b_dn."""
+    HD = num_heads * head_dim
+    e = np.cumsum([0, HD, HD, HD, 2 * ffn])
+    w_in, b_in, w_out = (np.asarray(a) for a in (w_in, b_in, w_out))
+    return {"w_q": w_in[e[0]:e[1]], "w_k": w_in[e[1]:e[2]], "w_v": w_in[e[2]:e[3]],
+            "b_q": b_in[e[0]:e[1]], "b_k": b_in[e[1]:e[2]], "b_v": b_in[e[2]:e[3]],
+            "w_up": w_in[e[3]:e[4]], "b_up": b_in[e[3]:e[4]],
+            "w_o": w_out[:, :HD], "b_o": np.asarray(b_out),
+            "w_dn": w_out[:, HD:], "b_dn": np.zeros_like(np.asarray(b_out))}
+
+
+# --------------------------------------------------------------------------
 # Row-sampled pieces for full-size checks (same definitions, fewer rows)
 # --------------------------------------------------------------------------
 
-def colwise_rows_sampled(x_rows, w, b=None, gelu: bool = False, bf16: bool = True) -> np.ndarray:
+def colwise_rows_sampled(x_rows, w, b=None, gelu: bool = False, bf16: bool = True,
+                         mlp_act: Optional[str] = None) -> np.ndarray:
     """A colwise projection evaluated only on some rows of x (each output row
-    depends only on its own input row)."""
-    y = linear(x_rows, w, b)
-    if gelu:
-        y = gelu_tanh(y)
+    depends only on its own input row); with mlp_act, the MLP hidden
+    activation of it."""
+    if mlp_act is not None:
+        y = mlp_hidden(x_rows, w, b, mlp_act)
+    else:
+        y = linear(x_rows, w, b)
+        if gelu:
+            y = gelu_tanh(y)
     return to_bf16_rne(y) if bf16 else y
 
 

@@ -13,8 +13,8 @@ float32 ``standard_normal`` scaled by the stated standard deviation):
     b_q, b_k, b_v ~ N(0, 0.01)                 [D]
     W_o ~ N(0, 0.02)                           [D, H*d]
     b_o ~ N(0, 0.01)                           [D]
-    W_up ~ N(0, 0.02)                          [F, D]
-    b_up ~ N(0, 0.01)                          [F]
+    W_up ~ N(0, 0.02)                          [F, D]  (SwiGLU: [2F, D] = [W_gate; W_up])
+    b_up ~ N(0, 0.01)                          [F]     (SwiGLU: [2F])
     W_dn ~ N(0, 0.02)                          [D, F]
     b_dn ~ N(0, 0.01)                          [D]
 
@@ -51,6 +51,7 @@ class Workload:
     tp_degree: int
     dtype: str          # "f32" or "bf16"
     description: str = ""
+    mlp_act: str = "gelu_tanh"   # or "swiglu" (packed gate/up, blocks [1, 1])
 
     @property
     def has_attn(self) -> bool:
@@ -77,7 +78,17 @@ C5_P2 = dataclasses.replace(C5_P4, name="block_bf16_T16384_D6144_H48_F18432_P2",
                             tp_degree=2,
                             description="bf16 full block, both rank shards then partial reduce")
 
-WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5_P4, C5_P2)}
+# Single-stream block with fused projections and a SwiGLU MLP at mlp_ratio 3:
+# the input projection packs Q, K, V, gate, up (blocks [1, 1, 1, 3, 3]) and the
+# output projection reads [attention output | hidden] (row blocks [6144, 18432]).
+C6 = Workload("single_swiglu_bf16_T4608_D6144_H48_F18432_P4", 4608, 6144, 48, 128, 18432, 4,
+              "bf16", "bf16 single-stream SwiGLU block shard, one rank of tp_degree 4",
+              mlp_act="swiglu")
+C7 = Workload("single_swiglu_bf16_T16384_D6144_H48_F18432_P4", 16384, 6144, 48, 128, 18432,
+              4, "bf16", "bf16 single-stream SwiGLU block, all 4 rank shards then partial reduce",
+              mlp_act="swiglu")
+
+WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5_P4, C5_P2, C6, C7)}
 
 
 def _shapes(w: Workload) -> Dict[str, tuple]:
@@ -89,7 +100,8 @@ def _shapes(w: Workload) -> Dict[str, tuple]:
                       b_q=(HD,), b_k=(HD,), b_v=(HD,),
                       w_o=(D, HD), b_o=(D,))
     if w.has_mlp:
-        shapes.update(w_up=(F, D), b_up=(F,), w_dn=(D, F), b_dn=(D,))
+        U = 2 * F if w.mlp_act == "swiglu" else F
+        shapes.update(w_up=(U, D), b_up=(U,), w_dn=(D, F), b_dn=(D,))
     return shapes
 
 
