@@ -17,6 +17,12 @@ for the kernel with the largest share of step time, from HIP events around
 each launch on the stream it runs on; "cpu_baseline" = the float64 oracle
 timed on the host cores on a bounded sample (rank 0's shard of the same
 block on the first 12288 tokens).
+
+--workload single_swiglu_bf16_T16384_D6144_H48_F18432_P4 times the
+single-stream variant of the same block instead: shards created from one
+packed input projection (Q, K, V, gate, up; blocks [1, 1, 1, 3, 3]) and one
+packed output projection over [inner_dim, mlp_hidden_dim], MLP activation
+SwiGLU fused into the colwise epilogue.
 """
 from __future__ import annotations
 
@@ -58,9 +64,9 @@ def load_traffic(kernel_key: str, source: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(tokens_sample: int = 12288):
-    """The oracle, as it stands, on rank 0 of the tp_degree-4 full block for
-    the first `tokens_sample` tokens (a shorter sequence of the same block)."""
+def cpu_baseline(w, tokens_sample: int = 12288):
+    """The oracle, as it stands, on rank 0 of workload `w` for the first
+    `tokens_sample` tokens (a shorter sequence of the same block)."""
     import numpy as np
     import oracle as O
     import tp_inputs
@@ -69,18 +75,40 @@ def cpu_baseline(tokens_sample: int = 12288):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    w = tp_inputs.C5_P4
+    tokens_sample = min(tokens_sample, w.tokens)
     inp = tp_inputs.make_inputs(w, seed=0, tokens=tokens_sample)
     t0 = time.perf_counter()
-    O.rank_forward(inp["x"], inp.values, w.tp_degree, 0, w.num_heads, w.head_dim, bf16=True)
+    O.rank_forward(inp["x"], inp.values, w.tp_degree, 0, w.num_heads, w.head_dim, bf16=True,
+                   mlp_act=w.mlp_act)
     dt = time.perf_counter() - t0
-    T, D, P = tokens_sample, w.hidden, w.tp_degree
-    Dr, Fr, Hr = D // P, w.ffn // P, w.num_heads // P
-    flops = 2 * T * D * (3 * Dr + Fr) + 4 * T * T * w.head_dim * Hr + 2 * T * (Dr + Fr) * D
+    T = tokens_sample
+    flops = sum(work for _src, work, bound in step_kernels(w, T).values() if bound == "mfma")
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"rank 0 of 4 of the full block (hidden 6144, 48 heads, ffn 18432) on "
-                      f"the first {T} tokens: {flops / 1e9:.0f} GFLOP fp64 in {dt:.1f} s",
+            "sample": f"rank 0 of {w.tp_degree} of {w.name} on the first {T} tokens: "
+                      f"{flops / 1e9:.0f} GFLOP fp64 in {dt:.1f} s",
             "seconds": round(dt, 2), "cpu_count": os.cpu_count()}
+
+
+def step_kernels(w, T):
+    """Kernels of one rank's pass, with algorithmic work per launch (FLOPs for
+    the MFMA kernels) and their bound."""
+    D, P, d = w.hidden, w.tp_degree, w.head_dim
+    Dr = D // P if w.has_attn else 0
+    Fr, Hr = w.ffn // P, w.num_heads // P
+    U = 2 * Fr if w.mlp_act == "swiglu" else Fr      # colwise MLP-in rows
+    kernels = {}
+    if w.has_attn and w.has_mlp:
+        kernels["colwise_qkv_up"] = ("gemm_bf16.hip", 2 * T * D * (3 * Dr + U), "mfma")
+        kernels["attention"] = ("attn_fwd.hip", 4 * T * T * d * Hr, "mfma")
+        kernels["rowwise_block_out"] = ("gemm_bf16.hip", 2 * T * (Dr + Fr) * D, "mfma")
+    elif w.has_attn:
+        kernels["colwise_qkv"] = ("gemm_bf16.hip", 2 * T * D * 3 * Dr, "mfma")
+        kernels["attention"] = ("attn_fwd.hip", 4 * T * T * d * Hr, "mfma")
+        kernels["rowwise_attn_out"] = ("gemm_bf16.hip", 2 * T * Dr * D, "mfma")
+    else:
+        kernels["colwise_mlp_up"] = ("gemm_bf16.hip", 2 * T * D * U, "mfma")
+        kernels["rowwise_mlp_down"] = ("gemm_bf16.hip", 2 * T * Fr * D, "mfma")
+    return kernels
 
 
 def main():
@@ -114,7 +142,10 @@ def main():
     log(f"[bench] generating inputs for {w.name}")
     t0 = time.time()
     inp = tp_inputs.make_inputs(w, seed=0)
-    shards = H.create_shards(w, inp)
+    # a single-stream SwiGLU block comes as a packed checkpoint (fused input
+    # and output projections)
+    packed = w.mlp_act == "swiglu" and w.has_attn
+    shards = H.create_shards(w, inp, packed=packed)
     x = H.to_device(inp, "x")
     biases = H.rowwise_biases(w, inp)
     del inp
@@ -124,18 +155,7 @@ def main():
     log(f"[bench] setup {time.time() - t0:.1f} s")
 
     # kernels of a step, with algorithmic work per launch
-    kernels = {}
-    if w.has_attn and w.has_mlp:
-        kernels["colwise_qkv_up"] = ("gemm_bf16.hip", 2 * T * D * (3 * Dr + Fr), "mfma")
-        kernels["attention"] = ("attn_fwd.hip", 4 * T * T * d * Hr, "mfma")
-        kernels["rowwise_block_out"] = ("gemm_bf16.hip", 2 * T * (Dr + Fr) * D, "mfma")
-    elif w.has_attn:
-        kernels["colwise_qkv"] = ("gemm_bf16.hip", 2 * T * D * 3 * Dr, "mfma")
-        kernels["attention"] = ("attn_fwd.hip", 4 * T * T * d * Hr, "mfma")
-        kernels["rowwise_attn_out"] = ("gemm_bf16.hip", 2 * T * Dr * D, "mfma")
-    else:
-        kernels["colwise_mlp_up"] = ("gemm_bf16.hip", 2 * T * D * Fr, "mfma")
-        kernels["rowwise_mlp_down"] = ("gemm_bf16.hip", 2 * T * Fr * D, "mfma")
+    kernels = step_kernels(w, T)
     reduce_bytes = (P + 1) * T * D * 4 + len(biases) * D * 4
     kernels["partial_reduce"] = ("partial_reduce.hip", reduce_bytes, "hbm")
 
@@ -237,7 +257,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle sample")
-        cpu = cpu_baseline()
+        cpu = cpu_baseline(w)
         log(f"[bench] oracle: {cpu['sample']}")
 
     out = {
@@ -256,7 +276,9 @@ def main():
         "mfma_peak_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "config": {"workload": w.name, "tokens": T, "hidden": D, "num_heads": w.num_heads,
                    "head_dim": d, "ffn": w.ffn, "tp_degree": P, "ranks_per_step": P,
-                   "step": "per rank: fused colwise QKV+up, attention, packed rowwise out; then partial reduce"},
+                   "mlp_act": w.mlp_act, "packed_checkpoint": packed,
+                   "step": "per rank: fused colwise QKV+MLP-in, attention, packed rowwise out; "
+                           "then partial reduce"},
         "roofline": roof,
         "kernels": per_kernel,
         "cpu_baseline": cpu,

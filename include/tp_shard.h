@@ -15,7 +15,9 @@
  *     the FFN out-projection); always colwise then rowwise, one AllReduce at
  *     the block boundary; colwise Q/K/V give each rank a subset of heads;
  *   - §"Projeções fundidas" (融合投影): a packed Linear is sharded block by
- *     block; a rowwise to_out may pack [inner_dim, mlp_hidden_dim];
+ *     block: [1, 1] for a SwiGLU gate/up projection, [1, 1, 1, 3, 3] for a
+ *     fused Q, K, V, gate, up projection at mlp_ratio 3; a rowwise to_out may
+ *     pack [inner_dim, mlp_hidden_dim];
  *   - §"Restrições e verificação" (约束与验证): tp_degree divides the head
  *     count and each packed block on its own, checked before any weight is
  *     touched;
@@ -23,7 +25,8 @@
  *     silently doing something else.
  *
  * Readings where the pages are silent: attention is softmax(Q K^T/sqrt(d)) V
- * per head, non-causal, unmasked; the MLP activation is GELU (tanh form);
+ * per head, non-causal, unmasked; the MLP activation is GELU (tanh form) or
+ * SwiGLU silu(gate) * up with the gate as the first packed half;
  * rank r owns heads [r*H/P, (r+1)*H/P) and the contiguous 1/P block of every
  * sharded feature dimension; the rowwise bias is added once, by the reduce.
  *
@@ -75,9 +78,17 @@ typedef enum tp_dtype {
   TP_BF16 = 1                /* bf16 activations and weights; fp32 accumulate */
 } tp_dtype;
 
+typedef enum tp_mlp_act {
+  TP_MLP_GELU_TANH = 0,      /* h = GELU-tanh(x W_up^T + b_up); W_up is [F, D] */
+  TP_MLP_SWIGLU = 1          /* h = silu(x W_gate^T + b_gate) * (x W_up^T + b_up); the
+                                in-projection packs [W_gate; W_up] as one [2F, D]
+                                weight (and [b_gate; b_up] as [2F]), sharded with
+                                blocks [1, 1] */
+} tp_mlp_act;
+
 typedef enum tp_layer {
   TP_QKV = 0,                /* colwise: packed [Q_r; K_r; V_r], blocks [1, 1, 1] */
-  TP_MLP_UP = 1,             /* colwise: FFN in-projection, fused bias + GELU-tanh */
+  TP_MLP_UP = 1,             /* colwise: FFN in-projection, fused bias + activation */
   TP_ATTN_OUT = 2,           /* rowwise: to_out.0 (attention out-projection) */
   TP_MLP_DOWN = 3,           /* rowwise: FFN out-projection */
   TP_BLOCK_OUT = 4           /* rowwise, packed over [inner_dim, ffn]: [o_r | h_r] */
@@ -93,20 +104,30 @@ typedef struct tp_block_config {
   int64_t head_dim;          /* d */
   int64_t ffn;               /* F */
   tp_dtype dtype;
+  tp_mlp_act mlp_act;        /* 0 = GELU-tanh */
 } tp_block_config;
 
 /* UNSHARDED weights in HOST memory, element type = config dtype (bf16 as raw
  * 16-bit patterns), row-major nn.Linear layout.  Only this rank's slices are
  * read and copied to the device; the arrays are not retained.  Biases may be
  * NULL (zero).  The rowwise biases (b_o, b_down) are not sharded: they are
- * added once after the partial sum, by tp_partial_reduce. */
+ * added once after the partial sum, by tp_partial_reduce.
+ *
+ * Packed checkpoints [TP page, §Projeções fundidas] need no copy: a fused
+ * input projection W_in = [W_q; W_k; W_v; W_gate; W_up] (blocks [1, 1, 1, 3, 3]
+ * at mlp_ratio 3 with SwiGLU) is passed as w_q = W_in, w_k = W_in + H*d*D,
+ * w_v = W_in + 2*H*d*D, w_up = W_in + 3*H*d*D (elements; biases alike), and a
+ * fused output projection W_out [D, H*d + F] over [inner_dim, mlp_hidden_dim]
+ * as w_o = W_out, w_down = W_out + H*d with ld_o = ld_down = H*d + F. */
 typedef struct tp_block_weights {
   const void *w_q, *w_k, *w_v;     /* [H*d, D] each */
   const void *b_q, *b_k, *b_v;     /* [H*d] each, nullable */
-  const void *w_o;                 /* [D, H*d] */
-  const void *w_up;                /* [F, D] */
-  const void *b_up;                /* [F], nullable */
-  const void *w_down;              /* [D, F] */
+  const void *w_o;                 /* [D, H*d], row stride ld_o */
+  const void *w_up;                /* [F, D]; SwiGLU: [2F, D] = [W_gate; W_up] */
+  const void *b_up;                /* [F] (SwiGLU: [2F]), nullable */
+  const void *w_down;              /* [D, F], row stride ld_down */
+  int64_t ld_o;                    /* row stride of w_o in elements; 0 = H*d */
+  int64_t ld_down;                 /* row stride of w_down in elements; 0 = F */
 } tp_block_weights;
 
 typedef struct tp_block_shard tp_block_shard;  /* opaque; owns the device weight slices */
@@ -116,16 +137,20 @@ typedef struct tp_block_shard tp_block_shard;  /* opaque; owns the device weight
  * reads only its own slice of each weight]:
  *   colwise (dim-0 rows):   W_qkv_r = [W_q[R_r,:]; W_k[R_r,:]; W_v[R_r,:]]  [3*D_r, D]
  *                           W_up_r  = W_up[C_r,:]                           [F_r, D]
+ *                 (SwiGLU:  [W_gate[C_r,:]; W_up[C_r,:]] = rows C_r and F + C_r of
+ *                           the packed [2F, D], stored with gate and up rows
+ *                           interleaved in blocks of 32)
  *   rowwise (dim-1 cols):   W_o_r   = W_o[:, R_r]                           [D, D_r]
  *                           W_dn_r  = W_down[:, C_r]                        [D, F_r]
  * with D_r = D/P, R_r = [r*D_r, (r+1)*D_r), F_r = F/P, C_r = [r*F_r, (r+1)*F_r).
  * Checks, in order, before any allocation [TP page, §Restrições e
- * verificação]: out != NULL (else TP_ERR_ARG); cfg, w != NULL; dtype known;
- * P >= 1 and 0 <= rank < P; D > 0, H >= 0, F >= 0, not both H and F zero,
- * d > 0 if H > 0 (TP_ERR_ARG); H*d == D, P | H, P | D (each Q/K/V block),
- * P | F (TP_ERR_DIVISIBILITY); D, D_r, F_r multiples of 8
- * (TP_ERR_UNSUPPORTED); the weights the enabled layers need are non-NULL
- * (TP_ERR_ARG).  On any error *out is set to NULL and nothing is allocated
+ * verificação]: out != NULL (else TP_ERR_ARG); cfg, w != NULL; dtype and
+ * mlp_act known; P >= 1 and 0 <= rank < P; D > 0, H >= 0, F >= 0, not both H
+ * and F zero, d > 0 if H > 0 (TP_ERR_ARG); H*d == D, P | H, P | D (each Q/K/V
+ * block), P | F (each gate/up block) (TP_ERR_DIVISIBILITY); D, D_r, F_r
+ * multiples of 8, and of 32 for F_r with SwiGLU (TP_ERR_UNSUPPORTED); the
+ * weights the enabled layers need are non-NULL, ld_o is 0 or >= H*d, ld_down
+ * is 0 or >= F (TP_ERR_ARG).  On any error *out is set to NULL and nothing is allocated
  * (or everything allocated so far is freed). */
 TP_API tp_status tp_block_shard_create(const tp_block_config *cfg, const tp_block_weights *w,
                                 tp_block_shard **out);
@@ -137,7 +162,8 @@ TP_API void tp_block_shard_destroy(tp_block_shard *shard);
 /* Colwise projection [TP page, §Colwise e rowwise]:
  *   y[t, n] = act( sum_k x[t, k] * W_r[n, k] + b_r[n] ),  t < tokens, n < N_r
  * layer TP_QKV:    N_r = 3*D_r, columns [Q_r | K_r | V_r], act = identity;
- * layer TP_MLP_UP: N_r = F_r, act = GELU-tanh.
+ * layer TP_MLP_UP: N_r = F_r, act = GELU-tanh, or with SwiGLU
+ *                  y[t, n] = silu(x W_gate_r[n]^T + b_gate_r[n]) * (x W_up_r[n]^T + b_up_r[n]).
  * x: device [tokens, D] (ldx >= D); y: device [tokens, N_r] (ldy >= N_r); both
  * in the config dtype.  tokens == 0 is a no-op; tokens < 0 is TP_ERR_ARG, as is
  * a layer that is not colwise or was not configured. */
@@ -149,6 +175,9 @@ TP_API tp_status tp_colwise_linear(tp_block_shard *shard, tp_layer layer, int64_
  * Q, K, V and MLP-in projection, sharded block by block):
  *   qkv[t, 0:3*D_r] = x W_qkv_r^T + b_qkv_r      (ldqkv >= 3*D_r)
  *   h  [t, 0:F_r]   = GELU-tanh(x W_up_r^T + b_up_r)  (ldh >= F_r)
+ *                     (SwiGLU: silu(x W_gate_r^T + b_gate_r) * (x W_up_r^T + b_up_r);
+ *                     with the [1, 1, 1, 3, 3]-style packing this is the whole
+ *                     fused single-stream input projection)
  * Needs both attention and MLP configured (else TP_ERR_ARG).  Results are
  * identical to TP_QKV followed by TP_MLP_UP. */
 TP_API tp_status tp_colwise_qkv_up(tp_block_shard *shard, int64_t tokens, const void *x, int64_t ldx,

@@ -9,7 +9,7 @@ ctypes binding (same entry-point names as the C ABI) and the build script.
 from .binding import (  # noqa: F401
     EXPORTED, LIB_PATH, TP_ATTN_OUT, TP_BF16, TP_BLOCK_OUT, TP_ERR_ARG,
     TP_ERR_DIVISIBILITY, TP_ERR_HIP, TP_ERR_OOM, TP_ERR_UNSUPPORTED, TP_F32,
-    TP_MLP_DOWN, TP_MLP_UP, TP_OK, TP_QKV, TpBlockConfig, TpBlockShard,
+    TP_MLP_DOWN, TP_MLP_GELU_TANH, TP_MLP_SWIGLU, TP_MLP_UP, TP_OK, TP_QKV, TpBlockConfig, TpBlockShard,
     TpBlockWeights, TpError, lib, make_config, status_string, tp_attn_heads,
     tp_block_shard_create, tp_block_shard_destroy, tp_colwise_linear,
     tp_colwise_qkv_up, tp_last_error_detail, tp_partial_reduce,

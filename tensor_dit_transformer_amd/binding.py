@@ -26,6 +26,9 @@ TP_ERR_OOM = -5
 # tp_dtype
 TP_F32 = 0
 TP_BF16 = 1
+# tp_mlp_act
+TP_MLP_GELU_TANH = 0
+TP_MLP_SWIGLU = 1
 # tp_layer
 TP_QKV = 0
 TP_MLP_UP = 1
@@ -44,14 +47,15 @@ class TpBlockConfig(ctypes.Structure):
     _fields_ = [("tp_degree", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("hidden", ctypes.c_int64), ("num_heads", ctypes.c_int64),
                 ("head_dim", ctypes.c_int64), ("ffn", ctypes.c_int64),
-                ("dtype", ctypes.c_int)]
+                ("dtype", ctypes.c_int), ("mlp_act", ctypes.c_int)]
 
 
 _WEIGHT_FIELDS = ("w_q", "w_k", "w_v", "b_q", "b_k", "b_v", "w_o", "w_up", "b_up", "w_down")
 
 
 class TpBlockWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS]
+    _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS] + [
+        ("ld_o", ctypes.c_int64), ("ld_down", ctypes.c_int64)]
 
 
 class TpError(RuntimeError):
@@ -156,6 +160,7 @@ class TpBlockShard:
         self.head_dim = cfg.head_dim
         self.ffn = cfg.ffn
         self.dtype = cfg.dtype
+        self.mlp_act = cfg.mlp_act
         P = cfg.tp_degree
         self.d_r = cfg.hidden // P if cfg.num_heads > 0 else 0
         self.f_r = cfg.ffn // P
@@ -176,36 +181,59 @@ class TpBlockShard:
 
 
 def make_config(tp_degree: int, rank: int, hidden: int, num_heads: int, head_dim: int,
-                ffn: int, dtype: int) -> TpBlockConfig:
-    return TpBlockConfig(tp_degree, rank, hidden, num_heads, head_dim, ffn, dtype)
+                ffn: int, dtype: int, mlp_act: int = TP_MLP_GELU_TANH) -> TpBlockConfig:
+    return TpBlockConfig(tp_degree, rank, hidden, num_heads, head_dim, ffn, dtype, mlp_act)
 
 
 def _weight_shapes(cfg: TpBlockConfig):
     D, HD, F = cfg.hidden, cfg.num_heads * cfg.head_dim, cfg.ffn
+    U = 2 * F if cfg.mlp_act == TP_MLP_SWIGLU else F
     return {"w_q": (HD, D), "w_k": (HD, D), "w_v": (HD, D), "b_q": (HD,), "b_k": (HD,),
-            "b_v": (HD,), "w_o": (D, HD), "w_up": (F, D), "b_up": (F,), "w_down": (D, F)}
+            "b_v": (HD,), "w_o": (D, HD), "w_up": (U, D), "b_up": (U,), "w_down": (D, F),
+            "w_in": (3 * HD + U, D), "b_in": (3 * HD + U,), "w_out": (D, HD + F)}
 
 
 def _host_weights(weights: Dict[str, np.ndarray], cfg: TpBlockConfig):
     """TpBlockWeights pointing at contiguous host arrays (kept alive by the
-    returned list).  bf16 arrays are uint16 bit patterns."""
+    returned list).  bf16 arrays are uint16 bit patterns.
+
+    Besides the separate projections, a packed checkpoint may be given as
+    ``w_in`` [3 H d + U, D] = [W_q; W_k; W_v; W_up-block] (with ``b_in``) and
+    ``w_out`` [D, H d + F] = [W_o | W_down]: the pointers then address the
+    blocks inside them (rows for w_in, columns with ld = H d + F for w_out)."""
     keep = []
     w = TpBlockWeights()
     want = np.uint16 if cfg.dtype == TP_BF16 else np.float32
+    es = np.dtype(want).itemsize
     shapes = _weight_shapes(cfg)
-    for name in _WEIGHT_FIELDS:
-        a = weights.get(name)
-        if a is None and name == "w_down":
-            a = weights.get("w_dn")
-        if a is None:
-            continue
-        a = np.ascontiguousarray(a)
+    D, HD, F = cfg.hidden, cfg.num_heads * cfg.head_dim, cfg.ffn
+
+    def host(name, key=None):
+        a = np.ascontiguousarray(weights[key or name])
         if a.dtype != want:
             raise ValueError(f"{name}: host weights must be {np.dtype(want).name} for this dtype")
         if a.size != int(np.prod(shapes[name])):
             raise ValueError(f"{name}: {a.size} elements, expected shape {shapes[name]}")
         keep.append(a)
-        setattr(w, name, a.ctypes.data)
+        return a.ctypes.data
+
+    if "w_in" in weights:
+        base = host("w_in")
+        w.w_q, w.w_k, w.w_v, w.w_up = (base + i * HD * D * es for i in range(4))
+        if weights.get("b_in") is not None:
+            bb = host("b_in")
+            w.b_q, w.b_k, w.b_v, w.b_up = (bb + i * HD * es for i in range(4))
+    if "w_out" in weights:
+        base = host("w_out")
+        w.w_o, w.w_down = base, base + HD * es
+        w.ld_o = w.ld_down = HD + F
+    for name in _WEIGHT_FIELDS:
+        if getattr(w, name):
+            continue
+        key = "w_dn" if name == "w_down" and name not in weights else name
+        if weights.get(key) is None:
+            continue
+        setattr(w, name, host(name, key))
     return w, keep
 
 

@@ -1,5 +1,6 @@
 // bf16 GEMM with fp32 accumulate on gfx950 matrix cores:
-//   C[M, N] = A[M, K] * B[N, K]^T  (+ bias, GELU-tanh, bf16 store | fp32 store | fp32 accumulate)
+//   C[M, N] = A[M, K] * B[N, K]^T  (+ bias, GELU-tanh or SwiGLU, bf16 store | fp32 store |
+//   fp32 accumulate)
 //
 // This is the colwise projection (output features = weight dim 0) and the
 // rowwise partial projection (input features = weight dim 1) of the Diffusers
@@ -47,6 +48,67 @@ __device__ __forceinline__ float gelu_tanh(float u) {
   const float c = 0.7978845608028654f;
   const float z = c * fmaf(0.044715f * u, u * u, u);
   return u / (1.0f + __expf(-2.0f * z));
+}
+
+// SiLU: u * sigmoid(u) = u / (1 + exp(-u)).
+__device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
+
+// Writes one wave's TM x TN accumulator tiles: tile (i, j) holds C rows
+// row0 + 32 i + [0, 32) and columns col0 + 32 j + [0, 32) in the 32x32 MFMA
+// layout (lane: column lane & 31, rows 8 (e / 4) + 4 (lane >> 5) + (e % 4)).
+// col0 is a multiple of 64, so under SWIGLU tile j (even) is a gate block and
+// tile j + 1 its up block: the pair is combined in registers and stored as
+// 32 output columns.
+template <OutKind KIND, int TM, int TN>
+__device__ __forceinline__ void store_tiles(const f32x16 (&acc)[TM][TN], const GemmProblem& p,
+                                            const GemmEpilogue& ep, int row0, int col0,
+                                            int lane) {
+  static_assert(TN % 2 == 0, "SwiGLU pairs tile j with tile j + 1");
+  const int col_l = lane & 31;
+  const int row_l = 4 * (lane >> 5);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = col0 + 32 * j + col_l;
+    if (col >= p.N) continue;
+    const bool active = KIND != OutKind::F32_ACC && col >= ep.act_from;
+    const bool glu = active && ep.act == Act::SWIGLU;
+    const bool gelu = active && ep.act == Act::GELU_TANH;
+    if (glu && (j & 1)) continue;  // an up block, consumed with its gate block
+    int ocol = glu ? ep.act_from + (((col - ep.act_from) >> 6) << 5) + col_l : col;
+    float bias = 0.0f, bias_up = 0.0f;
+    if constexpr (KIND != OutKind::F32_ACC) {
+      if (ep.bias) {
+        bias = ep.bias[col];
+        if (glu) bias_up = ep.bias[col + 32];
+      }
+    }
+    const bool second = ocol >= ep.split;
+    if (second) ocol -= ep.split;
+    const int64_t ld = second ? ep.ld1 : ep.ld0;
+    void* out = second ? ep.out1 : ep.out0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = row0 + 32 * i + 8 * (e >> 2) + row_l + (e & 3);
+        if (row >= p.M) continue;
+        const int64_t off = (int64_t)row * ld + ocol;
+        float v = acc[i][j][e];
+        if constexpr (KIND == OutKind::F32_ACC) {
+          float* o = static_cast<float*>(out) + off;
+          *o = *o + v;
+        } else {
+          v += bias;
+          if (glu) v = silu(v) * (acc[i][j | 1][e] + bias_up);
+          else if (gelu) v = gelu_tanh(v);
+          if constexpr (KIND == OutKind::BF16)
+            static_cast<bf16*>(out)[off] = static_cast<bf16>(v);
+          else
+            static_cast<float*>(out)[off] = v;
+        }
+      }
+    }
+  }
 }
 
 template <int BM, int BN, int WM, int WN, OutKind KIND, bool KTAIL>
@@ -157,208 +219,15 @@ gemm_bf16_nt(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
     __syncthreads();
   }
 
-  // ---- epilogue.  32x32 accumulator layout: lane holds column (lane & 31)
-  // and rows 8 (e / 4) + 4 (lane >> 5) + (e % 4), e = 0..15.
-  const int col_l = lane & 31;
-  const int row_l = 4 * (lane >> 5);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int col = n0 + wn * WTN + 32 * j + col_l;
-    if (col >= p.N) continue;
-    float bias = 0.0f;
-    if constexpr (KIND != OutKind::F32_ACC) {
-      if (ep.bias) bias = ep.bias[col];
-    }
-    const bool gelu = col >= ep.gelu_from;
-    const bool second = col >= ep.split;
-    const int ocol = second ? col - ep.split : col;
-    const int64_t ld = second ? ep.ld1 : ep.ld0;
-    void* out = second ? ep.out1 : ep.out0;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * WTM + 32 * i + 8 * (e >> 2) + row_l + (e & 3);
-        if (row >= p.M) continue;
-        const int64_t off = (int64_t)row * ld + ocol;
-        float v = acc[i][j][e];
-        if constexpr (KIND == OutKind::F32_ACC) {
-          float* o = static_cast<float*>(out) + off;
-          *o = *o + v;
-        } else {
-          v += bias;
-          if (gelu) v = gelu_tanh(v);
-          if constexpr (KIND == OutKind::BF16)
-            static_cast<bf16*>(out)[off] = static_cast<bf16>(v);
-          else
-            static_cast<float*>(out)[off] = v;
-        }
-      }
-    }
-  }
+  store_tiles<KIND, TM, TN>(acc, p, ep, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
-// 256x256 tile, 8 waves (2 per SIMD, so one wave's LDS reads and epilogue
-// overlap the other's MFMAs) in a 2 x 4 grid of 128x64 wave tiles.  A and B
-// tiles go global -> LDS directly (global_load_lds_dwordx4: each wave
-// instruction fills 1 KB = 8 tile rows), so no registers stage them and no
-// ds_write is issued.  Needs K % 64 == 0 (no zero-fill on this path).
-template <OutKind KIND>
-__global__ void __launch_bounds__(512)
-gemm_bf16_nt_256x256_8w(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
-  constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
-  constexpr int WTM = BM / WM, WTN = BN / WN;   // 128 x 64
-  constexpr int TM = WTM / 32, TN = WTN / 32;   // 4 x 2 MFMA tiles
-  constexpr int BUF = (BM + BN) * kRowChunks;   // 16-byte chunks per stage
-  constexpr int NWAVES = 8;
-  constexpr int A_INSTR = BM * kRowChunks / 64 / NWAVES;  // 4 wave loads of 1 KB
-  constexpr int B_INSTR = BN * kRowChunks / 64 / NWAVES;
-
-  __shared__ u32x4 smem[2 * BUF];
-
-  const int nb = gridDim.x, bid = blockIdx.x;
-  const int xcd = bid & 7, per = nb >> 3, rem = nb & 7;
-  const int id = xcd * per + min(xcd, rem) + (bid >> 3);
-  const int group = id / (kGroupM * tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int in_group = id - group * kGroupM * tiles_n;
-  const int m0 = (first_m + in_group % gm) * BM;
-  const int n0 = (in_group / gm) * BN;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bf16* __restrict__ A = static_cast<const bf16*>(p.A);
-  const bf16* __restrict__ B = static_cast<const bf16*>(p.B);
-
-  // Wave instruction i fills chunks c0 = (wave * A_INSTR + i) * 64 .. + 63 of
-  // the stage, i.e. tile rows 8 (wave * A_INSTR + i) + (lane >> 3); lane
-  // writes physical chunk (lane & 7) of its row, which holds logical k-group
-  // (lane & 7) ^ swizzle-of-row.
-  int64_t a_off[A_INSTR], b_off[B_INSTR];
-#pragma unroll
-  for (int i = 0; i < A_INSTR; ++i) {
-    const int row = 8 * (wave * A_INSTR + i) + (lane >> 3);
-    const int kc = swizzle(row, lane & 7);
-    a_off[i] = (int64_t)min(m0 + row, p.M - 1) * p.lda + kc * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < B_INSTR; ++i) {
-    const int row = 8 * (wave * B_INSTR + i) + (lane >> 3);
-    const int kc = swizzle(row, lane & 7);
-    b_off[i] = (int64_t)min(n0 + row, p.N - 1) * p.ldb + kc * 8;
-  }
-  auto issue = [&](int kt, int buf) {
-    const int k = kt * kBK;
-    u32x4* sa = smem + buf * BUF;
-    u32x4* sb = sa + BM * kRowChunks;
-#pragma unroll
-    for (int i = 0; i < A_INSTR; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(A + a_off[i] + k),
-          (void __attribute__((address_space(3)))*)(sa + (wave * A_INSTR + i) * 64), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < B_INSTR; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(B + b_off[i] + k),
-          (void __attribute__((address_space(3)))*)(sb + (wave * B_INSTR + i) * 64), 16, 0, 0);
-  };
-
-  const int wm = wave / WN, wn = wave % WN;
-  const int a_row = wm * WTM + (lane & 31);
-  const int b_row = wn * WTN + (lane & 31);
-  const int khalf = lane >> 5;
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  // Operand fragments are double-buffered in registers: the reads for k-step
-  // s + 1 are issued before the MFMAs of step s, so LDS latency hides behind
-  // matrix work within each wave.
-  bf16x8 fa[2][TM], fb[2][TN];
-  auto read_frags = [&](const u32x4* sa, const u32x4* sb, int s, int slot) {
-    const int kc = 2 * s + khalf;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-      fa[slot][i] = __builtin_bit_cast(bf16x8, sa[(a_row + 32 * i) * kRowChunks + swizzle(a_row, kc)]);
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      fb[slot][j] = __builtin_bit_cast(bf16x8, sb[(b_row + 32 * j) * kRowChunks + swizzle(b_row, kc)]);
-  };
-  auto mfmas = [&](int slot) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
-  };
-
-  const int nk = p.K / kBK;
-  issue(0, 0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
-    const u32x4* sa = smem + buf * BUF;
-    const u32x4* sb = sa + BM * kRowChunks;
-    read_frags(sa, sb, 0, 0);
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      // fences keep the compiler from sinking the next step's reads below
-      // this step's MFMAs (or merging the two fragment sets)
-      if (s + 1 < kBK / 16) read_frags(sa, sb, s + 1, (s + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(s & 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();  // waits for this wave's LDS-DMA loads, then for every wave
-  }
-
-  const int col_l = lane & 31;
-  const int row_l = 4 * (lane >> 5);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int col = n0 + wn * WTN + 32 * j + col_l;
-    if (col >= p.N) continue;
-    float bias = 0.0f;
-    if constexpr (KIND != OutKind::F32_ACC) {
-      if (ep.bias) bias = ep.bias[col];
-    }
-    const bool gelu = col >= ep.gelu_from;
-    const bool second = col >= ep.split;
-    const int ocol = second ? col - ep.split : col;
-    const int64_t ld = second ? ep.ld1 : ep.ld0;
-    void* out = second ? ep.out1 : ep.out0;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * WTM + 32 * i + 8 * (e >> 2) + row_l + (e & 3);
-        if (row >= p.M) continue;
-        const int64_t off = (int64_t)row * ld + ocol;
-        float v = acc[i][j][e];
-        if constexpr (KIND == OutKind::F32_ACC) {
-          float* o = static_cast<float*>(out) + off;
-          *o = *o + v;
-        } else {
-          v += bias;
-          if (gelu) v = gelu_tanh(v);
-          if constexpr (KIND == OutKind::BF16)
-            static_cast<bf16*>(out)[off] = static_cast<bf16>(v);
-          else
-            static_cast<float*>(out)[off] = v;
-        }
-      }
-    }
-  }
-}
-
-// Ping-pong variant of the 256x256 8-wave tile.  Waves 0-3 (group 0) own C
-// rows 0-127 and waves 4-7 (group 1) rows 128-255.  The groups run one phase
+// 256x256 tile, 8 waves (2 per SIMD) in a ping-pong schedule; each wave owns
+// a 128x64 block of C.  A and B tiles go global -> LDS directly
+// (global_load_lds_dwordx4: each wave instruction fills 1 KB = 8 tile rows),
+// so no registers stage them and no ds_write is issued; K % 64 == 0 (no
+// zero-fill on this path).  Waves 0-3 (group 0) own C rows 0-127 and waves
+// 4-7 (group 1) rows 128-255.  The groups run one phase
 // apart, separated by workgroup barriers: while one group reads a whole K
 // tile of operand fragments from LDS into registers (24 x 16 bytes per
 // lane), the other issues the 32 MFMAs of the tile it read in the previous
@@ -505,43 +374,7 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
     wg_barrier();
   }
 
-  const int col_l = lane & 31;
-  const int row_l = 4 * (lane >> 5);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int col = n0 + 64 * q + 32 * j + col_l;
-    if (col >= p.N) continue;
-    float bias = 0.0f;
-    if constexpr (KIND != OutKind::F32_ACC) {
-      if (ep.bias) bias = ep.bias[col];
-    }
-    const bool gelu = col >= ep.gelu_from;
-    const bool second = col >= ep.split;
-    const int ocol = second ? col - ep.split : col;
-    const int64_t ld = second ? ep.ld1 : ep.ld0;
-    void* out = second ? ep.out1 : ep.out0;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + 128 * g + 32 * i + 8 * (e >> 2) + row_l + (e & 3);
-        if (row >= p.M) continue;
-        const int64_t off = (int64_t)row * ld + ocol;
-        float v = acc[i][j][e];
-        if constexpr (KIND == OutKind::F32_ACC) {
-          float* o = static_cast<float*>(out) + off;
-          *o = *o + v;
-        } else {
-          v += bias;
-          if (gelu) v = gelu_tanh(v);
-          if constexpr (KIND == OutKind::BF16)
-            static_cast<bf16*>(out)[off] = static_cast<bf16>(v);
-          else
-            static_cast<float*>(out)[off] = v;
-        }
-      }
-    }
-  }
+  store_tiles<KIND, TM, TN>(acc, p, ep, m0 + 128 * g, n0 + 64 * q, lane);
 }
 
 hipError_t launch_256x256_8w(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,

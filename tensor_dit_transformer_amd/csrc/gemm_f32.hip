@@ -1,11 +1,13 @@
 // fp32 GEMM, C[M, N] = A[M, K] * B[N, K]^T with the same epilogues as the
-// bf16 kernel (bias, GELU-tanh on a column range, split output, fp32
-// accumulate).  It serves fp32 shards (colwise / rowwise projections of the
-// Diffusers TP page, §"Colwise e rowwise"), which are small and
+// bf16 kernel (bias, GELU-tanh or SwiGLU on a column range, split output,
+// fp32 accumulate).  It serves fp32 shards (colwise / rowwise projections of
+// the Diffusers TP page, §"Colwise e rowwise"), which are small and
 // correctness-oriented; it runs on the vector ALUs with plain fp32 FMA,
 // 64x64 output tiles, 16-deep K tiles staged through LDS, 4x4 outputs per
-// thread.  Out-of-range rows are clamped on load and masked on store; K past
-// the end is zero-filled (K is a multiple of 4).
+// thread (columns 2 tx, 2 tx + 1, 32 + 2 tx, 33 + 2 tx of the tile, so a
+// SwiGLU gate column and its up column, 32 apart, sit in one thread).
+// Out-of-range rows are clamped on load and masked on store; K past the end
+// is zero-filled (K is a multiple of 4).
 #include "tp_kernels.h"
 
 namespace tpk {
@@ -20,6 +22,11 @@ __device__ __forceinline__ float gelu_tanh(float u) {
   const float z = c * fmaf(0.044715f * u, u * u, u);
   return u / (1.0f + __expf(-2.0f * z));
 }
+
+__device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
+
+// Tile column of a thread's j-th output column.
+__device__ __forceinline__ int tile_col(int tx, int j) { return (j >> 1) * 32 + 2 * tx + (j & 1); }
 
 template <OutKind KIND>
 __global__ void __launch_bounds__(256) gemm_f32_nt(GemmProblem p, GemmEpilogue ep) {
@@ -54,7 +61,7 @@ __global__ void __launch_bounds__(256) gemm_f32_nt(GemmProblem p, GemmEpilogue e
 #pragma unroll
       for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx * 4 + j];
+      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tile_col(tx, j)];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -65,15 +72,22 @@ __global__ void __launch_bounds__(256) gemm_f32_nt(GemmProblem p, GemmEpilogue e
 
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int col = n0 + tx * 4 + j;
+    const int col = n0 + tile_col(tx, j);
     if (col >= p.N) continue;
-    float bias = 0.0f;
+    const bool active = KIND != OutKind::F32_ACC && col >= ep.act_from;
+    const bool glu = active && ep.act == Act::SWIGLU;
+    const bool gelu = active && ep.act == Act::GELU_TANH;
+    if (glu && j >= 2) continue;  // an up column, consumed with its gate (j - 2)
+    int ocol = glu ? ep.act_from + (((col - ep.act_from) >> 6) << 5) + ((col - ep.act_from) & 31) : col;
+    float bias = 0.0f, bias_up = 0.0f;
     if constexpr (KIND != OutKind::F32_ACC) {
-      if (ep.bias) bias = ep.bias[col];
+      if (ep.bias) {
+        bias = ep.bias[col];
+        if (glu) bias_up = ep.bias[col + 32];
+      }
     }
-    const bool gelu = col >= ep.gelu_from;
-    const bool second = col >= ep.split;
-    const int ocol = second ? col - ep.split : col;
+    const bool second = ocol >= ep.split;
+    if (second) ocol -= ep.split;
     const int64_t ld = second ? ep.ld1 : ep.ld0;
     float* out = static_cast<float*>(second ? ep.out1 : ep.out0);
 #pragma unroll
@@ -85,7 +99,9 @@ __global__ void __launch_bounds__(256) gemm_f32_nt(GemmProblem p, GemmEpilogue e
         *o = *o + acc[i][j];
       } else {
         float v = acc[i][j] + bias;
-        *o = gelu ? gelu_tanh(v) : v;
+        if (glu) v = silu(v) * (acc[i][(j + 2) & 3] + bias_up);
+        else if (gelu) v = gelu_tanh(v);
+        *o = v;
       }
     }
   }

@@ -18,13 +18,16 @@ struct tp_block_shard {
   int device;
   size_t es;        // element size of activations and weights
   int64_t D, Dr, Fr, Hr, d;
-  bool attn, mlp;
-  int64_t n_col;    // rows of the packed colwise weight: 3 Dr (attention) + Fr (MLP)
+  bool attn, mlp, swiglu;
+  int64_t n_up;     // rows of the MLP in-projection slice: Fr, or 2 Fr with SwiGLU
+  int64_t n_col;    // rows of the packed colwise weight: 3 Dr (attention) + n_up (MLP)
   int64_t up_row0;  // first row of W_up_r in it
   int64_t k_row;    // columns of the packed rowwise weight: Dr (attention) + Fr (MLP)
   int64_t dn_col0;  // first column of W_dn_r in it
   void* w_col;      // [n_col, D]      = [W_q[R_r]; W_k[R_r]; W_v[R_r]; W_up[C_r]]
-  float* b_col;     // [n_col] fp32    = [b_q[R_r]; b_k[R_r]; b_v[R_r]; b_up[C_r]]
+                    //   SwiGLU: the MLP part is W_gate[C_r] and W_up[C_r] interleaved
+                    //   in blocks of 32 rows: gate 0-31, up 0-31, gate 32-63, ...
+  float* b_col;     // [n_col] fp32, the biases in the same row order
   void* w_row;      // [D, k_row]      = [W_o[:, R_r] | W_dn[:, C_r]]
 };
 
@@ -117,6 +120,19 @@ tp_status launch(const tpk::GemmProblem& p, const tpk::GemmEpilogue& ep, tpk::Ou
   return TP_OK;
 }
 
+// Colwise GEMM over weight rows [row0, row0 + n_w) of the packed slice:
+// activation `act` on GEMM columns >= act_from, output columns < split to y0,
+// the rest to y1 (see tpk::GemmEpilogue).
+tp_status colwise(const tp_block_shard* s, int64_t tokens, const void* x, int64_t ldx, int64_t row0,
+                  int64_t n_w, tpk::Act act, int act_from, int split, void* y0, int64_t ld0,
+                  void* y1, int64_t ld1, hipStream_t stream) {
+  const tpk::GemmProblem p{x, ldx, static_cast<const char*>(s->w_col) + row0 * s->D * s->es, s->D,
+                           (int)tokens, (int)n_w, (int)s->D};
+  const tpk::GemmEpilogue ep{s->b_col + row0, act_from, act, split, y0, ld0, y1, ld1};
+  return launch(p, ep, s->cfg.dtype == TP_BF16 ? tpk::OutKind::BF16 : tpk::OutKind::F32_STORE,
+                s->cfg.dtype, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -128,6 +144,8 @@ TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_bloc
   if (!cfg || !w) return fail(TP_ERR_ARG, "config or weights is NULL");
   if (cfg->dtype != TP_F32 && cfg->dtype != TP_BF16)
     return fail(TP_ERR_ARG, "unknown dtype %d", (int)cfg->dtype);
+  if (cfg->mlp_act != TP_MLP_GELU_TANH && cfg->mlp_act != TP_MLP_SWIGLU)
+    return fail(TP_ERR_ARG, "unknown mlp_act %d", (int)cfg->mlp_act);
   const int64_t P = cfg->tp_degree, r = cfg->rank, D = cfg->hidden, H = cfg->num_heads,
                 d = cfg->head_dim, F = cfg->ffn;
   if (P < 1 || r < 0 || r >= P)
@@ -150,20 +168,31 @@ TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_bloc
     return fail(TP_ERR_DIVISIBILITY, "tp_degree %lld does not divide ffn %lld", (long long)P,
                 (long long)F);
   const int64_t Dr = H > 0 ? D / P : 0, Fr = F / P;
+  const bool swiglu = F > 0 && cfg->mlp_act == TP_MLP_SWIGLU;
   if (D % 8 || Dr % 8 || Fr % 8)
     return fail(TP_ERR_UNSUPPORTED, "hidden, hidden/tp and ffn/tp must be multiples of 8");
+  if (swiglu && Fr % 32)
+    return fail(TP_ERR_UNSUPPORTED, "SwiGLU needs ffn/tp (%lld) to be a multiple of 32",
+                (long long)Fr);
   if (H > 0 && (!w->w_q || !w->w_k || !w->w_v || !w->w_o))
     return fail(TP_ERR_ARG, "attention configured but w_q/w_k/w_v/w_o missing");
   if (F > 0 && (!w->w_up || !w->w_down))
     return fail(TP_ERR_ARG, "MLP configured but w_up/w_down missing");
+  const int64_t ld_o = w->ld_o ? w->ld_o : H * d, ld_dn = w->ld_down ? w->ld_down : F;
+  if (H > 0 && ld_o < H * d)
+    return fail(TP_ERR_ARG, "ld_o (%lld) < num_heads*head_dim (%lld)", (long long)ld_o,
+                (long long)(H * d));
+  if (F > 0 && ld_dn < F)
+    return fail(TP_ERR_ARG, "ld_down (%lld) < ffn (%lld)", (long long)ld_dn, (long long)F);
 
   tp_block_shard* s = new tp_block_shard();
   s->cfg = *cfg;
   s->es = cfg->dtype == TP_BF16 ? 2 : 4;
   s->D = D; s->Dr = Dr; s->Fr = Fr; s->Hr = H / P; s->d = d;
-  s->attn = H > 0; s->mlp = F > 0;
+  s->attn = H > 0; s->mlp = F > 0; s->swiglu = swiglu;
   s->up_row0 = 3 * Dr;
-  s->n_col = 3 * Dr + Fr;
+  s->n_up = swiglu ? 2 * Fr : Fr;
+  s->n_col = 3 * Dr + s->n_up;
   s->dn_col0 = Dr;
   s->k_row = Dr + Fr;
   hipError_t e = hipGetDevice(&s->device);
@@ -194,9 +223,24 @@ TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_bloc
       widen_bias(bias, b * Dr, bs[b], r * Dr, Dr, cfg->dtype);
     }
   }
-  if (e == hipSuccess && s->mlp) {
+  if (e == hipSuccess && s->mlp && !swiglu) {
     e = put_rows(w->w_up, r * Fr, Fr, s->up_row0);
     widen_bias(bias, s->up_row0, w->b_up, r * Fr, Fr, cfg->dtype);
+  }
+  if (e == hipSuccess && swiglu) {
+    // [1, 1] blocks: the rank's gate rows C_r and up rows F + C_r, stored as
+    // alternating 32-row blocks so the GEMM epilogue finds a gate column and
+    // its up column in neighbouring 32-column MFMA tiles.
+    const int64_t blk = 32, nblk = Fr / blk;
+    for (int half = 0; half < 2 && e == hipSuccess; ++half) {
+      const int64_t src_row0 = half * F + r * Fr;
+      e = hipMemcpy2D(wc + (s->up_row0 + half * blk) * row_bytes, 2 * blk * row_bytes,
+                      static_cast<const char*>(w->w_up) + src_row0 * row_bytes, blk * row_bytes,
+                      blk * row_bytes, (size_t)nblk, hipMemcpyHostToDevice);
+      for (int64_t b = 0; b < nblk; ++b)
+        widen_bias(bias, s->up_row0 + 2 * blk * b + half * blk, w->b_up, src_row0 + blk * b, blk,
+                   cfg->dtype);
+    }
   }
   if (e == hipSuccess)
     e = hipMemcpy(s->b_col, bias.data(), bias.size() * sizeof(float), hipMemcpyHostToDevice);
@@ -204,11 +248,11 @@ TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_bloc
   char* wr = static_cast<char*>(s->w_row);
   const size_t dpitch = (size_t)s->k_row * es;
   if (e == hipSuccess && s->attn)
-    e = hipMemcpy2D(wr, dpitch, static_cast<const char*>(w->w_o) + r * Dr * es, (size_t)(H * d) * es,
+    e = hipMemcpy2D(wr, dpitch, static_cast<const char*>(w->w_o) + r * Dr * es, (size_t)ld_o * es,
                     (size_t)Dr * es, (size_t)D, hipMemcpyHostToDevice);
   if (e == hipSuccess && s->mlp)
     e = hipMemcpy2D(wr + s->dn_col0 * es, dpitch, static_cast<const char*>(w->w_down) + r * Fr * es,
-                    (size_t)F * es, (size_t)Fr * es, (size_t)D, hipMemcpyHostToDevice);
+                    (size_t)ld_dn * es, (size_t)Fr * es, (size_t)D, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     free_shard(s);
     return hip_fail(e, "weight slice upload");
@@ -223,14 +267,15 @@ TP_API tp_status tp_colwise_linear(tp_block_shard* s, tp_layer layer, int64_t to
                                    int64_t ldx, void* y, int64_t ldy, void* stream) {
   tp_status st = check_shard(s);
   if (st != TP_OK) return st;
-  int64_t row0, n;
-  int gelu_from;
+  int64_t row0, n, n_w;  // first weight row, output width, weight rows (GEMM N)
+  tpk::Act act;
   if (layer == TP_QKV) {
     if (!s->attn) return fail(TP_ERR_ARG, "TP_QKV: shard has no attention layers");
-    row0 = 0; n = 3 * s->Dr; gelu_from = (int)n;
+    row0 = 0; n = n_w = 3 * s->Dr; act = tpk::Act::NONE;
   } else if (layer == TP_MLP_UP) {
     if (!s->mlp) return fail(TP_ERR_ARG, "TP_MLP_UP: shard has no MLP layers");
-    row0 = s->up_row0; n = s->Fr; gelu_from = 0;
+    row0 = s->up_row0; n = s->Fr; n_w = s->n_up;
+    act = s->swiglu ? tpk::Act::SWIGLU : tpk::Act::GELU_TANH;
   } else {
     return fail(TP_ERR_ARG, "layer %d is not colwise (TP_QKV or TP_MLP_UP)", (int)layer);
   }
@@ -238,11 +283,8 @@ TP_API tp_status tp_colwise_linear(tp_block_shard* s, tp_layer layer, int64_t to
   if ((st = check_matrix("x", x, ldx, s->D, s->es)) != TP_OK) return st;
   if ((st = check_matrix("y", y, ldy, n, s->es)) != TP_OK) return st;
   if (tokens == 0) return TP_OK;
-  const tpk::GemmProblem p{x, ldx, static_cast<const char*>(s->w_col) + row0 * s->D * s->es, s->D,
-                           (int)tokens, (int)n, (int)s->D};
-  const tpk::GemmEpilogue ep{s->b_col + row0, gelu_from, (int)n, y, ldy, nullptr, 0};
-  return launch(p, ep, s->cfg.dtype == TP_BF16 ? tpk::OutKind::BF16 : tpk::OutKind::F32_STORE,
-                s->cfg.dtype, static_cast<hipStream_t>(stream));
+  return colwise(s, tokens, x, ldx, row0, n_w, act, 0, (int)n, y, ldy, nullptr, 0,
+                 static_cast<hipStream_t>(stream));
 }
 
 TP_API tp_status tp_colwise_qkv_up(tp_block_shard* s, int64_t tokens, const void* x, int64_t ldx,
@@ -258,10 +300,19 @@ TP_API tp_status tp_colwise_qkv_up(tp_block_shard* s, int64_t tokens, const void
   if (overlap(qkv, span_bytes(tokens, ldqkv, 3 * s->Dr, s->es), h, span_bytes(tokens, ldh, s->Fr, s->es)))
     return fail(TP_ERR_ARG, "qkv and h overlap");
   const int split = (int)(3 * s->Dr);
-  const tpk::GemmProblem p{x, ldx, s->w_col, s->D, (int)tokens, (int)s->n_col, (int)s->D};
-  const tpk::GemmEpilogue ep{s->b_col, split, split, qkv, ldqkv, h, ldh};
-  return launch(p, ep, s->cfg.dtype == TP_BF16 ? tpk::OutKind::BF16 : tpk::OutKind::F32_STORE,
-                s->cfg.dtype, static_cast<hipStream_t>(stream));
+  const hipStream_t st_ = static_cast<hipStream_t>(stream);
+  if (s->swiglu && split % 64) {
+    // SwiGLU pairs need the MLP rows to start on a 64-column boundary of the
+    // GEMM; otherwise the two projections run as two launches.
+    if ((st = colwise(s, tokens, x, ldx, 0, split, tpk::Act::NONE, split, split, qkv, ldqkv,
+                      nullptr, 0, st_)) != TP_OK)
+      return st;
+    return colwise(s, tokens, x, ldx, s->up_row0, s->n_up, tpk::Act::SWIGLU, 0, (int)s->Fr, h, ldh,
+                   nullptr, 0, st_);
+  }
+  return colwise(s, tokens, x, ldx, 0, s->n_col,
+                 s->swiglu ? tpk::Act::SWIGLU : tpk::Act::GELU_TANH, split, split, qkv, ldqkv, h,
+                 ldh, st_);
 }
 
 TP_API tp_status tp_attn_heads(tp_block_shard* s, int64_t tokens, const void* qkv, int64_t ldqkv,
@@ -311,7 +362,7 @@ TP_API tp_status tp_rowwise_linear_partial(tp_block_shard* s, tp_layer layer, in
     return fail(TP_ERR_ARG, "partial overlaps x_local");
   const tpk::GemmProblem p{x_local, ldx, static_cast<const char*>(s->w_row) + col0 * s->es, s->k_row,
                            (int)tokens, (int)s->D, (int)k};
-  const tpk::GemmEpilogue ep{nullptr, (int)s->D, (int)s->D, partial, ldp, nullptr, 0};
+  const tpk::GemmEpilogue ep{nullptr, (int)s->D, tpk::Act::NONE, (int)s->D, partial, ldp, nullptr, 0};
   return launch(p, ep, accumulate ? tpk::OutKind::F32_ACC : tpk::OutKind::F32_STORE, s->cfg.dtype,
                 static_cast<hipStream_t>(stream));
 }

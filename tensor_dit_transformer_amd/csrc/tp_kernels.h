@@ -9,8 +9,8 @@ namespace tpk {
 
 // What the GEMM epilogue does with each fp32 accumulator.
 enum class OutKind : int {
-  BF16 = 0,       // (+bias, GELU on a column range) -> bf16 store
-  F32_STORE = 1,  // (+bias, GELU on a column range) -> fp32 store
+  BF16 = 0,       // (+bias, activation on a column range) -> bf16 store
+  F32_STORE = 1,  // (+bias, activation on a column range) -> fp32 store
   F32_ACC = 2,    // fp32 read-add-write (rowwise partial accumulate), no bias
 };
 
@@ -24,13 +24,25 @@ struct GemmProblem {
   int M, N, K;
 };
 
-// Output columns n < split go to out0[:, n], columns n >= split to
-// out1[:, n - split] (two tensors written by one launch: the packed
-// QKV+up colwise projection).  Columns n >= gelu_from get GELU-tanh after
-// the bias.  bias is fp32 [N] or nullptr.
+// Activation applied by the colwise epilogue to columns n >= act_from, after
+// the bias.
+enum class Act : int {
+  NONE = 0,
+  GELU_TANH = 1,  // y[n] = gelu_tanh(c[n] + b[n])
+  SWIGLU = 2,     // columns from act_from on come in 64-column pairs
+                  // [gate 32 | up 32]; pair p's lane c < 32 gives the ONE
+                  // output column act_from + 32 p + c = silu(gate + b) * (up + b)
+};
+
+// Output column o (after SwiGLU's pair -> column map) goes to out0[:, o] if
+// o < split, else to out1[:, o - split] (two tensors written by one launch:
+// the packed QKV + MLP-in colwise projection).  bias is fp32 [N] or nullptr.
+// SWIGLU needs act_from and N - act_from to be multiples of 64 (the kernels'
+// per-wave column blocks start at multiples of 64).
 struct GemmEpilogue {
   const float* bias;
-  int gelu_from;
+  int act_from;
+  Act act;
   int split;
   void* out0;
   int64_t ld0;

@@ -183,3 +183,78 @@ def test_binding_raises_with_detail(L):
                                  _tiny_weights(192, 24, 8, 0))
     assert e.value.status == tp.TP_ERR_DIVISIBILITY
     assert "divide" in str(e.value)
+
+
+def _swiglu_weights(D, H, d, F, dtype=np.uint16):
+    w = _tiny_weights(D, H, d, F, dtype)
+    w["w_up"] = np.zeros((2 * F, D), dtype)
+    return w
+
+
+def test_create_rejects_swiglu_and_stride_errors(L):
+    sw = tp.TP_MLP_SWIGLU
+    # ffn / tp = 40 is a multiple of 8 but not of 32: SwiGLU's paired tiles need 32
+    st, out = _create(L, tp.make_config(2, 0, 64, 0, 0, 80, tp.TP_BF16, sw), _swiglu_weights(64, 0, 0, 80))
+    assert st == tp.TP_ERR_UNSUPPORTED and out is None and "32" in tp.tp_last_error_detail()
+    # ... while GELU accepts it (past validation: created, or a HIP error without a device)
+    st, out = _create(L, tp.make_config(2, 0, 64, 0, 0, 80, tp.TP_BF16), _tiny_weights(64, 0, 0, 80))
+    assert st != tp.TP_ERR_UNSUPPORTED
+    if out:
+        L.tp_block_shard_destroy(out)
+    # unknown activation
+    st, out = _create(L, tp.make_config(1, 0, 64, 0, 0, 64, tp.TP_BF16, 5), _tiny_weights(64, 0, 0, 64))
+    assert st == tp.TP_ERR_ARG and "mlp_act" in tp.tp_last_error_detail()
+    # row strides of the rowwise weights shorter than their rows
+    for field, msg in (("ld_o", "ld_o"), ("ld_down", "ld_down")):
+        cfg = tp.make_config(2, 0, 32, 4, 8, 64, tp.TP_BF16)
+        weights = _tiny_weights(32, 4, 8, 64)
+        w = tp.TpBlockWeights()
+        for k, a in weights.items():
+            setattr(w, k, a.ctypes.data)
+        setattr(w, field, 16)
+        out = ctypes.c_void_p()
+        st = L.tp_block_shard_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(out))
+        assert st == tp.TP_ERR_ARG and msg in tp.tp_last_error_detail()
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """ctypes mirrors of tp_block_config / tp_block_weights have the C
+    compiler's sizes and field offsets."""
+    src = tmp_path / "layout.c"
+    fields_c = ["tp_degree", "rank", "hidden", "num_heads", "head_dim", "ffn", "dtype", "mlp_act"]
+    fields_w = list(binding._WEIGHT_FIELDS) + ["ld_o", "ld_down"]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tp_shard.h"', 'int main(void) {',
+             'printf("%zu\\n", sizeof(tp_block_config));', 'printf("%zu\\n", sizeof(tp_block_weights));']
+    lines += [f'printf("%zu\\n", offsetof(tp_block_config, {f}));' for f in fields_c]
+    lines += [f'printf("%zu\\n", offsetof(tp_block_weights, {f}));' for f in fields_w]
+    lines += ['return 0; }']
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [ctypes.sizeof(tp.TpBlockConfig), ctypes.sizeof(tp.TpBlockWeights)]
+    want += [getattr(tp.TpBlockConfig, f).offset for f in fields_c]
+    want += [getattr(tp.TpBlockWeights, f).offset for f in fields_w]
+    assert got == want
+
+
+def test_binding_packed_weights_address_the_blocks():
+    """A packed input projection and a packed output projection are passed as
+    pointers into the blocks, with the output projection's row stride."""
+    H, d, F, D = 4, 8, 96, 32
+    HD = H * d
+    cfg = tp.make_config(2, 0, D, H, d, F, tp.TP_BF16, tp.TP_MLP_SWIGLU)
+    w_in = np.zeros((3 * HD + 2 * F, D), np.uint16)
+    b_in = np.zeros(3 * HD + 2 * F, np.uint16)
+    w_out = np.zeros((D, HD + F), np.uint16)
+    w, keep = binding._host_weights({"w_in": w_in, "b_in": b_in, "w_out": w_out}, cfg)
+    base = keep[0].ctypes.data
+    assert [w.w_q, w.w_k, w.w_v, w.w_up] == [base + i * HD * D * 2 for i in range(4)]
+    bb = keep[1].ctypes.data
+    assert [w.b_q, w.b_k, w.b_v, w.b_up] == [bb + i * HD * 2 for i in range(4)]
+    ob = keep[2].ctypes.data
+    assert (w.w_o, w.w_down, w.ld_o, w.ld_down) == (ob, ob + HD * 2, HD + F, HD + F)
+    with pytest.raises(ValueError):      # a GELU config expects W_up [F, D], not [2F, D]
+        binding._host_weights({"w_in": w_in}, tp.make_config(2, 0, D, H, d, F, tp.TP_BF16))

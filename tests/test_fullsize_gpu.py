@@ -1,7 +1,8 @@
 """GPU parity at the workloads' full sizes.
 
-C2 (MLP shard), C3 (attention shard) and C4 (wide block shard) are compared
-element by element with the float64 oracle.  The full block (T=16384,
+The MLP shard, the attention shard, the wide block shard and the
+single-stream SwiGLU block shard (4608 tokens) are compared element by
+element with the float64 oracle.  The full block (T=16384,
 hidden 6144, 48 heads, ffn 18432, tp_degree 4 and 2) runs in exactly the
 launch configuration the benchmark times; there the oracle computes sampled
 outputs one by one (each output row depends on its own input row, plus all
@@ -63,6 +64,7 @@ def _check(buf, ref, what):
     ("mlp_bf16_T4608_D3072_F12288_P4", (0, 3)),
     ("attn_bf16_T4608_D3072_H24_P4", (0, 3)),
     ("block_bf16_T4608_D6144_H48_F18432_P4", (0,)),
+    ("single_swiglu_bf16_T4608_D6144_H48_F18432_P4", (1,)),
 ])
 def test_one_rank_shards_full_compare(name, ranks):
     w = tp_inputs.WORKLOADS[name]
@@ -70,7 +72,8 @@ def test_one_rank_shards_full_compare(name, ranks):
     say(f"[{name}] inputs ready")
     shards, outs = _run(w, inp, ranks)
     for r, b in zip(ranks, outs):
-        ref = O.rank_forward(inp["x"], inp.values, w.tp_degree, r, w.num_heads, w.head_dim, bf16=True)
+        ref = O.rank_forward(inp["x"], inp.values, w.tp_degree, r, w.num_heads, w.head_dim, bf16=True,
+                             mlp_act=w.mlp_act)
         _check(b, ref, f"{name} rank {r}")
     _close(shards)
 
@@ -177,3 +180,44 @@ def test_full_size_kernels_on_seeded_inputs():
     e_y = H.rel_err(H.as_f64(y), ref)
     say(f"[C5 kernels] reduce (4 x 16384 x 6144): {e_y:.2e}")
     assert e_y <= 1e-6
+
+
+def test_single_stream_swiglu_bench_configuration():
+    """The single-stream SwiGLU block at 16384 tokens, tp_degree 4, created
+    from the packed checkpoint layout, in the launch configuration the
+    benchmark times: sampled rows of every rank's q/k/v, SwiGLU hidden and one
+    head's attention output against the oracle."""
+    w = tp_inputs.C7
+    inp = tp_inputs.make_inputs(w, seed=0)
+    v = inp.values
+    T, d, P, F = w.tokens, w.head_dim, w.tp_degree, w.ffn
+    HD = w.num_heads * d
+    rows = tp_inputs.sample_rows(T, 16, seed=3)
+    xr = v["x"][rows]
+    x64 = v["x"].astype(np.float64)
+    x = H.to_device(inp, "x")
+    say("[single-stream T=16384] inputs ready")
+    shards = H.create_shards(w, inp, packed=True)
+    for r, s in enumerate(shards):
+        b = H.RankBuffers(s, T)
+        H.run_rank(s, x, b)
+        torch.cuda.synchronize()
+        R, C = O.colwise_range(HD, P, r), O.colwise_range(F, P, r)
+        w_qkv = np.concatenate([v["w_q"][R], v["w_k"][R], v["w_v"][R]])
+        b_qkv = np.concatenate([v["b_q"][R], v["b_k"][R], v["b_v"][R]])
+        e_qkv = H.rel_err(H.as_f64(b.qkv[rows]), O.colwise_rows_sampled(xr, w_qkv, b_qkv))
+        gu = np.concatenate([np.arange(C.start, C.stop), F + np.arange(C.start, C.stop)])
+        e_h = H.rel_err(H.as_f64(b.h[rows]),
+                        O.colwise_rows_sampled(xr, v["w_up"][gu], v["b_up"][gu], mlp_act="swiglu"))
+        j = (7 * r + 2) % s.heads_r
+        g = slice(R.start + j * d, R.start + (j + 1) * d)
+        k = O.to_bf16_rne(O.linear(x64, v["w_k"][g], v["b_k"][g]))
+        vv = O.to_bf16_rne(O.linear(x64, v["w_v"][g], v["b_v"][g]))
+        q = O.to_bf16_rne(O.linear(xr, v["w_q"][g], v["b_q"][g]))
+        o_ref = O.to_bf16_rne(O.attention_rows(q, k, vv, 1, d))
+        e_o = H.rel_err(H.as_f64(b.o[rows, j * d:(j + 1) * d]), o_ref)
+        say(f"[single-stream T=16384] rank {r}: qkv {e_qkv:.2e} h {e_h:.2e} o(head {j}) {e_o:.2e}")
+        for e in (e_qkv, e_h, e_o):
+            assert e <= H.TOL["bf16"]
+        del b
+    _close(shards)

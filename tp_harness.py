@@ -26,13 +26,27 @@ def host_weights(inp: tp_inputs.Inputs) -> Dict[str, np.ndarray]:
     return out
 
 
-def create_shards(w: tp_inputs.Workload, inp: tp_inputs.Inputs, ranks=None) -> List[tp.TpBlockShard]:
+def config(w: tp_inputs.Workload, rank: int) -> tp.TpBlockConfig:
     dt = tp.TP_BF16 if w.dtype == "bf16" else tp.TP_F32
-    hw = host_weights(inp)
+    act = tp.TP_MLP_SWIGLU if w.mlp_act == "swiglu" else tp.TP_MLP_GELU_TANH
+    return tp.make_config(w.tp_degree, rank, w.hidden, w.num_heads, w.head_dim, w.ffn, dt, act)
+
+
+def packed_host_weights(inp: tp_inputs.Inputs) -> Dict[str, np.ndarray]:
+    """The same weights as one fused input projection w_in = [W_q; W_k; W_v;
+    W_up-block] (+ b_in) and one fused output projection w_out = [W_o | W_dn]
+    (a packed checkpoint's layout; concatenation only)."""
+    h = host_weights(inp)
+    return {"w_in": np.concatenate([h["w_q"], h["w_k"], h["w_v"], h["w_up"]]),
+            "b_in": np.concatenate([h["b_q"], h["b_k"], h["b_v"], h["b_up"]]),
+            "w_out": np.ascontiguousarray(np.concatenate([h["w_o"], h["w_down"]], axis=1))}
+
+
+def create_shards(w: tp_inputs.Workload, inp: tp_inputs.Inputs, ranks=None,
+                  packed: bool = False) -> List[tp.TpBlockShard]:
+    hw = packed_host_weights(inp) if packed else host_weights(inp)
     ranks = range(w.tp_degree) if ranks is None else ranks
-    return [tp.tp_block_shard_create(
-        tp.make_config(w.tp_degree, r, w.hidden, w.num_heads, w.head_dim, w.ffn, dt), hw)
-        for r in ranks]
+    return [tp.tp_block_shard_create(config(w, r), hw) for r in ranks]
 
 
 def rowwise_biases(w: tp_inputs.Workload, inp: tp_inputs.Inputs) -> List[torch.Tensor]:
