@@ -49,7 +49,7 @@ __all__ = [
     "block_unsharded", "partial_reduce", "rowwise_bias",
     "attention_rows", "colwise_rows_sampled", "silu", "swiglu", "MLP_ACTS",
     "mlp_hidden", "packed_rowwise_cols", "single_stream_block",
-    "single_stream_rank", "single_stream_as_block",
+    "single_stream_rank", "single_stream_as_block", "split_input_rank",
 ]
 
 
@@ -159,7 +159,7 @@ def attention_heads(q, k, v, num_heads: int, head_dim: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def check_config(tp_degree: int, rank: int, hidden: int, num_heads: int,
-                 head_dim: int, ffn: int) -> None:
+                 head_dim: int, ffn: int, mod_in: int = 0) -> None:
     """[TP page, §Restrições e verificação] tp_degree must divide the head
     count, and each packed block (Q, K, V of width H*d, and the FFN width) must
     be divisible by tp_degree on its own; checked before any weight is used.
@@ -169,8 +169,10 @@ def check_config(tp_degree: int, rank: int, hidden: int, num_heads: int,
         raise ShardConfigError("argument", f"rank {rank} not in [0, {tp_degree})")
     if hidden <= 0 or num_heads < 0 or ffn < 0 or (num_heads > 0 and head_dim <= 0):
         raise ShardConfigError("argument", "sizes must be positive")
-    if num_heads == 0 and ffn == 0:
-        raise ShardConfigError("argument", "neither attention nor MLP")
+    if mod_in < 0:
+        raise ShardConfigError("argument", "sizes must be positive")
+    if num_heads == 0 and ffn == 0 and mod_in == 0:
+        raise ShardConfigError("argument", "neither attention nor MLP nor modulation")
     if num_heads > 0:
         if num_heads * head_dim != hidden:
             raise ShardConfigError("divisibility",
@@ -183,6 +185,9 @@ def check_config(tp_degree: int, rank: int, hidden: int, num_heads: int,
                 raise ShardConfigError("divisibility", f"packed block {name} not divisible")
     if ffn > 0 and ffn % tp_degree:
         raise ShardConfigError("divisibility", f"tp_degree {tp_degree} does not divide ffn {ffn}")
+    if mod_in > 0 and mod_in % tp_degree:
+        raise ShardConfigError("divisibility",
+                               f"tp_degree {tp_degree} does not divide the modulation input {mod_in}")
 
 
 def colwise_range(n_out: int, tp_degree: int, rank: int) -> slice:
@@ -364,6 +369,25 @@ def block_unsharded(x, wts: Dict[str, np.ndarray], num_heads: int, head_dim: int
         ys.append(res["y_mlp"])
     res["y"] = ys[0] if len(ys) == 1 else ys[0] + ys[1]
     return res
+
+
+# --------------------------------------------------------------------------
+# "rowwise_split_input" [TP page, §Colwise e rowwise; §O que deixar de fora]
+# --------------------------------------------------------------------------
+
+def split_input_rank(c, w, tp_degree: int, rank: int) -> np.ndarray:
+    """An independent projection whose input c [R, K] is replicated on every
+    rank (e.g. an AdaLN modulation projection reading the timestep
+    embedding), sharded by input features: the rank takes its contiguous
+    block K_r of columns from its own copy of c and of W [N, K] (weight dim
+    1) and returns the partial sum c[:, K_r] W[:, K_r]^T [R, N].  No bias:
+    it is added once, after the partials are summed."""
+    w = np.asarray(w, dtype=np.float64)
+    K = w.shape[1]
+    if K % tp_degree:
+        raise ShardConfigError("divisibility", f"tp_degree {tp_degree} does not divide {K} input features")
+    cols = rowwise_range(K, tp_degree, rank)
+    return linear(np.asarray(c, dtype=np.float64)[:, cols], w[:, cols])
 
 
 # --------------------------------------------------------------------------

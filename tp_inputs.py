@@ -17,6 +17,9 @@ float32 ``standard_normal`` scaled by the stated standard deviation):
     b_up ~ N(0, 0.01)                          [F]     (SwiGLU: [2F])
     W_dn ~ N(0, 0.02)                          [D, F]
     b_dn ~ N(0, 0.01)                          [D]
+    c ~ N(0, 1)                                [R, D]   (replicated conditioning input)
+    W_mod ~ N(0, 0.02)                         [N_mod, D]
+    b_mod ~ N(0, 0.01)                         [N_mod]
 
 Tensors a workload lacks (no attention, or no MLP) are skipped, not drawn.
 For bf16 workloads every array is rounded to bfloat16 with torch's
@@ -36,7 +39,7 @@ BIAS_STD = 0.01
 
 # Names in the order they are drawn.
 DRAW_ORDER = ("x", "w_q", "w_k", "w_v", "b_q", "b_k", "b_v", "w_o", "b_o",
-              "w_up", "b_up", "w_dn", "b_dn")
+              "w_up", "b_up", "w_dn", "b_dn", "c", "w_mod", "b_mod")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -52,6 +55,8 @@ class Workload:
     dtype: str          # "f32" or "bf16"
     description: str = ""
     mlp_act: str = "gelu_tanh"   # or "swiglu" (packed gate/up, blocks [1, 1])
+    mod_rows: int = 0            # rows R of the replicated modulation input
+    mod_out: int = 0             # N_mod, output features of the modulation projection
 
     @property
     def has_attn(self) -> bool:
@@ -60,6 +65,10 @@ class Workload:
     @property
     def has_mlp(self) -> bool:
         return self.ffn > 0
+
+    @property
+    def has_mod(self) -> bool:
+        return self.mod_out > 0
 
 
 # The five workloads of the tensor-parallel block shard.  Token count 4608 is
@@ -88,13 +97,21 @@ C7 = Workload("single_swiglu_bf16_T16384_D6144_H48_F18432_P4", 16384, 6144, 48, 
               4, "bf16", "bf16 single-stream SwiGLU block, all 4 rank shards then partial reduce",
               mlp_act="swiglu")
 
-WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5_P4, C5_P2, C6, C7)}
+# AdaLN modulation projection of the wide block (shift, scale and gate for
+# attention and MLP: 6 x 6144 outputs) sharded "rowwise_split_input": every
+# rank holds the replicated conditioning rows and a quarter of the input
+# features.  8 rows: one conditioning vector per sample of a batch of 8.
+C8 = Workload("adaln_mod_bf16_R8_D6144_N36864_P4", 0, 6144, 0, 0, 0, 4, "bf16",
+              "bf16 AdaLN modulation projection, all 4 rank shards then partial reduce",
+              mod_rows=8, mod_out=36864)
+
+WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5_P4, C5_P2, C6, C7, C8)}
 
 
 def _shapes(w: Workload) -> Dict[str, tuple]:
     T, D, F = w.tokens, w.hidden, w.ffn
     HD = w.num_heads * w.head_dim
-    shapes = {"x": (T, D)}
+    shapes = {"x": (T, D)} if T > 0 else {}
     if w.has_attn:
         shapes.update(w_q=(HD, D), w_k=(HD, D), w_v=(HD, D),
                       b_q=(HD,), b_k=(HD,), b_v=(HD,),
@@ -102,11 +119,13 @@ def _shapes(w: Workload) -> Dict[str, tuple]:
     if w.has_mlp:
         U = 2 * F if w.mlp_act == "swiglu" else F
         shapes.update(w_up=(U, D), b_up=(U,), w_dn=(D, F), b_dn=(D,))
+    if w.has_mod:
+        shapes.update(c=(w.mod_rows, D), w_mod=(w.mod_out, D), b_mod=(w.mod_out,))
     return shapes
 
 
 def _std(name: str) -> float:
-    if name == "x":
+    if name in ("x", "c"):
         return 1.0
     return WEIGHT_STD if name.startswith("w_") else BIAS_STD
 
