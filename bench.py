@@ -78,14 +78,18 @@ def cpu_baseline(w, tokens_sample: int = 12288):
     tokens_sample = min(tokens_sample, w.tokens)
     inp = tp_inputs.make_inputs(w, seed=0, tokens=tokens_sample)
     t0 = time.perf_counter()
-    O.rank_forward(inp["x"], inp.values, w.tp_degree, 0, w.num_heads, w.head_dim, bf16=True,
-                   mlp_act=w.mlp_act)
+    if w.has_attn or w.has_mlp:
+        O.rank_forward(inp["x"], inp.values, w.tp_degree, 0, w.num_heads, w.head_dim, bf16=True,
+                       mlp_act=w.mlp_act)
+    if w.has_mod:
+        O.split_input_rank(inp["c"], inp["w_mod"], w.tp_degree, 0)
     dt = time.perf_counter() - t0
     T = tokens_sample
-    flops = sum(work for _src, work, bound in step_kernels(w, T).values() if bound == "mfma")
+    flops = step_flops(w, T)
+    what = f"the first {T} tokens" if T > 0 else f"its {w.mod_rows} conditioning rows"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"rank 0 of {w.tp_degree} of {w.name} on the first {T} tokens: "
-                      f"{flops / 1e9:.0f} GFLOP fp64 in {dt:.1f} s",
+            "sample": f"rank 0 of {w.tp_degree} of {w.name} on {what}: "
+                      f"{flops / 1e9:.1f} GFLOP fp64 in {dt:.2f} s",
             "seconds": round(dt, 2), "cpu_count": os.cpu_count()}
 
 
@@ -105,10 +109,37 @@ def step_kernels(w, T):
         kernels["colwise_qkv"] = ("gemm_bf16.hip", 2 * T * D * 3 * Dr, "mfma")
         kernels["attention"] = ("attn_fwd.hip", 4 * T * T * d * Hr, "mfma")
         kernels["rowwise_attn_out"] = ("gemm_bf16.hip", 2 * T * Dr * D, "mfma")
-    else:
+    elif w.has_mlp:
         kernels["colwise_mlp_up"] = ("gemm_bf16.hip", 2 * T * D * U, "mfma")
         kernels["rowwise_mlp_down"] = ("gemm_bf16.hip", 2 * T * Fr * D, "mfma")
+    if w.has_mod:
+        # few-row split-input partial: streams the weight slice; bytes =
+        # weight slice + replicated input slice + fp32 partial written
+        R, Kr, N = w.mod_rows, D // P, w.mod_out
+        kernels["split_input_mod"] = ("skinny_bf16.hip", 2 * N * Kr + 2 * R * Kr + 4 * R * N, "hbm")
     return kernels
+
+
+def step_text(w):
+    parts = []
+    if w.has_mod:
+        parts.append(f"split-input modulation partial over {w.mod_rows} replicated rows")
+    if w.has_attn and w.has_mlp:
+        parts.append("fused colwise QKV+MLP-in, attention, packed rowwise out")
+    elif w.has_attn:
+        parts.append("colwise QKV, attention, rowwise attention out")
+    elif w.has_mlp:
+        parts.append("colwise MLP-in, rowwise MLP-down")
+    return "per rank: " + "; ".join(parts) + "; then partial reduce"
+
+
+def step_flops(w, T):
+    """Algorithmic FLOPs of one rank's pass (GEMMs 2 M N K, attention 4 T^2 d
+    per head, the modulation projection 2 R K_r N)."""
+    f = sum(work for _src, work, bound in step_kernels(w, T).values() if bound == "mfma")
+    if w.has_mod:
+        f += 2 * w.mod_rows * (w.hidden // w.tp_degree) * w.mod_out
+    return f
 
 
 def main():
@@ -135,10 +166,6 @@ def main():
 
     w = tp_inputs.WORKLOADS[args.workload]
     T, D, P, d = w.tokens, w.hidden, w.tp_degree, w.head_dim
-    Dr = D // P if w.has_attn else 0
-    Fr = w.ffn // P
-    Hr = w.num_heads // P
-
     log(f"[bench] generating inputs for {w.name}")
     t0 = time.time()
     inp = tp_inputs.make_inputs(w, seed=0)
@@ -146,18 +173,30 @@ def main():
     # and output projections)
     packed = w.mlp_act == "swiglu" and w.has_attn
     shards = H.create_shards(w, inp, packed=packed)
-    x = H.to_device(inp, "x")
+    x = H.to_device(inp, "x") if w.tokens > 0 else None
     biases = H.rowwise_biases(w, inp)
+    c = H.to_device(inp, "c") if w.has_mod else None
+    mod_bias = [H.f32_device(inp.values["b_mod"])] if w.has_mod else []
     del inp
-    partials = [torch.empty((T, D), dtype=torch.float32, device="cuda") for _ in range(P)]
-    bufs = H.RankBuffers(shards[0], T, partial=partials[0])
-    y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    block = w.has_attn or w.has_mlp
+    if block:
+        partials = [torch.empty((T, D), dtype=torch.float32, device="cuda") for _ in range(P)]
+        bufs = H.RankBuffers(shards[0], T, partial=partials[0])
+        y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    if w.has_mod:
+        mod_parts = [torch.empty((w.mod_rows, w.mod_out), dtype=torch.float32, device="cuda")
+                     for _ in range(P)]
+        y_mod = torch.empty((w.mod_rows, w.mod_out), dtype=torch.float32, device="cuda")
     log(f"[bench] setup {time.time() - t0:.1f} s")
 
     # kernels of a step, with algorithmic work per launch
     kernels = step_kernels(w, T)
-    reduce_bytes = (P + 1) * T * D * 4 + len(biases) * D * 4
-    kernels["partial_reduce"] = ("partial_reduce.hip", reduce_bytes, "hbm")
+    if block:
+        reduce_bytes = (P + 1) * T * D * 4 + len(biases) * D * 4
+        kernels["partial_reduce"] = ("partial_reduce.hip", reduce_bytes, "hbm")
+    if w.has_mod:
+        kernels["mod_reduce"] = ("partial_reduce.hip",
+                                 (P + 1) * w.mod_rows * w.mod_out * 4 + w.mod_out * 4, "hbm")
 
     stream = torch.cuda.current_stream()
     if args.copy_calibration:
@@ -181,6 +220,11 @@ def main():
             ev.setdefault(name, []).append((a, b))
 
         for r, s in enumerate(shards):
+            if w.has_mod:
+                mark("split_input_mod", lambda: tp.tp_rowwise_split_input_partial(
+                    s, tp.TP_ADALN_MOD, w.mod_rows, c, mod_parts[r]))
+            if not block:
+                continue
             bufs.partial = partials[r]
             if w.has_attn and w.has_mlp:
                 mark("colwise_qkv_up", lambda: tp.tp_colwise_qkv_up(s, T, x, bufs.qkv, bufs.h))
@@ -196,7 +240,10 @@ def main():
                 mark("colwise_mlp_up", lambda: tp.tp_colwise_linear(s, tp.TP_MLP_UP, T, x, bufs.h))
                 mark("rowwise_mlp_down", lambda: tp.tp_rowwise_linear_partial(
                     s, tp.TP_MLP_DOWN, T, bufs.h, bufs.partial))
-        mark("partial_reduce", lambda: tp.tp_partial_reduce(partials, biases, y))
+        if block:
+            mark("partial_reduce", lambda: tp.tp_partial_reduce(partials, biases, y))
+        if w.has_mod:
+            mark("mod_reduce", lambda: tp.tp_partial_reduce(mod_parts, mod_bias, y_mod))
 
     for _ in range(args.warmup):
         step()
@@ -218,8 +265,7 @@ def main():
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
-    step_flops = sum(k[1] for n, k in kernels.items() if k[2] == "mfma") * P
-    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    value = step_flops(w, T) * P / (ms_per_step * 1e-3) / 1e12
 
     per_kernel = {}
     for name, (src, work, bound) in kernels.items():
@@ -277,8 +323,7 @@ def main():
         "config": {"workload": w.name, "tokens": T, "hidden": D, "num_heads": w.num_heads,
                    "head_dim": d, "ffn": w.ffn, "tp_degree": P, "ranks_per_step": P,
                    "mlp_act": w.mlp_act, "packed_checkpoint": packed,
-                   "step": "per rank: fused colwise QKV+MLP-in, attention, packed rowwise out; "
-                           "then partial reduce"},
+                   "step": step_text(w)},
         "roofline": roof,
         "kernels": per_kernel,
         "cpu_baseline": cpu,

@@ -18,6 +18,10 @@
  *     block: [1, 1] for a SwiGLU gate/up projection, [1, 1, 1, 3, 3] for a
  *     fused Q, K, V, gate, up projection at mlp_ratio 3; a rowwise to_out may
  *     pack [inner_dim, mlp_hidden_dim];
+ *   - style table, "rowwise_split_input", and §"O que deixar de fora": an
+ *     independent projection whose input is replicated (a large AdaLN
+ *     modulation projection reading the timestep embedding) is sharded by
+ *     input features, each rank slicing its own copy of the input;
  *   - §"Restrições e verificação" (约束与验证): tp_degree divides the head
  *     count and each packed block on its own, checked before any weight is
  *     touched;
@@ -91,11 +95,13 @@ typedef enum tp_layer {
   TP_MLP_UP = 1,             /* colwise: FFN in-projection, fused bias + activation */
   TP_ATTN_OUT = 2,           /* rowwise: to_out.0 (attention out-projection) */
   TP_MLP_DOWN = 3,           /* rowwise: FFN out-projection */
-  TP_BLOCK_OUT = 4           /* rowwise, packed over [inner_dim, ffn]: [o_r | h_r] */
+  TP_BLOCK_OUT = 4,          /* rowwise, packed over [inner_dim, ffn]: [o_r | h_r] */
+  TP_ADALN_MOD = 5           /* rowwise_split_input: AdaLN modulation projection */
 } tp_layer;
 
 /* UNSHARDED sizes of the block and this shard's place in the group.
- * num_heads == 0: no attention layers; ffn == 0: no MLP layers. */
+ * num_heads == 0: no attention layers; ffn == 0: no MLP layers; mod_out == 0:
+ * no modulation projection. */
 typedef struct tp_block_config {
   int32_t tp_degree;         /* P >= 1 */
   int32_t rank;              /* 0 <= rank < P */
@@ -105,6 +111,8 @@ typedef struct tp_block_config {
   int64_t ffn;               /* F */
   tp_dtype dtype;
   tp_mlp_act mlp_act;        /* 0 = GELU-tanh */
+  int64_t mod_in;            /* input features of the AdaLN modulation projection (0: none) */
+  int64_t mod_out;           /* its output features */
 } tp_block_config;
 
 /* UNSHARDED weights in HOST memory, element type = config dtype (bf16 as raw
@@ -128,6 +136,7 @@ typedef struct tp_block_weights {
   const void *w_down;              /* [D, F], row stride ld_down */
   int64_t ld_o;                    /* row stride of w_o in elements; 0 = H*d */
   int64_t ld_down;                 /* row stride of w_down in elements; 0 = F */
+  const void *w_mod;               /* [mod_out, mod_in]; its bias goes to tp_partial_reduce */
 } tp_block_weights;
 
 typedef struct tp_block_shard tp_block_shard;  /* opaque; owns the device weight slices */
@@ -142,15 +151,18 @@ typedef struct tp_block_shard tp_block_shard;  /* opaque; owns the device weight
  *                           interleaved in blocks of 32)
  *   rowwise (dim-1 cols):   W_o_r   = W_o[:, R_r]                           [D, D_r]
  *                           W_dn_r  = W_down[:, C_r]                        [D, F_r]
- * with D_r = D/P, R_r = [r*D_r, (r+1)*D_r), F_r = F/P, C_r = [r*F_r, (r+1)*F_r).
+ *                           W_mod_r = W_mod[:, M_r]               [mod_out, mod_in/P]
+ * with D_r = D/P, R_r = [r*D_r, (r+1)*D_r), F_r = F/P, C_r = [r*F_r, (r+1)*F_r),
+ * M_r = [r*mod_in/P, (r+1)*mod_in/P).
  * Checks, in order, before any allocation [TP page, §Restrições e
  * verificação]: out != NULL (else TP_ERR_ARG); cfg, w != NULL; dtype and
- * mlp_act known; P >= 1 and 0 <= rank < P; D > 0, H >= 0, F >= 0, not both H
- * and F zero, d > 0 if H > 0 (TP_ERR_ARG); H*d == D, P | H, P | D (each Q/K/V
- * block), P | F (each gate/up block) (TP_ERR_DIVISIBILITY); D, D_r, F_r
- * multiples of 8, and of 32 for F_r with SwiGLU (TP_ERR_UNSUPPORTED); the
- * weights the enabled layers need are non-NULL, ld_o is 0 or >= H*d, ld_down
- * is 0 or >= F (TP_ERR_ARG).  On any error *out is set to NULL and nothing is allocated
+ * mlp_act known; P >= 1 and 0 <= rank < P; D > 0, H >= 0, F >= 0, mod_in >= 0,
+ * mod_out >= 0 (mod_in > 0 exactly when mod_out > 0), not all of H, F and
+ * mod_out zero, d > 0 if H > 0 (TP_ERR_ARG); H*d == D, P | H, P | D (each
+ * Q/K/V block), P | F (each gate/up block), P | mod_in (TP_ERR_DIVISIBILITY);
+ * D, D_r, F_r, mod_in/P, mod_out multiples of 8, and of 32 for F_r with
+ * SwiGLU (TP_ERR_UNSUPPORTED); the weights the enabled layers need are
+ * non-NULL, ld_o is 0 or >= H*d, ld_down is 0 or >= F (TP_ERR_ARG).  On any error *out is set to NULL and nothing is allocated
  * (or everything allocated so far is freed). */
 TP_API tp_status tp_block_shard_create(const tp_block_config *cfg, const tp_block_weights *w,
                                 tp_block_shard **out);
@@ -207,6 +219,23 @@ TP_API tp_status tp_attn_heads(tp_block_shard *shard, int64_t tokens, const void
 TP_API tp_status tp_rowwise_linear_partial(tp_block_shard *shard, tp_layer layer, int64_t tokens,
                                     const void *x_local, int64_t ldx, float *partial,
                                     int64_t ldp, int accumulate, void *stream);
+
+/* "rowwise_split_input" partial [TP page, style table; §O que deixar de
+ * fora]: the input is REPLICATED (every rank holds all of it) and the rank
+ * slices its own input features from it:
+ *   partial[t, n] (+)= sum_{k in K_r} x_full[t, k] * W[n, k]      (no bias)
+ * layer TP_ADALN_MOD: x_full [rows, mod_in], K_r = M_r, partial [rows, mod_out];
+ * layer TP_ATTN_OUT:  x_full [rows, H*d] (all heads' output), K_r = R_r, partial [rows, D];
+ * layer TP_MLP_DOWN:  x_full [rows, F], K_r = C_r, partial [rows, D];
+ * layer TP_BLOCK_OUT: x_full [rows, H*d + F] = [o | h], K_r = R_r and H*d + C_r
+ *                     (the packed row blocks), partial [rows, D].
+ * x_full: device, config dtype, ldx >= its width; partial: device fp32, ldp >=
+ * its width; accumulate = 0 stores, 1 adds.  rows == 0 is a no-op.  Results
+ * equal tp_rowwise_linear_partial on the sliced columns.  The summed partials
+ * plus the bias (tp_partial_reduce) give the unsharded projection. */
+TP_API tp_status tp_rowwise_split_input_partial(tp_block_shard *shard, tp_layer layer, int64_t rows,
+                                                const void *x_full, int64_t ldx, float *partial,
+                                                int64_t ldp, int accumulate, void *stream);
 
 /* The layer-boundary AllReduce of the TP page's intro, on one GPU: all
  * simulated ranks' partials summed in rank order, then the rowwise biases:

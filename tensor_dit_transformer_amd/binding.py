@@ -35,11 +35,13 @@ TP_MLP_UP = 1
 TP_ATTN_OUT = 2
 TP_MLP_DOWN = 3
 TP_BLOCK_OUT = 4
+TP_ADALN_MOD = 5
 
 EXPORTED = (
     "tp_block_shard_create", "tp_block_shard_destroy", "tp_colwise_linear",
     "tp_colwise_qkv_up", "tp_attn_heads", "tp_rowwise_linear_partial",
     "tp_partial_reduce", "tp_status_string", "tp_last_error_detail",
+    "tp_rowwise_split_input_partial",
 )
 
 
@@ -47,15 +49,17 @@ class TpBlockConfig(ctypes.Structure):
     _fields_ = [("tp_degree", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("hidden", ctypes.c_int64), ("num_heads", ctypes.c_int64),
                 ("head_dim", ctypes.c_int64), ("ffn", ctypes.c_int64),
-                ("dtype", ctypes.c_int), ("mlp_act", ctypes.c_int)]
+                ("dtype", ctypes.c_int), ("mlp_act", ctypes.c_int),
+                ("mod_in", ctypes.c_int64), ("mod_out", ctypes.c_int64)]
 
 
-_WEIGHT_FIELDS = ("w_q", "w_k", "w_v", "b_q", "b_k", "b_v", "w_o", "w_up", "b_up", "w_down")
+_WEIGHT_FIELDS = ("w_q", "w_k", "w_v", "b_q", "b_k", "b_v", "w_o", "w_up", "b_up", "w_down",
+                  "w_mod")
 
 
 class TpBlockWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS] + [
-        ("ld_o", ctypes.c_int64), ("ld_down", ctypes.c_int64)]
+    _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS[:10]] + [
+        ("ld_o", ctypes.c_int64), ("ld_down", ctypes.c_int64), ("w_mod", ctypes.c_void_p)]
 
 
 class TpError(RuntimeError):
@@ -86,10 +90,13 @@ def lib() -> ctypes.CDLL:
         L.tp_attn_heads.argtypes = [vp, i64, vp, i64, vp, i64, vp]
         L.tp_rowwise_linear_partial.argtypes = [vp, ctypes.c_int, i64, vp, i64, vp, i64,
                                                 ctypes.c_int, vp]
+        L.tp_rowwise_split_input_partial.argtypes = [vp, ctypes.c_int, i64, vp, i64, vp, i64,
+                                                     ctypes.c_int, vp]
         L.tp_partial_reduce.argtypes = [ctypes.POINTER(vp), i32, i64, ctypes.POINTER(vp), i32,
                                         i64, i64, vp, i64, vp]
         for f in ("tp_block_shard_create", "tp_colwise_linear", "tp_colwise_qkv_up",
-                  "tp_attn_heads", "tp_rowwise_linear_partial", "tp_partial_reduce"):
+                  "tp_attn_heads", "tp_rowwise_linear_partial", "tp_partial_reduce",
+                  "tp_rowwise_split_input_partial"):
             getattr(L, f).restype = ctypes.c_int
         L.tp_status_string.argtypes = [ctypes.c_int]
         L.tp_status_string.restype = ctypes.c_char_p
@@ -161,6 +168,8 @@ class TpBlockShard:
         self.ffn = cfg.ffn
         self.dtype = cfg.dtype
         self.mlp_act = cfg.mlp_act
+        self.mod_in = cfg.mod_in
+        self.mod_out = cfg.mod_out
         P = cfg.tp_degree
         self.d_r = cfg.hidden // P if cfg.num_heads > 0 else 0
         self.f_r = cfg.ffn // P
@@ -181,8 +190,10 @@ class TpBlockShard:
 
 
 def make_config(tp_degree: int, rank: int, hidden: int, num_heads: int, head_dim: int,
-                ffn: int, dtype: int, mlp_act: int = TP_MLP_GELU_TANH) -> TpBlockConfig:
-    return TpBlockConfig(tp_degree, rank, hidden, num_heads, head_dim, ffn, dtype, mlp_act)
+                ffn: int, dtype: int, mlp_act: int = TP_MLP_GELU_TANH, mod_in: int = 0,
+                mod_out: int = 0) -> TpBlockConfig:
+    return TpBlockConfig(tp_degree, rank, hidden, num_heads, head_dim, ffn, dtype, mlp_act,
+                         mod_in, mod_out)
 
 
 def _weight_shapes(cfg: TpBlockConfig):
@@ -190,7 +201,8 @@ def _weight_shapes(cfg: TpBlockConfig):
     U = 2 * F if cfg.mlp_act == TP_MLP_SWIGLU else F
     return {"w_q": (HD, D), "w_k": (HD, D), "w_v": (HD, D), "b_q": (HD,), "b_k": (HD,),
             "b_v": (HD,), "w_o": (D, HD), "w_up": (U, D), "b_up": (U,), "w_down": (D, F),
-            "w_in": (3 * HD + U, D), "b_in": (3 * HD + U,), "w_out": (D, HD + F)}
+            "w_in": (3 * HD + U, D), "b_in": (3 * HD + U,), "w_out": (D, HD + F),
+            "w_mod": (cfg.mod_out, cfg.mod_in)}
 
 
 def _host_weights(weights: Dict[str, np.ndarray], cfg: TpBlockConfig):
@@ -281,6 +293,18 @@ def tp_rowwise_linear_partial(shard: TpBlockShard, layer: int, tokens: int, x_lo
     pp, ldp = _mat(partial, "partial", tokens, shard.hidden, TP_F32)
     _check(lib().tp_rowwise_linear_partial(shard.handle, layer, tokens, xp, ldx, pp, ldp,
                                            1 if accumulate else 0, _stream(stream)))
+
+
+def tp_rowwise_split_input_partial(shard: TpBlockShard, layer: int, rows: int, x_full, partial,
+                                   accumulate: bool = False, stream=None) -> None:
+    HD = shard.d_r * shard.tp_degree
+    width, n = {TP_ADALN_MOD: (shard.mod_in, shard.mod_out), TP_ATTN_OUT: (HD, shard.hidden),
+                TP_MLP_DOWN: (shard.ffn, shard.hidden),
+                TP_BLOCK_OUT: (HD + shard.ffn, shard.hidden)}.get(layer, (0, 0))
+    xp, ldx = _mat(x_full, "x_full", rows, width, shard.dtype)
+    pp, ldp = _mat(partial, "partial", rows, n, TP_F32)
+    _check(lib().tp_rowwise_split_input_partial(shard.handle, layer, rows, xp, ldx, pp, ldp,
+                                                1 if accumulate else 0, _stream(stream)))
 
 
 def tp_partial_reduce(partials: Sequence, biases: Sequence, out, stream=None) -> None:

@@ -29,6 +29,9 @@ struct tp_block_shard {
                     //   in blocks of 32 rows: gate 0-31, up 0-31, gate 32-63, ...
   float* b_col;     // [n_col] fp32, the biases in the same row order
   void* w_row;      // [D, k_row]      = [W_o[:, R_r] | W_dn[:, C_r]]
+  bool mod;
+  int64_t mod_in, mod_out, mod_kr;  // modulation projection: K, N, K_r = K / P
+  void* w_mod;      // [mod_out, mod_kr] = W_mod[:, M_r]
 };
 
 namespace {
@@ -109,6 +112,7 @@ void free_shard(tp_block_shard* s) {
   if (s->w_col) (void)hipFree(s->w_col);
   if (s->b_col) (void)hipFree(s->b_col);
   if (s->w_row) (void)hipFree(s->w_row);
+  if (s->w_mod) (void)hipFree(s->w_mod);
   delete s;
 }
 
@@ -118,6 +122,19 @@ tp_status launch(const tpk::GemmProblem& p, const tpk::GemmEpilogue& ep, tpk::Ou
                                      : tpk::launch_gemm_f32(p, ep, kind, stream);
   if (e != hipSuccess) return hip_fail(e, "GEMM launch");
   return TP_OK;
+}
+
+// A rowwise partial (no bias, fp32 out): the few-row bf16 kernel when the
+// input has at most 64 rows, else the GEMM.
+tp_status rowwise(const tpk::GemmProblem& p, float* partial, int64_t ldp, bool accumulate,
+                  tp_dtype dt, hipStream_t stream) {
+  if (dt == TP_BF16 && tpk::skinny_bf16_fits(p)) {
+    const hipError_t e = tpk::launch_skinny_bf16(p, partial, ldp, accumulate, stream);
+    if (e != hipSuccess) return hip_fail(e, "rowwise launch");
+    return TP_OK;
+  }
+  const tpk::GemmEpilogue ep{nullptr, p.N, tpk::Act::NONE, p.N, partial, ldp, nullptr, 0};
+  return launch(p, ep, accumulate ? tpk::OutKind::F32_ACC : tpk::OutKind::F32_STORE, dt, stream);
 }
 
 // Colwise GEMM over weight rows [row0, row0 + n_w) of the packed slice:
@@ -150,8 +167,12 @@ TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_bloc
                 d = cfg->head_dim, F = cfg->ffn;
   if (P < 1 || r < 0 || r >= P)
     return fail(TP_ERR_ARG, "rank %lld not in [0, tp_degree=%lld)", (long long)r, (long long)P);
-  if (D <= 0 || H < 0 || F < 0) return fail(TP_ERR_ARG, "sizes must be positive");
-  if (H == 0 && F == 0) return fail(TP_ERR_ARG, "neither attention (num_heads) nor MLP (ffn)");
+  const int64_t Mi = cfg->mod_in, Mo = cfg->mod_out;
+  if (D <= 0 || H < 0 || F < 0 || Mi < 0 || Mo < 0) return fail(TP_ERR_ARG, "sizes must be positive");
+  if ((Mi > 0) != (Mo > 0))
+    return fail(TP_ERR_ARG, "mod_in and mod_out must both be zero or both positive");
+  if (H == 0 && F == 0 && Mo == 0)
+    return fail(TP_ERR_ARG, "neither attention (num_heads), MLP (ffn) nor modulation (mod_out)");
   if (H > 0 && d <= 0) return fail(TP_ERR_ARG, "head_dim must be positive");
   if (H > 0) {
     if (H * d != D)
@@ -167,10 +188,15 @@ TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_bloc
   if (F % P)
     return fail(TP_ERR_DIVISIBILITY, "tp_degree %lld does not divide ffn %lld", (long long)P,
                 (long long)F);
+  if (Mi % P)
+    return fail(TP_ERR_DIVISIBILITY, "tp_degree %lld does not divide the modulation input %lld",
+                (long long)P, (long long)Mi);
   const int64_t Dr = H > 0 ? D / P : 0, Fr = F / P;
   const bool swiglu = F > 0 && cfg->mlp_act == TP_MLP_SWIGLU;
   if (D % 8 || Dr % 8 || Fr % 8)
     return fail(TP_ERR_UNSUPPORTED, "hidden, hidden/tp and ffn/tp must be multiples of 8");
+  if ((Mi / P) % 8 || Mo % 8)
+    return fail(TP_ERR_UNSUPPORTED, "mod_in/tp and mod_out must be multiples of 8");
   if (swiglu && Fr % 32)
     return fail(TP_ERR_UNSUPPORTED, "SwiGLU needs ffn/tp (%lld) to be a multiple of 32",
                 (long long)Fr);
@@ -178,6 +204,7 @@ TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_bloc
     return fail(TP_ERR_ARG, "attention configured but w_q/w_k/w_v/w_o missing");
   if (F > 0 && (!w->w_up || !w->w_down))
     return fail(TP_ERR_ARG, "MLP configured but w_up/w_down missing");
+  if (Mo > 0 && !w->w_mod) return fail(TP_ERR_ARG, "modulation configured but w_mod missing");
   const int64_t ld_o = w->ld_o ? w->ld_o : H * d, ld_dn = w->ld_down ? w->ld_down : F;
   if (H > 0 && ld_o < H * d)
     return fail(TP_ERR_ARG, "ld_o (%lld) < num_heads*head_dim (%lld)", (long long)ld_o,
@@ -195,15 +222,21 @@ TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_bloc
   s->n_col = 3 * Dr + s->n_up;
   s->dn_col0 = Dr;
   s->k_row = Dr + Fr;
+  s->mod = Mo > 0; s->mod_in = Mi; s->mod_out = Mo; s->mod_kr = Mi / P;
   hipError_t e = hipGetDevice(&s->device);
   if (e != hipSuccess) { free_shard(s); return hip_fail(e, "hipGetDevice"); }
 
   const size_t es = s->es;
-  if ((e = hipMalloc(&s->w_col, (size_t)(s->n_col * D) * es)) != hipSuccess ||
-      (e = hipMalloc(reinterpret_cast<void**>(&s->b_col), (size_t)s->n_col * sizeof(float))) != hipSuccess ||
-      (e = hipMalloc(&s->w_row, (size_t)(D * s->k_row) * es)) != hipSuccess) {
+  const bool block = s->attn || s->mlp;
+  if (block && ((e = hipMalloc(&s->w_col, (size_t)(s->n_col * D) * es)) != hipSuccess ||
+                (e = hipMalloc(reinterpret_cast<void**>(&s->b_col), (size_t)s->n_col * sizeof(float))) != hipSuccess ||
+                (e = hipMalloc(&s->w_row, (size_t)(D * s->k_row) * es)) != hipSuccess)) {
     free_shard(s);
     return hip_fail(e, "hipMalloc of the weight slices");
+  }
+  if (s->mod && (e = hipMalloc(&s->w_mod, (size_t)(Mo * s->mod_kr) * es)) != hipSuccess) {
+    free_shard(s);
+    return hip_fail(e, "hipMalloc of the modulation slice");
   }
 
   // Colwise slices: contiguous blocks of dim-0 rows, one per packed block.
@@ -242,7 +275,7 @@ TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_bloc
                    cfg->dtype);
     }
   }
-  if (e == hipSuccess)
+  if (e == hipSuccess && block)
     e = hipMemcpy(s->b_col, bias.data(), bias.size() * sizeof(float), hipMemcpyHostToDevice);
   // Rowwise slices: dim-1 column blocks, copied as strided 2-D regions.
   char* wr = static_cast<char*>(s->w_row);
@@ -253,6 +286,11 @@ TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_bloc
   if (e == hipSuccess && s->mlp)
     e = hipMemcpy2D(wr + s->dn_col0 * es, dpitch, static_cast<const char*>(w->w_down) + r * Fr * es,
                     (size_t)ld_dn * es, (size_t)Fr * es, (size_t)D, hipMemcpyHostToDevice);
+  // Modulation slice ("rowwise_split_input"): dim-1 columns M_r.
+  if (e == hipSuccess && s->mod)
+    e = hipMemcpy2D(s->w_mod, (size_t)s->mod_kr * es,
+                    static_cast<const char*>(w->w_mod) + r * s->mod_kr * es, (size_t)Mi * es,
+                    (size_t)s->mod_kr * es, (size_t)Mo, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     free_shard(s);
     return hip_fail(e, "weight slice upload");
@@ -362,9 +400,62 @@ TP_API tp_status tp_rowwise_linear_partial(tp_block_shard* s, tp_layer layer, in
     return fail(TP_ERR_ARG, "partial overlaps x_local");
   const tpk::GemmProblem p{x_local, ldx, static_cast<const char*>(s->w_row) + col0 * s->es, s->k_row,
                            (int)tokens, (int)s->D, (int)k};
-  const tpk::GemmEpilogue ep{nullptr, (int)s->D, tpk::Act::NONE, (int)s->D, partial, ldp, nullptr, 0};
-  return launch(p, ep, accumulate ? tpk::OutKind::F32_ACC : tpk::OutKind::F32_STORE, s->cfg.dtype,
-                static_cast<hipStream_t>(stream));
+  return rowwise(p, partial, ldp, accumulate != 0, s->cfg.dtype, static_cast<hipStream_t>(stream));
+}
+
+TP_API tp_status tp_rowwise_split_input_partial(tp_block_shard* s, tp_layer layer, int64_t rows,
+                                                const void* x_full, int64_t ldx, float* partial,
+                                                int64_t ldp, int accumulate, void* stream) {
+  tp_status st = check_shard(s);
+  if (st != TP_OK) return st;
+  const int64_t r = s->cfg.rank, HD = s->Dr * s->cfg.tp_degree, F = s->cfg.ffn;
+  int64_t width, n;        // replicated input width, output width
+  if (layer == TP_ADALN_MOD) {
+    if (!s->mod) return fail(TP_ERR_ARG, "TP_ADALN_MOD: shard has no modulation projection");
+    width = s->mod_in; n = s->mod_out;
+  } else if (layer == TP_ATTN_OUT) {
+    if (!s->attn) return fail(TP_ERR_ARG, "TP_ATTN_OUT: shard has no attention layers");
+    width = HD; n = s->D;
+  } else if (layer == TP_MLP_DOWN) {
+    if (!s->mlp) return fail(TP_ERR_ARG, "TP_MLP_DOWN: shard has no MLP layers");
+    width = F; n = s->D;
+  } else if (layer == TP_BLOCK_OUT) {
+    if (!s->attn || !s->mlp) return fail(TP_ERR_ARG, "TP_BLOCK_OUT needs attention and MLP");
+    width = HD + F; n = s->D;
+  } else {
+    return fail(TP_ERR_ARG, "layer %d is not rowwise", (int)layer);
+  }
+  if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_ARG, "accumulate must be 0 or 1");
+  if ((st = check_tokens(rows)) != TP_OK) return st;
+  if ((st = check_matrix("x_full", x_full, ldx, width, s->es)) != TP_OK) return st;
+  if ((st = check_matrix("partial", partial, ldp, n, sizeof(float))) != TP_OK) return st;
+  if (rows == 0) return TP_OK;
+  if (overlap(x_full, span_bytes(rows, ldx, width, s->es), partial,
+              span_bytes(rows, ldp, n, sizeof(float))))
+    return fail(TP_ERR_ARG, "partial overlaps x_full");
+  const char* x = static_cast<const char*>(x_full);
+  const hipStream_t st_ = static_cast<hipStream_t>(stream);
+  const tp_dtype dt = s->cfg.dtype;
+  if (layer == TP_ADALN_MOD) {
+    const tpk::GemmProblem p{x + r * s->mod_kr * s->es, ldx, s->w_mod, s->mod_kr, (int)rows,
+                             (int)s->mod_out, (int)s->mod_kr};
+    return rowwise(p, partial, ldp, accumulate != 0, dt, st_);
+  }
+  const char* w_row = static_cast<const char*>(s->w_row);
+  // attention part: input columns R_r, weight columns [0, Dr)
+  if (layer == TP_ATTN_OUT || layer == TP_BLOCK_OUT) {
+    const tpk::GemmProblem p{x + r * s->Dr * s->es, ldx, w_row, s->k_row, (int)rows, (int)s->D,
+                             (int)s->Dr};
+    if ((st = rowwise(p, partial, ldp, accumulate != 0, dt, st_)) != TP_OK) return st;
+  }
+  // MLP part: input columns (H*d if packed) + C_r, weight columns [Dr, Dr + Fr)
+  if (layer == TP_MLP_DOWN || layer == TP_BLOCK_OUT) {
+    const int64_t c0 = (layer == TP_BLOCK_OUT ? HD : 0) + r * s->Fr;
+    const tpk::GemmProblem p{x + c0 * s->es, ldx, w_row + s->dn_col0 * s->es, s->k_row, (int)rows,
+                             (int)s->D, (int)s->Fr};
+    return rowwise(p, partial, ldp, layer == TP_BLOCK_OUT || accumulate != 0, dt, st_);
+  }
+  return TP_OK;
 }
 
 TP_API tp_status tp_partial_reduce(const float* const* partials, int32_t n_partials, int64_t ldp,

@@ -55,6 +55,13 @@ hipError_t launch_gemm_bf16(const GemmProblem& p, const GemmEpilogue& ep, OutKin
 hipError_t launch_gemm_f32(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
                            hipStream_t stream);
 
+// Rowwise partial with few rows (bf16 in, fp32 out, store or accumulate):
+// out[m, n] (+)= sum_k A[m, k] B[n, k].  Applies when 1 <= M <= 64,
+// N % 16 == 0 and K % 8 == 0 (skinny_bf16_fits); an HBM-bound weight stream.
+bool skinny_bf16_fits(const GemmProblem& p);
+hipError_t launch_skinny_bf16(const GemmProblem& p, float* out, int64_t ldo, bool accumulate,
+                              hipStream_t stream);
+
 // Non-causal multi-head attention, bf16 in/out, head_dim 128, fp32 softmax.
 // qkv: [T, 3*Dr] (Q | K | V, head j at columns j*128 of each block);
 // o: [T, Dr].

@@ -221,7 +221,7 @@ def test_struct_layouts_match_the_header(tmp_path):
     """ctypes mirrors of tp_block_config / tp_block_weights have the C
     compiler's sizes and field offsets."""
     src = tmp_path / "layout.c"
-    fields_c = ["tp_degree", "rank", "hidden", "num_heads", "head_dim", "ffn", "dtype", "mlp_act"]
+    fields_c = ["tp_degree", "rank", "hidden", "num_heads", "head_dim", "ffn", "dtype", "mlp_act", "mod_in", "mod_out"]
     fields_w = list(binding._WEIGHT_FIELDS) + ["ld_o", "ld_down"]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tp_shard.h"', 'int main(void) {',
              'printf("%zu\\n", sizeof(tp_block_config));', 'printf("%zu\\n", sizeof(tp_block_weights));']
@@ -258,3 +258,55 @@ def test_binding_packed_weights_address_the_blocks():
     assert (w.w_o, w.w_down, w.ld_o, w.ld_down) == (ob, ob + HD * 2, HD + F, HD + F)
     with pytest.raises(ValueError):      # a GELU config expects W_up [F, D], not [2F, D]
         binding._host_weights({"w_in": w_in}, tp.make_config(2, 0, D, H, d, F, tp.TP_BF16))
+
+
+@pytest.mark.parametrize("P,mi,mo,want", [
+    (4, 30, 64, tp.TP_ERR_DIVISIBILITY),     # tp_degree does not divide the modulation input
+    (4, 64, 0, tp.TP_ERR_ARG),               # mod_in without mod_out
+    (4, 0, 64, tp.TP_ERR_ARG),               # mod_out without mod_in
+    (4, -8, 64, tp.TP_ERR_ARG),
+    (4, 96, 64, None),                       # mod_in / tp = 24, a multiple of 8: accepted
+    (4, 64, 36, tp.TP_ERR_UNSUPPORTED),      # mod_out not a multiple of 8
+    (4, 80, 64, tp.TP_ERR_UNSUPPORTED),      # mod_in / tp = 20 not a multiple of 8
+])
+def test_create_modulation_checks(L, P, mi, mo, want):
+    cfg = tp.make_config(P, 0, 64, 0, 0, 0, tp.TP_BF16, mod_in=mi, mod_out=mo)
+    w = {"w_mod": np.zeros((max(mo, 1), max(mi, 1)), np.uint16)}
+    st, out = _create(L, cfg, w)
+    if (mi, mo) == (96, 64):
+        assert st != tp.TP_ERR_UNSUPPORTED and st != tp.TP_ERR_ARG   # valid: created or HIP error
+        if out:
+            L.tp_block_shard_destroy(out)
+        return
+    assert st == want, tp.tp_last_error_detail()
+    assert out is None
+
+
+def test_create_modulation_needs_its_weight(L):
+    st, out = _create(L, tp.make_config(4, 0, 64, 0, 0, 0, tp.TP_BF16, mod_in=64, mod_out=64))
+    assert st == tp.TP_ERR_ARG and "w_mod" in tp.tp_last_error_detail()
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("mi", [64, 96, 100])
+def test_modulation_create_agrees_with_oracle(L, P, mi):
+    try:
+        O.check_config(P, 0, 64, 0, 0, 0, mod_in=mi)
+        kind = None
+    except O.ShardConfigError as e:
+        kind = e.kind
+    st, out = _create(L, tp.make_config(P, 0, 64, 0, 0, 0, tp.TP_BF16, mod_in=mi, mod_out=64),
+                      {"w_mod": np.zeros((64, mi), np.uint16)})
+    if out:
+        L.tp_block_shard_destroy(out)
+    if kind == "divisibility":
+        assert st == tp.TP_ERR_DIVISIBILITY
+    else:
+        assert st in (tp.TP_OK, tp.TP_ERR_HIP, tp.TP_ERR_UNSUPPORTED, tp.TP_ERR_OOM)
+        if st == tp.TP_ERR_UNSUPPORTED:
+            assert (mi // P) % 8
+
+
+def test_split_input_rejects_null_shard(L):
+    vp = ctypes.c_void_p(0x10000)
+    assert L.tp_rowwise_split_input_partial(None, tp.TP_ADALN_MOD, 8, vp, 64, vp, 64, 0, None) == tp.TP_ERR_ARG

@@ -20,7 +20,7 @@ def to_device(inp: tp_inputs.Inputs, name: str) -> torch.Tensor:
 
 def host_weights(inp: tp_inputs.Inputs) -> Dict[str, np.ndarray]:
     src = inp.bits if inp.bits is not None else inp.values
-    out = {k: v for k, v in src.items() if k != "x"}
+    out = {k: v for k, v in src.items() if k not in ("x", "c")}
     if "w_dn" in out:
         out["w_down"] = out.pop("w_dn")
     return out
@@ -29,7 +29,8 @@ def host_weights(inp: tp_inputs.Inputs) -> Dict[str, np.ndarray]:
 def config(w: tp_inputs.Workload, rank: int) -> tp.TpBlockConfig:
     dt = tp.TP_BF16 if w.dtype == "bf16" else tp.TP_F32
     act = tp.TP_MLP_SWIGLU if w.mlp_act == "swiglu" else tp.TP_MLP_GELU_TANH
-    return tp.make_config(w.tp_degree, rank, w.hidden, w.num_heads, w.head_dim, w.ffn, dt, act)
+    return tp.make_config(w.tp_degree, rank, w.hidden, w.num_heads, w.head_dim, w.ffn, dt, act,
+                          w.hidden if w.has_mod else 0, w.mod_out)
 
 
 def packed_host_weights(inp: tp_inputs.Inputs) -> Dict[str, np.ndarray]:
@@ -47,6 +48,11 @@ def create_shards(w: tp_inputs.Workload, inp: tp_inputs.Inputs, ranks=None,
     hw = packed_host_weights(inp) if packed else host_weights(inp)
     ranks = range(w.tp_degree) if ranks is None else ranks
     return [tp.tp_block_shard_create(config(w, r), hw) for r in ranks]
+
+
+def f32_device(a: np.ndarray) -> torch.Tensor:
+    """An fp32 device copy of a host array (exact widening of bf16 values)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
 def rowwise_biases(w: tp_inputs.Workload, inp: tp_inputs.Inputs) -> List[torch.Tensor]:
