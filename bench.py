@@ -194,6 +194,10 @@ def main():
     if block:
         reduce_bytes = (P + 1) * T * D * 4 + len(biases) * D * 4
         kernels["partial_reduce"] = ("partial_reduce.hip", reduce_bytes, "hbm")
+    if block and bufs.splits > 1:
+        S, Hr = bufs.splits, w.num_heads // P
+        Dr = Hr * d
+        kernels["attn_merge"] = ("attn_merge.hip", S * T * (Dr + Hr) * 4 + T * Dr * 2, "hbm")
     if w.has_mod:
         kernels["mod_reduce"] = ("partial_reduce.hip",
                                  (P + 1) * w.mod_rows * w.mod_out * 4 + w.mod_out * 4, "hbm")
@@ -219,6 +223,15 @@ def main():
             b.record(stream)
             ev.setdefault(name, []).append((a, b))
 
+        def attention(s):
+            if bufs.splits > 1:
+                mark("attention", lambda: tp.tp_attn_heads_split(s, T, bufs.qkv, bufs.o_parts,
+                                                                 bufs.lse_parts))
+                mark("attn_merge", lambda: tp.tp_attn_merge(list(bufs.o_parts), list(bufs.lse_parts),
+                                                            bufs.o, s.heads_r, d))
+            else:
+                mark("attention", lambda: tp.tp_attn_heads(s, T, bufs.qkv, bufs.o))
+
         for r, s in enumerate(shards):
             if w.has_mod:
                 mark("split_input_mod", lambda: tp.tp_rowwise_split_input_partial(
@@ -228,12 +241,12 @@ def main():
             bufs.partial = partials[r]
             if w.has_attn and w.has_mlp:
                 mark("colwise_qkv_up", lambda: tp.tp_colwise_qkv_up(s, T, x, bufs.qkv, bufs.h))
-                mark("attention", lambda: tp.tp_attn_heads(s, T, bufs.qkv, bufs.o))
+                attention(s)
                 mark("rowwise_block_out", lambda: tp.tp_rowwise_linear_partial(
                     s, tp.TP_BLOCK_OUT, T, bufs.oh, bufs.partial))
             elif w.has_attn:
                 mark("colwise_qkv", lambda: tp.tp_colwise_linear(s, tp.TP_QKV, T, x, bufs.qkv))
-                mark("attention", lambda: tp.tp_attn_heads(s, T, bufs.qkv, bufs.o))
+                attention(s)
                 mark("rowwise_attn_out", lambda: tp.tp_rowwise_linear_partial(
                     s, tp.TP_ATTN_OUT, T, bufs.o, bufs.partial))
             else:

@@ -28,6 +28,9 @@
  *   - §"Limitações": unsupported combinations raise an error instead of
  *     silently doing something else.
  *
+ * Context parallelism follows the Diffusers context-parallelism page
+ * ("Paralelismo de contexto"), cited as [CP page, §section].
+ *
  * Readings where the pages are silent: attention is softmax(Q K^T/sqrt(d)) V
  * per head, non-causal, unmasked; the MLP activation is GELU (tanh form) or
  * SwiGLU silu(gate) * up with the gate as the first packed half;
@@ -206,6 +209,65 @@ TP_API tp_status tp_colwise_qkv_up(tp_block_shard *shard, int64_t tokens, const 
  * o must not overlap qkv. */
 TP_API tp_status tp_attn_heads(tp_block_shard *shard, int64_t tokens, const void *qkv, int64_t ldqkv,
                         void *o, int64_t ldo, void *stream);
+
+/* Attention of this rank's heads for the queries of one packed qkv buffer
+ * against the keys and values of another -- one step of Ring Attention
+ * [CP page, §Ring Attention: each rank attends its queries to the K/V block
+ * it holds, then passes the block on], or one key split of a long
+ * attention.  For local head j (d = 128):
+ *   s      = Q_j K_j^T / sqrt(d)  over the kv_tokens keys of the block
+ *   lse[t * ld_lse + j]  = log sum_k exp(s[t][k])            (natural log)
+ *   o[t, j*d:(j+1)*d]    = sum_k exp(s[t][k] - lse) V_j[k]   (fp32, normalised)
+ * Q_j = q_qkv[:, j*d : (j+1)*d] (only the Q columns [0, D_r) are read; ldq >=
+ * D_r); K_j, V_j = columns D_r + j*d and 2*D_r + j*d of kv_qkv (ldkv >=
+ * 3*D_r): both are packed [tokens, 3*D_r] buffers as tp_colwise_linear writes
+ * them, or row ranges of one.  o: device fp32 [q_tokens, D_r], ldo >= D_r;
+ * lse: device fp32, 4-byte aligned, ld_lse >= H/P.  q_tokens == 0 is a no-op;
+ * kv_tokens must be >= 1.  bf16 and head_dim 128 only (TP_ERR_UNSUPPORTED);
+ * o and lse must not overlap each other or the inputs.  tp_attn_merge
+ * combines the blocks. */
+TP_API tp_status tp_attn_heads_block(tp_block_shard *shard, int64_t q_tokens, const void *q_qkv,
+                                     int64_t ldq, int64_t kv_tokens, const void *kv_qkv,
+                                     int64_t ldkv, float *o, int64_t ldo, float *lse,
+                                     int64_t ld_lse, void *stream);
+
+/* tp_attn_heads with the keys cut into n_splits contiguous ranges
+ * [floor(z*T/n_splits), floor((z+1)*T/n_splits)) processed in ONE launch, so
+ * a short sequence over few heads still gives the GPU enough workgroups; each
+ * range z writes its partial result like tp_attn_heads_block:
+ *   o_parts + z * o_part_stride    fp32 [tokens, D_r], row stride ldo
+ *   lse_parts + z * lse_part_stride fp32 [tokens, H/P], row stride ld_lse
+ * (strides in elements; the parts must not overlap each other or qkv).
+ * tp_attn_merge over the n_splits parts gives tp_attn_heads' result.
+ * 1 <= n_splits <= 16 (else TP_ERR_ARG / TP_ERR_UNSUPPORTED) and
+ * n_splits <= tokens; bf16 and head_dim 128 only. */
+TP_API tp_status tp_attn_heads_split(tp_block_shard *shard, int64_t tokens, const void *qkv,
+                                     int64_t ldqkv, int32_t n_splits, float *o_parts, int64_t ldo,
+                                     int64_t o_part_stride, float *lse_parts, int64_t ld_lse,
+                                     int64_t lse_part_stride, void *stream);
+
+/* Host-only query: the n_splits (1..4) at which tp_attn_heads_split over
+ * `tokens` tokens fills the GPU with its long-sequence kernel -- 1 when
+ * tp_attn_heads already does (or the shard has no attention, or tokens < 1).
+ * A split count above 1 pays for the merge's extra pass only when this says so. */
+TP_API int32_t tp_attn_split_hint(const tp_block_shard *shard, int64_t tokens);
+
+/* Merge of partial attention results over disjoint key blocks (the
+ * combination that makes a full ring cycle equal attention over the whole
+ * sequence [CP page, §Ring Attention]), per (token t, head j):
+ *   lse = log sum_i exp(lse_i[t, j]),  o[t, j*hd + c] = sum_i exp(lse_i - lse) o_i[t, j*hd + c]
+ * o_parts / lse_parts: HOST arrays of n_parts DEVICE pointers (1 <= n_parts
+ * <= 16, else TP_ERR_ARG below / TP_ERR_UNSUPPORTED above), each o_i fp32
+ * [tokens, heads*head_dim] with row stride ldo_parts, each lse_i fp32 with row
+ * stride ld_lse_parts >= heads.  o: device, o_dtype (TP_BF16 or TP_F32),
+ * ldo >= heads*head_dim.  lse_out: device fp32 (row stride ld_lse_out >=
+ * heads) or NULL.  head_dim a positive multiple of 4.  The outputs must not
+ * overlap the inputs.  Shard-independent; tokens == 0 is a no-op. */
+TP_API tp_status tp_attn_merge(const float *const *o_parts, const float *const *lse_parts,
+                               int32_t n_parts, int64_t ldo_parts, int64_t ld_lse_parts,
+                               int64_t tokens, int64_t heads, int64_t head_dim, void *o,
+                               int64_t ldo, tp_dtype o_dtype, float *lse_out, int64_t ld_lse_out,
+                               void *stream);
 
 /* Rowwise projection, partial sum [TP page, §Colwise e rowwise]:
  *   partial[t, n] (+)= sum_k x_local[t, k] * W_r[n, k],  n < D, k < K_r   (no bias)

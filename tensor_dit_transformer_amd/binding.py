@@ -41,7 +41,8 @@ EXPORTED = (
     "tp_block_shard_create", "tp_block_shard_destroy", "tp_colwise_linear",
     "tp_colwise_qkv_up", "tp_attn_heads", "tp_rowwise_linear_partial",
     "tp_partial_reduce", "tp_status_string", "tp_last_error_detail",
-    "tp_rowwise_split_input_partial",
+    "tp_rowwise_split_input_partial", "tp_attn_heads_block", "tp_attn_merge",
+    "tp_attn_heads_split", "tp_attn_split_hint",
 )
 
 
@@ -92,11 +93,18 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.c_int, vp]
         L.tp_rowwise_split_input_partial.argtypes = [vp, ctypes.c_int, i64, vp, i64, vp, i64,
                                                      ctypes.c_int, vp]
+        L.tp_attn_heads_block.argtypes = [vp, i64, vp, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+        L.tp_attn_heads_split.argtypes = [vp, i64, vp, i64, i32, vp, i64, i64, vp, i64, i64, vp]
+        L.tp_attn_split_hint.argtypes = [vp, i64]
+        L.tp_attn_split_hint.restype = ctypes.c_int32
+        L.tp_attn_merge.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, i64, i64, i64,
+                                    i64, vp, i64, ctypes.c_int, vp, i64, vp]
         L.tp_partial_reduce.argtypes = [ctypes.POINTER(vp), i32, i64, ctypes.POINTER(vp), i32,
                                         i64, i64, vp, i64, vp]
         for f in ("tp_block_shard_create", "tp_colwise_linear", "tp_colwise_qkv_up",
                   "tp_attn_heads", "tp_rowwise_linear_partial", "tp_partial_reduce",
-                  "tp_rowwise_split_input_partial"):
+                  "tp_rowwise_split_input_partial", "tp_attn_heads_block", "tp_attn_merge",
+                  "tp_attn_heads_split"):
             getattr(L, f).restype = ctypes.c_int
         L.tp_status_string.argtypes = [ctypes.c_int]
         L.tp_status_string.restype = ctypes.c_char_p
@@ -283,6 +291,58 @@ def tp_attn_heads(shard: TpBlockShard, tokens: int, qkv, o, stream=None) -> None
     qp, ldq = _mat(qkv, "qkv", tokens, 3 * shard.d_r, shard.dtype)
     op, ldo = _mat(o, "o", tokens, shard.d_r, shard.dtype)
     _check(lib().tp_attn_heads(shard.handle, tokens, qp, ldq, op, ldo, _stream(stream)))
+
+
+def tp_attn_heads_block(shard: TpBlockShard, q_tokens: int, q_qkv, kv_tokens: int, kv_qkv, o, lse,
+                        stream=None) -> None:
+    """One key block of attention: fp32 normalised o [q_tokens, D_r] and the
+    natural log-sum-exp lse [q_tokens, H/P] (fp32)."""
+    qp, ldq = _mat(q_qkv, "q_qkv", q_tokens, shard.d_r, shard.dtype)
+    kp, ldk = _mat(kv_qkv, "kv_qkv", kv_tokens, 3 * shard.d_r, shard.dtype)
+    op, ldo = _mat(o, "o", q_tokens, shard.d_r, TP_F32)
+    lp, ldl = _mat(lse, "lse", q_tokens, shard.heads_r, TP_F32)
+    _check(lib().tp_attn_heads_block(shard.handle, q_tokens, qp, ldq, kv_tokens, kp, ldk, op, ldo,
+                                     lp, ldl, _stream(stream)))
+
+
+def tp_attn_heads_split(shard: TpBlockShard, tokens: int, qkv, o_parts, lse_parts,
+                        stream=None) -> None:
+    """Attention with the keys split len-wise into o_parts.shape[0] ranges in
+    one launch: o_parts fp32 [S, tokens, D_r], lse_parts fp32 [S, tokens, H/P]
+    (3-D device tensors; each part a 2-D row-major slice)."""
+    S = o_parts.shape[0]
+    if o_parts.dim() != 3 or lse_parts.dim() != 3 or lse_parts.shape[0] != S:
+        raise ValueError("o_parts / lse_parts must be 3-D with one part per split")
+    qp, ldq = _mat(qkv, "qkv", tokens, 3 * shard.d_r, shard.dtype)
+    op, ldo = _mat(o_parts[0], "o_parts[0]", tokens, shard.d_r, TP_F32)
+    lp, ldl = _mat(lse_parts[0], "lse_parts[0]", tokens, shard.heads_r, TP_F32)
+    _check(lib().tp_attn_heads_split(shard.handle, tokens, qp, ldq, S, op, ldo, o_parts.stride(0),
+                                     lp, ldl, lse_parts.stride(0), _stream(stream)))
+
+
+def tp_attn_split_hint(shard: TpBlockShard, tokens: int) -> int:
+    return int(lib().tp_attn_split_hint(shard.handle, tokens))
+
+
+def tp_attn_merge(o_parts: Sequence, lse_parts: Sequence, o, heads: int, head_dim: int,
+                  lse_out=None, stream=None) -> None:
+    """o = merge of the partial results (o_i fp32 [T, heads*head_dim], lse_i
+    fp32 [T, heads]); o is bf16 or fp32; lse_out optional fp32 [T, heads]."""
+    if len(o_parts) != len(lse_parts) or not o_parts:
+        raise ValueError("need as many lse parts as output parts, at least one")
+    T = o.shape[0]
+    W = heads * head_dim
+    ops = [_mat(p, "o_part", T, W, TP_F32) for p in o_parts]
+    lps = [_mat(p, "lse_part", T, heads, TP_F32) for p in lse_parts]
+    if any(ld != ops[0][1] for _, ld in ops) or any(ld != lps[0][1] for _, ld in lps):
+        raise ValueError("parts must share one row stride each")
+    od = _dtype_code(o)
+    op, ldo = _mat(o, "o", T, W, od)
+    lo, ldl = (None, 0) if lse_out is None else _mat(lse_out, "lse_out", T, heads, TP_F32)
+    OP = (ctypes.c_void_p * len(ops))(*[p for p, _ in ops])
+    LP = (ctypes.c_void_p * len(lps))(*[p for p, _ in lps])
+    _check(lib().tp_attn_merge(OP, LP, len(ops), ops[0][1], lps[0][1], T, heads, head_dim, op, ldo,
+                               od, lo, ldl, _stream(stream)))
 
 
 def tp_rowwise_linear_partial(shard: TpBlockShard, layer: int, tokens: int, x_local, partial,

@@ -33,6 +33,11 @@
 //     exp2(m_old - m_new) only when a row max outgrows the reference by 8
 //     (log2 units).  Keys past T get -inf (last tile only); query rows past T
 //     are clamped on load and not stored.
+//   * Queries and keys/values may come from different tensors and lengths
+//     (a K/V block of a longer sequence, the Ring Attention step of the
+//     Diffusers context-parallelism page): the block form stores the
+//     normalised output in fp32 and the natural log-sum-exp of the scaled
+//     scores, lse = ln 2 * (m + log2 l), for the merge.
 #include "tp_kernels.h"
 
 namespace tpk {
@@ -64,6 +69,64 @@ __device__ __forceinline__ int swz(int r) { return ((r << 1) | ((r >> 3) & 1)) &
 constexpr float kRescaleSlack = 8.0f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Operands of one launch: head j's Q, K, V at columns j*128 of q, k, v.
+// Key split z = blockIdx.z of kv_splits covers keys
+// [floor(z Tkv / kv_splits), floor((z+1) Tkv / kv_splits)) -- never empty when
+// Tkv >= kv_splits -- and writes its partial result at o + z o_split,
+// lse + z lse_split.
+struct AttnIO {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  int64_t ldq, ldkv;
+  int Tq, Tkv, kv_splits;
+  void* o;          // bf16 output, or fp32 with LSE
+  int64_t ldo, o_split;
+  float* lse;
+  int64_t ld_lse, lse_split;
+  float scale_log2;
+};
+
+// Epilogue of one wave's 32 queries (lane: query q = q0 + lane % 32, dims
+// 32 t + 8 (e / 4) + 4 half + (e % 4)): normalise by the row sum, store bf16,
+// or fp32 plus the row's log-sum-exp.
+template <bool LSE>
+__device__ __forceinline__ void store_rows(const AttnIO& a, int head, int q, int half,
+                                           const f32x16 (&acc_o)[kD / 32], float m_ref,
+                                           float l_run) {
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  if (q >= a.Tq) return;
+  if constexpr (LSE) {
+    const int z = blockIdx.z;
+    float* orow = static_cast<float*>(a.o) + z * a.o_split + (int64_t)q * a.ldo + head * kD;
+#pragma unroll
+    for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc_o[t][4 * g + e] * inv;
+        *reinterpret_cast<f32x4*>(orow + 32 * t + 8 * g + 4 * half) = v;
+      }
+    if (half == 0)
+      a.lse[z * a.lse_split + (int64_t)q * a.ld_lse + head] =
+          0.6931471805599453f * (m_ref + __log2f(l_tot));
+  } else {
+    bf16* orow = static_cast<bf16*>(a.o) + (int64_t)q * a.ldo + head * kD;
+#pragma unroll
+    for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(acc_o[t][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * half) = v;
+      }
+  }
+}
 
 // One 64-key tile for one wave.  dma(j), j = 0..7, issues this wave's share
 // of the next tile's global -> LDS loads; the calls are spread over the
@@ -177,10 +240,9 @@ __device__ __forceinline__ void attn_tile(const u32x4* __restrict__ sK, const u3
 // one wave's softmax arithmetic overlaps another's matrix instructions.  The
 // 8-wave form shares each K/V tile among 256 queries, halving the tile
 // traffic per query; it is used when the sequence gives enough workgroups.
-template <int NW>
+template <int NW, bool LSE>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
-attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict__ o,
-                   int64_t ldo, int T, int heads, float scale_log2) {
+attn_fwd_bf16_d128(AttnIO a) {
   constexpr int BQ = 32 * NW;
   constexpr int PER_WAVE = 32 / NW;     // 1 KB K/V loads per wave per tile
   __shared__ u32x4 sK[2][kBKV * kRowChunks];
@@ -190,19 +252,20 @@ attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int head = blockIdx.y;
   const int q0 = blockIdx.x * BQ + wave * 32;
-  const int Dr = heads * kD;
-  const bf16* Qg = qkv + head * kD;
-  const bf16* Kg = qkv + Dr + head * kD;
-  const bf16* Vg = qkv + 2 * Dr + head * kD;
+  const int k0 = (int)((int64_t)blockIdx.z * a.Tkv / a.kv_splits);
+  const int T = (int)((int64_t)(blockIdx.z + 1) * a.Tkv / a.kv_splits) - k0;   // >= 1
+  const bf16* Qg = a.q + head * kD;
+  const bf16* Kg = a.k + head * kD + (int64_t)k0 * a.ldkv;
+  const bf16* Vg = a.v + head * kD + (int64_t)k0 * a.ldkv;
   const int half = lane >> 5, l32 = lane & 31;
 
   // Q^T operand: lane holds query q0 + l32, dims 16 s + 8 half .. +7
   bf16x8 qf[kD / 16];
   {
-    const int64_t row = min(q0 + l32, T - 1);
+    const int64_t row = min(q0 + l32, a.Tq - 1);
 #pragma unroll
     for (int s = 0; s < kD / 16; ++s)
-      qf[s] = *reinterpret_cast<const bf16x8*>(Qg + row * ldqkv + 16 * s + 8 * half);
+      qf[s] = *reinterpret_cast<const bf16x8*>(Qg + row * a.ldq + 16 * s + 8 * half);
   }
 
   // K and V tiles go global -> LDS directly.  Load n (0..31) of a tile fills
@@ -214,7 +277,7 @@ attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict
     const int rr = 4 * blk + (lane >> 4);
     const int c = (lane & 15) ^ swz(rr);
     const int64_t row = min(kt * kBKV + rr, T - 1);
-    const bf16* src = (n < 16 ? Kg : Vg) + row * ldqkv + 8 * c;
+    const bf16* src = (n < 16 ? Kg : Vg) + row * a.ldkv + 8 * c;
     u32x4* dst = (n < 16 ? sK[buf] : sV[buf]) + 64 * blk;
     __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                      (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
@@ -245,28 +308,13 @@ attn_fwd_bf16_d128(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict
       }
     };
     if (kt < nfull)
-      attn_tile<false>(sK[buf], sV[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, scale_log2, lane, dma);
+      attn_tile<false>(sK[buf], sV[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, a.scale_log2, lane, dma);
     else
-      attn_tile<true>(sK[buf], sV[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, scale_log2, lane, dma);
+      attn_tile<true>(sK[buf], sV[buf], qf, acc_o, m_ref, l_run, kt * kBKV, T, a.scale_log2, lane, dma);
     __syncthreads();  // tile kt + 1 landed (this wave's DMA) and every wave is done with buf
   }
 
-  // normalise and store: lane holds query q0 + l32, dims 32 t + 8 (e/4) + 4 half + (e%4)
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  const int q = q0 + l32;
-  if (q < T) {
-    bf16* orow = o + (int64_t)q * ldo + head * kD;
-#pragma unroll
-    for (int t = 0; t < kD / 32; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(acc_o[t][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * half) = v;
-      }
-  }
+  store_rows<LSE>(a, head, q0 + l32, half, acc_o, m_ref, l_run);
 }
 
 // ---------------------------------------------------------------------------
@@ -289,10 +337,9 @@ __device__ __forceinline__ void barrier_keep_newest_loads() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int NQ, int NW>
+template <int NQ, int NW, bool LSE>
 __global__ void __launch_bounds__(64 * NW, 1)
-attn_fwd_pipe(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict__ o, int64_t ldo,
-              int T, int heads, float scale_log2) {
+attn_fwd_pipe(AttnIO io) {
   constexpr int NSTAGE = 4;
   constexpr int BQ = NW * 32 * NQ;
   constexpr int PER_WAVE = 32 / NW;   // 1 KB loads per wave per tile
@@ -303,19 +350,21 @@ attn_fwd_pipe(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict__ o,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int head = blockIdx.y;
   const int q0 = blockIdx.x * BQ + wave * 32 * NQ;
-  const int Dr = heads * kD;
-  const bf16* Qg = qkv + head * kD;
-  const bf16* Kg = qkv + Dr + head * kD;
-  const bf16* Vg = qkv + 2 * Dr + head * kD;
+  const int k0 = (int)((int64_t)blockIdx.z * io.Tkv / io.kv_splits);
+  const int T = (int)((int64_t)(blockIdx.z + 1) * io.Tkv / io.kv_splits) - k0;   // >= 1
+  const bf16* Qg = io.q + head * kD;
+  const bf16* Kg = io.k + head * kD + (int64_t)k0 * io.ldkv;
+  const bf16* Vg = io.v + head * kD + (int64_t)k0 * io.ldkv;
+  const float scale_log2 = io.scale_log2;
   const int half = lane >> 5, l32 = lane & 31;
 
   bf16x8 qf[NQ][kD / 16];
 #pragma unroll
   for (int a = 0; a < NQ; ++a) {
-    const int64_t row = min(q0 + 32 * a + l32, T - 1);
+    const int64_t row = min(q0 + 32 * a + l32, io.Tq - 1);
 #pragma unroll
     for (int st = 0; st < kD / 16; ++st)
-      qf[a][st] = *reinterpret_cast<const bf16x8*>(Qg + row * ldqkv + 16 * st + 8 * half);
+      qf[a][st] = *reinterpret_cast<const bf16x8*>(Qg + row * io.ldq + 16 * st + 8 * half);
   }
 
   const int nkt = (T + kBKV - 1) / kBKV;
@@ -331,7 +380,7 @@ attn_fwd_pipe(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict__ o,
       const int rr = 4 * blk + (lane >> 4);
       const int c = (lane & 15) ^ swz(rr);
       const int64_t row = min(tt * kBKV + rr, T - 1);
-      const bf16* src = (n < 16 ? Kg : Vg) + row * ldqkv + 8 * c;
+      const bf16* src = (n < 16 ? Kg : Vg) + row * io.ldkv + 8 * c;
       u32x4* dst = (n < 16 ? sK[buf] : sV[buf]) + 64 * blk;
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                        (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
@@ -478,43 +527,64 @@ attn_fwd_pipe(const bf16* __restrict__ qkv, int64_t ldqkv, bf16* __restrict__ o,
   if (kt < nkt) step(kt, sa, sb);
 
 #pragma unroll
-  for (int a = 0; a < NQ; ++a) {
-    const float l_tot = l_run[a] + __shfl_xor(l_run[a], 32);
-    const float inv = 1.0f / l_tot;
-    const int q = q0 + 32 * a + l32;
-    if (q < T) {
-      bf16* orow = o + (int64_t)q * ldo + head * kD;
-#pragma unroll
-      for (int t = 0; t < kD / 32; ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(acc_o[a][t][4 * g + e] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * half) = v;
-        }
-    }
-  }
+  for (int a = 0; a < NQ; ++a)
+    store_rows<LSE>(io, head, q0 + 32 * a + l32, half, acc_o[a], m_ref[a], l_run[a]);
 }
 
 }  // namespace
 
+namespace {
+
+// Long query sets: the software-pipelined form in 256-query workgroups (one
+// per CU), when they cover at least three quarters of the 256 CUs;
+// otherwise 128-query workgroups, two per CU.
+// The pipelined kernel needs 256-query workgroups covering three quarters of
+// the CUs.
+constexpr long kPipeMinWorkgroups = 192;
+
+long pipe_workgroups(int Tq, int heads, int splits) {
+  return (long)((Tq + 255) / 256) * heads * splits;
+}
+
+template <bool LSE>
+void launch_io(const AttnIO& io, int heads, int splits, hipStream_t stream) {
+  if (pipe_workgroups(io.Tq, heads, splits) >= kPipeMinWorkgroups) {
+    const dim3 grid((io.Tq + 255) / 256, heads, splits), block(512);
+    hipLaunchKernelGGL((attn_fwd_pipe<1, 8, LSE>), grid, block, 0, stream, io);
+  } else {
+    const dim3 grid((io.Tq + 127) / 128, heads, splits), block(256);
+    hipLaunchKernelGGL((attn_fwd_bf16_d128<4, LSE>), grid, block, 0, stream, io);
+  }
+}
+
+constexpr float kScaleLog2 = 1.4426950408889634f / 11.313708498984761f;  // log2(e) / sqrt(128)
+
+}  // namespace
+
+int attn_split_hint(int T, int heads) {
+  if (pipe_workgroups(T, heads, 1) >= kPipeMinWorkgroups) return 1;
+  for (int s = 2; s <= 4; ++s)
+    if (pipe_workgroups(T, heads, s) >= kPipeMinWorkgroups && T >= s) return s;
+  return 1;
+}
+
 hipError_t launch_attn_fwd_bf16_d128(const void* qkv, int64_t ldqkv, void* o, int64_t ldo,
                                      int T, int heads, hipStream_t stream) {
-  const float scale_log2 = 1.4426950408889634f / sqrtf((float)kD);
-  // Long sequences: the software-pipelined form in 256-query workgroups (one
-  // per CU), when they cover at least three quarters of the 256 CUs;
-  // otherwise 128-query workgroups, two per CU.
-  const long wg8 = (long)((T + 255) / 256) * heads;
-  if (wg8 >= 192) {
-    const dim3 grid((T + 255) / 256, heads), block(512);
-    hipLaunchKernelGGL((attn_fwd_pipe<1, 8>), grid, block, 0, stream, static_cast<const bf16*>(qkv),
-                       ldqkv, static_cast<bf16*>(o), ldo, T, heads, scale_log2);
-  } else {
-    const dim3 grid((T + 127) / 128, heads), block(256);
-    hipLaunchKernelGGL(attn_fwd_bf16_d128<4>, grid, block, 0, stream, static_cast<const bf16*>(qkv),
-                       ldqkv, static_cast<bf16*>(o), ldo, T, heads, scale_log2);
-  }
+  const bf16* base = static_cast<const bf16*>(qkv);
+  const int64_t Dr = (int64_t)heads * kD;
+  const AttnIO io{base, base + Dr, base + 2 * Dr, ldqkv, ldqkv, T, T, 1, o, ldo, 0, nullptr, 0, 0,
+                  kScaleLog2};
+  launch_io<false>(io, heads, 1, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_block_bf16_d128(const AttnBlockArgs& a, hipStream_t stream) {
+  const int splits = a.splits < 1 ? 1 : a.splits;
+  if (a.Tkv < splits) return hipErrorInvalidValue;   // a split would be empty
+  const AttnIO io{static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                  static_cast<const bf16*>(a.v), a.ldq, a.ldkv, a.Tq, a.Tkv, splits, a.o, a.ldo,
+                  a.o_split, a.lse, a.ld_lse, a.lse_split, kScaleLog2};
+  launch_io<true>(io, a.heads, splits, stream);
   return hipGetLastError();
 }
 

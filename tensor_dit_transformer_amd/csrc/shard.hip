@@ -372,6 +372,148 @@ TP_API tp_status tp_attn_heads(tp_block_shard* s, int64_t tokens, const void* qk
   return TP_OK;
 }
 
+TP_API tp_status tp_attn_heads_block(tp_block_shard* s, int64_t q_tokens, const void* q_qkv,
+                                     int64_t ldq, int64_t kv_tokens, const void* kv_qkv,
+                                     int64_t ldkv, float* o, int64_t ldo, float* lse,
+                                     int64_t ld_lse, void* stream) {
+  tp_status st = check_shard(s);
+  if (st != TP_OK) return st;
+  if (!s->attn) return fail(TP_ERR_ARG, "shard has no attention layers");
+  if (s->cfg.dtype != TP_BF16) return fail(TP_ERR_UNSUPPORTED, "attention is built for bf16 only");
+  if (s->d != 128) return fail(TP_ERR_UNSUPPORTED, "attention is built for head_dim 128 only");
+  if ((st = check_tokens(q_tokens)) != TP_OK) return st;
+  if ((st = check_tokens(kv_tokens)) != TP_OK) return st;
+  if (q_tokens > 0 && kv_tokens < 1) return fail(TP_ERR_ARG, "kv_tokens must be >= 1");
+  const int64_t Dr = s->Dr, Hr = s->Hr;
+  if ((st = check_matrix("q_qkv", q_qkv, ldq, Dr, s->es)) != TP_OK) return st;
+  if ((st = check_matrix("kv_qkv", kv_qkv, ldkv, 3 * Dr, s->es)) != TP_OK) return st;
+  if ((st = check_matrix("o", o, ldo, Dr, sizeof(float))) != TP_OK) return st;
+  if (!lse) return fail(TP_ERR_ARG, "lse is NULL");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(TP_ERR_ARG, "lse is not 4-byte aligned");
+  if (ld_lse < Hr) return fail(TP_ERR_ARG, "ld_lse (%lld) < local heads %lld", (long long)ld_lse,
+                               (long long)Hr);
+  if (q_tokens == 0) return TP_OK;
+  const int64_t ob = span_bytes(q_tokens, ldo, Dr, sizeof(float));
+  const int64_t lb = span_bytes(q_tokens, ld_lse, Hr, sizeof(float));
+  const int64_t qb = span_bytes(q_tokens, ldq, Dr, s->es);
+  const int64_t kb = span_bytes(kv_tokens, ldkv, 3 * Dr, s->es);
+  if (overlap(o, ob, q_qkv, qb) || overlap(o, ob, kv_qkv, kb) || overlap(lse, lb, q_qkv, qb) ||
+      overlap(lse, lb, kv_qkv, kb) || overlap(o, ob, lse, lb))
+    return fail(TP_ERR_ARG, "o / lse overlap each other or the inputs");
+  const char* kv = static_cast<const char*>(kv_qkv);
+  const tpk::AttnBlockArgs a{q_qkv, ldq, kv + Dr * s->es, kv + 2 * Dr * s->es, ldkv,
+                             (int)q_tokens, (int)kv_tokens, (int)Hr, o, ldo, lse, ld_lse, 1, 0, 0};
+  const hipError_t e = tpk::launch_attn_block_bf16_d128(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return TP_OK;
+}
+
+TP_API tp_status tp_attn_heads_split(tp_block_shard* s, int64_t tokens, const void* qkv,
+                                     int64_t ldqkv, int32_t n_splits, float* o_parts, int64_t ldo,
+                                     int64_t o_part_stride, float* lse_parts, int64_t ld_lse,
+                                     int64_t lse_part_stride, void* stream) {
+  tp_status st = check_shard(s);
+  if (st != TP_OK) return st;
+  if (!s->attn) return fail(TP_ERR_ARG, "shard has no attention layers");
+  if (s->cfg.dtype != TP_BF16) return fail(TP_ERR_UNSUPPORTED, "attention is built for bf16 only");
+  if (s->d != 128) return fail(TP_ERR_UNSUPPORTED, "attention is built for head_dim 128 only");
+  if ((st = check_tokens(tokens)) != TP_OK) return st;
+  if (n_splits < 1) return fail(TP_ERR_ARG, "n_splits (%d) < 1", n_splits);
+  if (n_splits > tpk::kMaxMergeParts)
+    return fail(TP_ERR_UNSUPPORTED, "n_splits (%d) > %d", n_splits, tpk::kMaxMergeParts);
+  const int64_t Dr = s->Dr, Hr = s->Hr;
+  if ((st = check_matrix("qkv", qkv, ldqkv, 3 * Dr, s->es)) != TP_OK) return st;
+  if ((st = check_matrix("o_parts", o_parts, ldo, Dr, sizeof(float))) != TP_OK) return st;
+  if (o_part_stride % 4) return fail(TP_ERR_ARG, "o_part_stride must keep parts 16-byte aligned");
+  if (!lse_parts || (reinterpret_cast<uintptr_t>(lse_parts) & 3u))
+    return fail(TP_ERR_ARG, "lse_parts is NULL or not 4-byte aligned");
+  if (ld_lse < Hr) return fail(TP_ERR_ARG, "ld_lse (%lld) < local heads %lld", (long long)ld_lse,
+                               (long long)Hr);
+  if (tokens == 0) return TP_OK;
+  if (tokens < n_splits) return fail(TP_ERR_ARG, "fewer tokens than key splits");
+  const int64_t ob = span_bytes(tokens, ldo, Dr, sizeof(float));
+  const int64_t lb = span_bytes(tokens, ld_lse, Hr, sizeof(float));
+  if (n_splits > 1 && (o_part_stride * (int64_t)sizeof(float) < ob ||
+                       lse_part_stride * (int64_t)sizeof(float) < lb))
+    return fail(TP_ERR_ARG, "part strides shorter than one part (parts would overlap)");
+  const int64_t o_all = (n_splits - 1) * o_part_stride * (int64_t)sizeof(float) + ob;
+  const int64_t l_all = (n_splits - 1) * lse_part_stride * (int64_t)sizeof(float) + lb;
+  const int64_t qb = span_bytes(tokens, ldqkv, 3 * Dr, s->es);
+  if (overlap(o_parts, o_all, qkv, qb) || overlap(lse_parts, l_all, qkv, qb) ||
+      overlap(o_parts, o_all, lse_parts, l_all))
+    return fail(TP_ERR_ARG, "the parts overlap each other or qkv");
+  const char* base = static_cast<const char*>(qkv);
+  const tpk::AttnBlockArgs a{qkv, ldqkv, base + Dr * s->es, base + 2 * Dr * s->es, ldqkv,
+                             (int)tokens, (int)tokens, (int)Hr, o_parts, ldo, lse_parts, ld_lse,
+                             n_splits, o_part_stride, lse_part_stride};
+  const hipError_t e = tpk::launch_attn_block_bf16_d128(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return TP_OK;
+}
+
+TP_API int32_t tp_attn_split_hint(const tp_block_shard* s, int64_t tokens) {
+  if (!s || !s->attn || tokens < 1 || tokens > INT32_MAX) return 1;
+  return tpk::attn_split_hint((int)tokens, (int)s->Hr);
+}
+
+TP_API tp_status tp_attn_merge(const float* const* o_parts, const float* const* lse_parts,
+                               int32_t n_parts, int64_t ldo_parts, int64_t ld_lse_parts,
+                               int64_t tokens, int64_t heads, int64_t head_dim, void* o,
+                               int64_t ldo, tp_dtype o_dtype, float* lse_out, int64_t ld_lse_out,
+                               void* stream) {
+  if (!o_parts || !lse_parts) return fail(TP_ERR_ARG, "o_parts or lse_parts is NULL");
+  if (n_parts < 1) return fail(TP_ERR_ARG, "n_parts (%d) < 1", n_parts);
+  if (n_parts > tpk::kMaxMergeParts)
+    return fail(TP_ERR_UNSUPPORTED, "n_parts (%d) > %d", n_parts, tpk::kMaxMergeParts);
+  if (o_dtype != TP_F32 && o_dtype != TP_BF16) return fail(TP_ERR_ARG, "unknown o_dtype");
+  tp_status st = check_tokens(tokens);
+  if (st != TP_OK) return st;
+  if (heads < 1 || head_dim < 4 || head_dim % 4)
+    return fail(TP_ERR_ARG, "heads >= 1 and head_dim a positive multiple of 4 required");
+  const int64_t W = heads * head_dim;
+  if (W > INT32_MAX) return fail(TP_ERR_UNSUPPORTED, "heads*head_dim too large");
+  if (ld_lse_parts < heads) return fail(TP_ERR_ARG, "ld_lse_parts < heads");
+  tpk::MergeArgs a{};
+  for (int i = 0; i < n_parts; ++i) {
+    if ((st = check_matrix("o_parts[i]", o_parts[i], ldo_parts, W, sizeof(float))) != TP_OK) return st;
+    if (!lse_parts[i] || (reinterpret_cast<uintptr_t>(lse_parts[i]) & 3u))
+      return fail(TP_ERR_ARG, "lse_parts[%d] is NULL or not 4-byte aligned", i);
+    a.o[i] = o_parts[i];
+    a.lse[i] = lse_parts[i];
+  }
+  const size_t oes = o_dtype == TP_BF16 ? 2 : 4;
+  if ((st = check_matrix("o", o, ldo, W, oes)) != TP_OK) return st;
+  if (lse_out) {
+    if (reinterpret_cast<uintptr_t>(lse_out) & 3u) return fail(TP_ERR_ARG, "lse_out not 4-byte aligned");
+    if (ld_lse_out < heads) return fail(TP_ERR_ARG, "ld_lse_out < heads");
+  }
+  if (tokens == 0) return TP_OK;
+  const int64_t ob = span_bytes(tokens, ldo, W, oes);
+  const int64_t lb = lse_out ? span_bytes(tokens, ld_lse_out, heads, sizeof(float)) : 0;
+  for (int i = 0; i < n_parts; ++i) {
+    const int64_t pb = span_bytes(tokens, ldo_parts, W, sizeof(float));
+    const int64_t qb = span_bytes(tokens, ld_lse_parts, heads, sizeof(float));
+    if (overlap(o, ob, o_parts[i], pb) || overlap(o, ob, lse_parts[i], qb) ||
+        (lse_out && (overlap(lse_out, lb, o_parts[i], pb) || overlap(lse_out, lb, lse_parts[i], qb))))
+      return fail(TP_ERR_ARG, "the merged output overlaps part %d", i);
+  }
+  if (lse_out && overlap(o, ob, lse_out, lb)) return fail(TP_ERR_ARG, "o overlaps lse_out");
+  a.n = n_parts;
+  a.ldo_in = ldo_parts;
+  a.ld_lse_in = ld_lse_parts;
+  a.T = (int)tokens;
+  a.heads = (int)heads;
+  a.head_dim = (int)head_dim;
+  a.out = o;
+  a.out_bf16 = o_dtype == TP_BF16;
+  a.ldo = ldo;
+  a.lse_out = lse_out;
+  a.ld_lse_out = ld_lse_out;
+  const hipError_t e = tpk::launch_attn_merge(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return TP_OK;
+}
+
 TP_API tp_status tp_rowwise_linear_partial(tp_block_shard* s, tp_layer layer, int64_t tokens,
                                            const void* x_local, int64_t ldx, float* partial,
                                            int64_t ldp, int accumulate, void* stream) {

@@ -68,6 +68,50 @@ hipError_t launch_skinny_bf16(const GemmProblem& p, float* out, int64_t ldo, boo
 hipError_t launch_attn_fwd_bf16_d128(const void* qkv, int64_t ldqkv, void* o, int64_t ldo,
                                      int T, int heads, hipStream_t stream);
 
+// Attention of Tq queries against a block of Tkv keys/values (head j at
+// columns j*128 of q, k and v, all bf16): the block's normalised output in
+// fp32, o[t, j*128 + c], and the natural log-sum-exp of its scaled scores,
+// lse[t * ld_lse + j].  With splits > 1 the keys are cut into that many
+// contiguous ranges [floor(z Tkv / splits), floor((z+1) Tkv / splits)), all
+// in one launch, range z writing at o + z o_split and lse + z lse_split
+// (Tkv < splits is hipErrorInvalidValue).
+struct AttnBlockArgs {
+  const void* q;
+  int64_t ldq;
+  const void* k;
+  const void* v;
+  int64_t ldkv;
+  int Tq, Tkv, heads;
+  float* o;
+  int64_t ldo;
+  float* lse;
+  int64_t ld_lse;
+  int splits;
+  int64_t o_split, lse_split;
+};
+hipError_t launch_attn_block_bf16_d128(const AttnBlockArgs& a, hipStream_t stream);
+// Key splits (1..4) at which one launch over T queries and `heads` heads
+// runs the pipelined kernel on enough workgroups; 1 when it already does or
+// when no split up to 4 gets there.
+int attn_split_hint(int T, int heads);
+
+// Merge of partial attention results over disjoint key blocks, per (token t,
+// head j): lse = log sum_i exp(lse_i), o = sum_i exp(lse_i - lse) o_i.
+constexpr int kMaxMergeParts = 16;
+struct MergeArgs {
+  const float* o[kMaxMergeParts];
+  const float* lse[kMaxMergeParts];
+  int n;
+  int64_t ldo_in, ld_lse_in;
+  int T, heads, head_dim;    // head_dim % 4 == 0
+  void* out;                 // bf16 or fp32 [T, heads*head_dim]
+  bool out_bf16;
+  int64_t ldo;
+  float* lse_out;            // nullable
+  int64_t ld_lse_out;
+};
+hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t stream);
+
 constexpr int kMaxReducePartials = 16;
 constexpr int kMaxReduceBiases = 4;
 

@@ -310,3 +310,35 @@ def test_modulation_create_agrees_with_oracle(L, P, mi):
 def test_split_input_rejects_null_shard(L):
     vp = ctypes.c_void_p(0x10000)
     assert L.tp_rowwise_split_input_partial(None, tp.TP_ADALN_MOD, 8, vp, 64, vp, 64, 0, None) == tp.TP_ERR_ARG
+
+
+def test_block_attention_and_merge_validation_without_device(L):
+    vp = ctypes.c_void_p(0x10000)
+    assert L.tp_attn_heads_block(None, 8, vp, 384, 8, vp, 384, vp, 128, vp, 1, None) == tp.TP_ERR_ARG
+    a, b, c, d, o = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000   # never dereferenced
+
+    def merge(o_parts=(a, b), lse_parts=(c, d), n=2, ldo_p=256, ld_l=2, T=0, heads=2, hd=128,
+              out=o, ldo=256, dt=tp.TP_BF16, lse_out=None, ld_lo=0):
+        OP = (ctypes.c_void_p * 2)(*o_parts)
+        LP = (ctypes.c_void_p * 2)(*lse_parts)
+        return L.tp_attn_merge(OP, LP, n, ldo_p, ld_l, T, heads, hd, out, ldo, dt, lse_out, ld_lo, None)
+
+    assert merge() == tp.TP_OK                                  # tokens == 0: no-op
+    assert merge(n=0) == tp.TP_ERR_ARG
+    assert merge(n=17) == tp.TP_ERR_UNSUPPORTED
+    assert merge(hd=6) == tp.TP_ERR_ARG                         # head_dim % 4
+    assert merge(heads=0) == tp.TP_ERR_ARG
+    assert merge(ld_l=1) == tp.TP_ERR_ARG                       # lse stride < heads
+    assert merge(ldo_p=255) == tp.TP_ERR_ARG                    # < width / not 16-byte rows
+    assert merge(o_parts=(a + 4, b)) == tp.TP_ERR_ARG           # misaligned
+    assert merge(lse_parts=(0, d)) == tp.TP_ERR_ARG             # NULL
+    assert merge(dt=9) == tp.TP_ERR_ARG
+    assert merge(T=-1) == tp.TP_ERR_ARG
+    assert merge(T=4, out=a) == tp.TP_ERR_ARG                   # output on top of a part
+    assert "overlap" in tp.tp_last_error_detail()
+    assert merge(T=4, lse_out=c, ld_lo=2) == tp.TP_ERR_ARG      # lse_out on top of a part
+
+
+def test_split_attention_rejects_null_shard(L):
+    vp = ctypes.c_void_p(0x10000)
+    assert L.tp_attn_heads_split(None, 8, vp, 384, 2, vp, 128, 1024, vp, 1, 8, None) == tp.TP_ERR_ARG

@@ -1,0 +1,181 @@
+"""GPU parity of context-parallel attention against the float64 oracle
+(Diffusers CP page, §Ring Attention): the block attention call (fp32
+normalised output and log-sum-exp) on both attention kernels, ragged and
+single-token blocks; the merge on seeded partials (1..16 parts, bf16 and
+fp32 output, optional lse); and Ring Attention simulated on one GPU -- every
+ring rank's steps plus the merge -- against attention over the whole
+sequence, also at the full 16384-token, 12-head rank shape on sampled rows.
+Tolerances: outputs 2e-2 of max|ref| (bf16 operands, bf16 P); log-sum-exp
+5e-3 absolute (the only rounding is the bf16 P summed in fp32, relative
+2^-9 per term, so ln of the sum moves by at most ~2e-3)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import tensor_dit_transformer_amd as tp
+import tp_harness as H
+import tp_inputs
+from tp_inputs import Workload
+
+pytestmark = pytest.mark.gpu
+LSE_ATOL = 5e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def attn_shard(heads_r, P=2):
+    """A bf16 attention-only shard with heads_r local heads of 128."""
+    H_ = heads_r * P
+    w = Workload(f"attn_H{H_}_P{P}", 8, H_ * 128, H_, 128, 0, P, "bf16")
+    inp = tp_inputs.make_inputs(w, seed=2)
+    return H.create_shards(w, inp, ranks=(0,))[0]
+
+
+def seeded_qkv(T, heads_r, seed, std=1.5):
+    v, b = tp_inputs.random_matrix((T, 3 * heads_r * 128), seed=seed, std=std)
+    return v.astype(np.float64), torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def qkv_parts(a, Dr):
+    return a[:, :Dr], a[:, Dr:2 * Dr], a[:, 2 * Dr:]
+
+
+@pytest.mark.parametrize("Tq,Tkv,heads_r", [(777, 333, 2), (1, 1, 2), (65, 4000, 3), (300, 64, 1),
+                                           (8192, 1000, 6)])
+def test_block_attention(Tq, Tkv, heads_r):
+    s = attn_shard(heads_r)
+    Dr = s.d_r
+    qv, qd = seeded_qkv(Tq, heads_r, seed=40)
+    kv, kd = seeded_qkv(Tkv, heads_r, seed=41)
+    o = torch.empty((Tq, Dr), dtype=torch.float32, device="cuda")
+    lse = torch.empty((Tq, heads_r), dtype=torch.float32, device="cuda")
+    tp.tp_attn_heads_block(s, Tq, qd, Tkv, kd, o, lse)
+    torch.cuda.synchronize()
+    q = qkv_parts(qv, Dr)[0]
+    _, k, v = qkv_parts(kv, Dr)
+    rows = tp_inputs.sample_rows(Tq, 64, seed=5) if Tq > 2048 else np.arange(Tq)
+    o_ref, l_ref = O.attention_block(q[rows], k, v, heads_r, 128)
+    e_o = H.rel_err(H.as_f64(o[rows]), o_ref)
+    e_l = float(np.max(np.abs(H.as_f64(lse[rows]) - l_ref)))
+    say(f"block Tq={Tq} Tkv={Tkv} heads={heads_r}: o {e_o:.2e}  lse abs {e_l:.2e}")
+    assert e_o <= H.TOL["bf16"] and e_l <= LSE_ATOL
+    torch.cuda.synchronize()
+    s.close()
+
+
+@pytest.mark.parametrize("n,out_dtype,with_lse", [(1, "bf16", True), (2, "f32", True),
+                                                  (5, "bf16", False), (16, "f32", True)])
+def test_merge_on_seeded_partials(n, out_dtype, with_lse):
+    T, heads, hd = 333, 3, 128
+    o_parts = [tp_inputs.random_matrix((T, heads * hd), seed=50 + i, dtype="f32")[0] for i in range(n)]
+    lse_parts = [3.0 * tp_inputs.random_matrix((T, heads), seed=80 + i, dtype="f32")[0] for i in range(n)]
+    od = [torch.from_numpy(a).cuda() for a in o_parts]
+    ld = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in lse_parts]
+    dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = torch.empty((T, heads * hd), dtype=dt, device="cuda")
+    lse_out = torch.empty((T, heads), dtype=torch.float32, device="cuda") if with_lse else None
+    tp.tp_attn_merge(od, ld, out, heads, hd, lse_out=lse_out)
+    torch.cuda.synchronize()
+    o_ref, l_ref = O.attention_merge(o_parts, lse_parts, hd)
+    if out_dtype == "bf16":
+        o_ref = O.to_bf16_rne(o_ref)
+    e = H.rel_err(H.as_f64(out), o_ref)
+    tol = 8e-3 if out_dtype == "bf16" else 1e-5
+    say(f"merge n={n} {out_dtype}: o {e:.2e}")
+    assert e <= tol
+    if with_lse:
+        assert float(np.max(np.abs(H.as_f64(lse_out) - l_ref))) <= 1e-5
+
+
+def ring_on_one_gpu(s, qkv, T, R):
+    """Every ring rank c: step t attends its query chunk to K/V chunk
+    (c - t) mod R, then merges its R partials into its output chunk."""
+    n, Dr, Hr = T // R, s.d_r, s.heads_r
+    out = torch.empty((T, Dr), dtype=torch.bfloat16, device="cuda")
+    o_parts = [torch.empty((n, Dr), dtype=torch.float32, device="cuda") for _ in range(R)]
+    l_parts = [torch.empty((n, Hr), dtype=torch.float32, device="cuda") for _ in range(R)]
+    for c in range(R):
+        for t in range(R):
+            j = (c - t) % R
+            tp.tp_attn_heads_block(s, n, qkv[c * n:(c + 1) * n], n, qkv[j * n:(j + 1) * n],
+                                   o_parts[t], l_parts[t])
+        tp.tp_attn_merge(o_parts, l_parts, out[c * n:(c + 1) * n], Hr, 128)
+    return out
+
+
+@pytest.mark.parametrize("T,heads_r,R", [(4096, 2, 4), (1200, 3, 3), (2048, 2, 1)])
+def test_ring_attention_equals_attention(T, heads_r, R):
+    s = attn_shard(heads_r)
+    qv, qd = seeded_qkv(T, heads_r, seed=60)
+    out = ring_on_one_gpu(s, qd, T, R)
+    mono = torch.empty((T, s.d_r), dtype=torch.bfloat16, device="cuda")
+    tp.tp_attn_heads(s, T, qd, mono)
+    torch.cuda.synchronize()
+    q, k, v = qkv_parts(qv, s.d_r)
+    ref = O.to_bf16_rne(O.attention_heads(q, k, v, heads_r, 128))
+    e = H.rel_err(H.as_f64(out), ref)
+    e_m = H.rel_err(H.as_f64(out), H.as_f64(mono))
+    say(f"ring T={T} heads={heads_r} R={R}: vs oracle {e:.2e}, vs one-call attention {e_m:.2e}")
+    assert e <= H.TOL["bf16"] and e_m <= H.TOL["bf16"]
+    torch.cuda.synchronize()
+    s.close()
+
+
+def test_ring_attention_full_rank_shape():
+    """16384 tokens, 12 local heads, ring of 4: sampled rows of two heads."""
+    T, heads_r, R = 16384, 12, 4
+    s = attn_shard(heads_r, P=4)
+    qv, qd = seeded_qkv(T, heads_r, seed=61)
+    out = ring_on_one_gpu(s, qd, T, R)
+    torch.cuda.synchronize()
+    rows = tp_inputs.sample_rows(T, 32, seed=7)
+    Dr = s.d_r
+    for j in (0, 11):
+        c = slice(j * 128, (j + 1) * 128)
+        ref = O.to_bf16_rne(O.attention_rows(qv[rows, c], qv[:, Dr + j * 128:Dr + (j + 1) * 128],
+                                             qv[:, 2 * Dr + j * 128:2 * Dr + (j + 1) * 128], 1, 128))
+        e = H.rel_err(H.as_f64(out[rows, c]), ref)
+        say(f"ring T=16384 R=4 head {j}: {e:.2e}")
+        assert e <= H.TOL["bf16"]
+    s.close()
+
+
+@pytest.mark.parametrize("T,heads_r,S", [(4608, 6, 2), (4608, 6, 4), (777, 2, 3), (5, 1, 5),
+                                         (1000, 3, 16), (300, 2, 1)])
+def test_single_launch_key_split_then_merge(T, heads_r, S):
+    """Key ranges [floor(zT/S), floor((z+1)T/S)) in one launch: each part
+    against the oracle's block attention over its keys, and the merge
+    against attention over all keys and the one-call attention."""
+    s = attn_shard(heads_r)
+    Dr = s.d_r
+    qv, qd = seeded_qkv(T, heads_r, seed=70)
+    op = torch.empty((S, T, Dr), dtype=torch.float32, device="cuda")
+    lp = torch.empty((S, T, heads_r), dtype=torch.float32, device="cuda")
+    tp.tp_attn_heads_split(s, T, qd, op, lp)
+    out = torch.empty((T, Dr), dtype=torch.bfloat16, device="cuda")
+    tp.tp_attn_merge(list(op), list(lp), out, heads_r, 128)
+    mono = torch.empty((T, Dr), dtype=torch.bfloat16, device="cuda")
+    tp.tp_attn_heads(s, T, qd, mono)
+    torch.cuda.synchronize()
+    q, k, v = qkv_parts(qv, Dr)
+    rows = tp_inputs.sample_rows(T, 48, seed=8)
+    for z in range(S):
+        a, b = (z * T) // S, ((z + 1) * T) // S
+        o_ref, l_ref = O.attention_block(q[rows], k[a:b], v[a:b], heads_r, 128)
+        assert H.rel_err(H.as_f64(op[z][rows]), o_ref) <= H.TOL["bf16"]
+        assert float(np.max(np.abs(H.as_f64(lp[z][rows]) - l_ref))) <= LSE_ATOL
+    ref = O.to_bf16_rne(O.attention_rows(q[rows], k, v, heads_r, 128))
+    e = H.rel_err(H.as_f64(out[rows]), ref)
+    e_m = H.rel_err(H.as_f64(out), H.as_f64(mono))
+    say(f"split T={T} heads={heads_r} S={S}: merged vs oracle {e:.2e}, vs one call {e_m:.2e}")
+    assert e <= H.TOL["bf16"] and e_m <= H.TOL["bf16"]
+    if S == 1:
+        assert torch.equal(out, mono)
+    torch.cuda.synchronize()
+    s.close()

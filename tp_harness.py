@@ -66,7 +66,8 @@ def rowwise_biases(w: tp_inputs.Workload, inp: tp_inputs.Inputs) -> List[torch.T
 
 class RankBuffers:
     """Activation buffers of one rank: qkv [T, 3Dr], oh = [o_r | h_r]
-    [T, Dr + Fr], partial fp32 [T, D]."""
+    [T, Dr + Fr], partial fp32 [T, D]; and, when the library's split hint
+    asks for key splits, their fp32 partial outputs and log-sum-exps."""
 
     def __init__(self, shard: tp.TpBlockShard, T: int, partial: torch.Tensor = None):
         dt = torch.bfloat16 if shard.dtype == tp.TP_BF16 else torch.float32
@@ -77,6 +78,21 @@ class RankBuffers:
         self.h = self.oh[:, Dr:] if Fr else None
         self.partial = partial if partial is not None else torch.empty((T, D), dtype=torch.float32,
                                                                       device="cuda")
+        self.splits = tp.tp_attn_split_hint(shard, T) if Dr and shard.dtype == tp.TP_BF16 else 1
+        if self.splits > 1:
+            self.o_parts = torch.empty((self.splits, T, Dr), dtype=torch.float32, device="cuda")
+            self.lse_parts = torch.empty((self.splits, T, shard.heads_r), dtype=torch.float32,
+                                         device="cuda")
+
+
+def attention(shard: tp.TpBlockShard, T: int, buf: RankBuffers) -> None:
+    """The rank's attention: one call, or key splits in one launch plus the
+    merge when the split hint says the single launch leaves the GPU idle."""
+    if buf.splits > 1:
+        tp.tp_attn_heads_split(shard, T, buf.qkv, buf.o_parts, buf.lse_parts)
+        tp.tp_attn_merge(list(buf.o_parts), list(buf.lse_parts), buf.o, shard.heads_r, shard.head_dim)
+    else:
+        tp.tp_attn_heads(shard, T, buf.qkv, buf.o)
 
 
 def run_rank(shard: tp.TpBlockShard, x: torch.Tensor, buf: RankBuffers, fused: bool = True) -> None:
@@ -89,11 +105,11 @@ def run_rank(shard: tp.TpBlockShard, x: torch.Tensor, buf: RankBuffers, fused: b
         else:
             tp.tp_colwise_linear(shard, tp.TP_QKV, T, x, buf.qkv)
             tp.tp_colwise_linear(shard, tp.TP_MLP_UP, T, x, buf.h)
-        tp.tp_attn_heads(shard, T, buf.qkv, buf.o)
+        attention(shard, T, buf)
         tp.tp_rowwise_linear_partial(shard, tp.TP_BLOCK_OUT, T, buf.oh, buf.partial)
     elif attn:
         tp.tp_colwise_linear(shard, tp.TP_QKV, T, x, buf.qkv)
-        tp.tp_attn_heads(shard, T, buf.qkv, buf.o)
+        attention(shard, T, buf)
         tp.tp_rowwise_linear_partial(shard, tp.TP_ATTN_OUT, T, buf.o, buf.partial)
     else:
         tp.tp_colwise_linear(shard, tp.TP_MLP_UP, T, x, buf.h)
