@@ -22,7 +22,11 @@ block on the first 12288 tokens).
 single-stream variant of the same block instead: shards created from one
 packed input projection (Q, K, V, gate, up; blocks [1, 1, 1, 3, 3]) and one
 packed output projection over [inner_dim, mlp_hidden_dim], MLP activation
-SwiGLU fused into the colwise epilogue.
+SwiGLU fused into the colwise epilogue.  Other workloads: the mid-size
+shards (4608 tokens), the AdaLN modulation projection sharded
+"rowwise_split_input" (adaln_mod_bf16_R8_D6144_N36864_P4), and
+context-parallel attention over 4 simulated GPUs at the CP page's
+benchmark size (cp_ring_bf16_T4608_H24_R4, cp_ulysses_bf16_T4608_H24_U4).
 """
 from __future__ import annotations
 
@@ -75,6 +79,22 @@ def cpu_baseline(w, tokens_sample: int = 12288):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    if w.cp:
+        T = min(1536, w.tokens)
+        qv, _ = tp_inputs.cp_qkv(w, seed=0, tokens=T)
+        HD = w.num_heads * w.head_dim
+        q, k, v = qv[:, :HD], qv[:, HD:2 * HD], qv[:, 2 * HD:]
+        t0 = time.perf_counter()
+        if w.cp == "ring":
+            O.ring_attention(q, k, v, w.num_heads, w.head_dim, w.cp_degree)
+        else:
+            O.ulysses_attention(q, k, v, w.num_heads, w.head_dim, w.cp_degree)
+        dt = time.perf_counter() - t0
+        flops = 4 * T * T * w.head_dim * w.num_heads
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": f"{w.cp} attention over {w.cp_degree} ranks of {w.name} on the first {T} "
+                          f"tokens: {flops / 1e9:.1f} GFLOP fp64 in {dt:.2f} s",
+                "seconds": round(dt, 2), "cpu_count": os.cpu_count()}
     tokens_sample = min(tokens_sample, w.tokens)
     inp = tp_inputs.make_inputs(w, seed=0, tokens=tokens_sample)
     t0 = time.perf_counter()
@@ -142,32 +162,23 @@ def step_flops(w, T):
     return f
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="block_bf16_T16384_D6144_H48_F18432_P4")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="before warmup, run a plain 512 MiB device-to-device copy twice so a "
-                         "counter run can scale FETCH_SIZE / WRITE_SIZE by a kernel of known traffic")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the shard's ranks are "
-              "simulated one after another on a single MI355X; there is no multi-GPU path.",
-              file=sys.stderr)
-        sys.exit(2)
+class Setup:
+    """What one workload's step needs: `kernels` maps a kernel name to
+    (source file, algorithmic work per launch, bound), `run(mark)` enqueues
+    one step (each launch wrapped in mark(name, fn)), `flops` is the step's
+    algorithmic FLOPs, `config` its description, `close()` frees it."""
 
+    def __init__(self, kernels, run, flops, config, close):
+        self.kernels, self.run, self.flops, self.config, self.close = kernels, run, flops, config, close
+
+
+def setup_block(w):
     import torch
     import tensor_dit_transformer_amd as tp
     import tp_harness as H
     import tp_inputs
 
-    w = tp_inputs.WORKLOADS[args.workload]
     T, D, P, d = w.tokens, w.hidden, w.tp_degree, w.head_dim
-    log(f"[bench] generating inputs for {w.name}")
-    t0 = time.time()
     inp = tp_inputs.make_inputs(w, seed=0)
     # a single-stream SwiGLU block comes as a packed checkpoint (fused input
     # and output projections)
@@ -187,9 +198,7 @@ def main():
         mod_parts = [torch.empty((w.mod_rows, w.mod_out), dtype=torch.float32, device="cuda")
                      for _ in range(P)]
         y_mod = torch.empty((w.mod_rows, w.mod_out), dtype=torch.float32, device="cuda")
-    log(f"[bench] setup {time.time() - t0:.1f} s")
 
-    # kernels of a step, with algorithmic work per launch
     kernels = step_kernels(w, T)
     if block:
         reduce_bytes = (P + 1) * T * D * 4 + len(biases) * D * 4
@@ -202,27 +211,7 @@ def main():
         kernels["mod_reduce"] = ("partial_reduce.hip",
                                  (P + 1) * w.mod_rows * w.mod_out * 4 + w.mod_out * 4, "hbm")
 
-    stream = torch.cuda.current_stream()
-    if args.copy_calibration:
-        src = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    def step(ev=None):
-        def mark(name, fn):
-            if ev is None:
-                fn()
-                return
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            ev.setdefault(name, []).append((a, b))
-
+    def run(mark):
         def attention(s):
             if bufs.splits > 1:
                 mark("attention", lambda: tp.tp_attn_heads_split(s, T, bufs.qkv, bufs.o_parts,
@@ -258,6 +247,141 @@ def main():
         if w.has_mod:
             mark("mod_reduce", lambda: tp.tp_partial_reduce(mod_parts, mod_bias, y_mod))
 
+    def close():
+        torch.cuda.synchronize()
+        for s in shards:
+            s.close()
+
+    config = {"workload": w.name, "tokens": T, "hidden": D, "num_heads": w.num_heads,
+              "head_dim": d, "ffn": w.ffn, "tp_degree": P, "ranks_per_step": P,
+              "mlp_act": w.mlp_act, "packed_checkpoint": packed, "step": step_text(w)}
+    return Setup(kernels, run, step_flops(w, T) * P, config, close)
+
+
+def setup_cp(w):
+    """Context-parallel attention of all heads over cp_degree simulated GPUs:
+    Ring (every rank's steps over the K/V chunks it is passed, then the merge)
+    or Ulysses (first all-to-all, each rank's attention over its heads, second
+    all-to-all)."""
+    import numpy as np
+    import torch
+    import tensor_dit_transformer_amd as tp
+    import tp_harness as H
+    import tp_inputs
+
+    T, Hh, d, R = w.tokens, w.num_heads, w.head_dim, w.cp_degree
+    HD, n = Hh * d, w.tokens // w.cp_degree
+    _, bits = tp_inputs.cp_qkv(w, seed=0)
+    qkv = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    # an attention-capable shard handle with the heads one rank attends to
+    P = 1 if w.cp == "ring" else R
+    hw = tp_inputs.Workload("cp_heads", 8, HD, Hh, d, 0, P, "bf16")
+    shard = H.create_shards(hw, tp_inputs.make_inputs(hw, seed=0), ranks=(0,))[0]
+    kernels = {}
+    if w.cp == "ring":
+        o_parts = [torch.empty((n, HD), dtype=torch.float32, device="cuda") for _ in range(R)]
+        l_parts = [torch.empty((n, Hh), dtype=torch.float32, device="cuda") for _ in range(R)]
+        out = torch.empty((T, HD), dtype=torch.bfloat16, device="cuda")
+        kernels["attention_block"] = ("attn_fwd.hip", 4 * n * n * d * Hh, "mfma")
+        kernels["attn_merge"] = ("attn_merge.hip", R * n * (HD + Hh) * 4 + n * HD * 2, "hbm")
+
+        def run(mark):
+            for c in range(R):
+                for t in range(R):
+                    j = (c - t) % R
+                    mark("attention_block", lambda: tp.tp_attn_heads_block(
+                        shard, n, qkv[c * n:(c + 1) * n], n, qkv[j * n:(j + 1) * n], o_parts[t],
+                        l_parts[t]))
+                mark("attn_merge", lambda: tp.tp_attn_merge(o_parts, l_parts, out[c * n:(c + 1) * n],
+                                                            Hh, d))
+    else:
+        W = HD // R
+        chunks = [qkv[s * n:(s + 1) * n] for s in range(R)]
+        hv = torch.empty((T, 3 * W), dtype=torch.bfloat16, device="cuda")
+        o_heads = [torch.empty((T, W), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        back = [torch.empty((n, HD), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        splits = tp.tp_attn_split_hint(shard, T)
+        if splits > 1:
+            op = torch.empty((splits, T, W), dtype=torch.float32, device="cuda")
+            lp = torch.empty((splits, T, Hh // R), dtype=torch.float32, device="cuda")
+            kernels["attn_merge"] = ("attn_merge.hip", splits * T * (W + Hh // R) * 4 + T * W * 2, "hbm")
+        kernels["ulysses_seq_to_heads"] = ("relayout.hip", 2 * T * 3 * W * 2, "hbm")
+        kernels["attention"] = ("attn_fwd.hip", 4 * T * T * d * (Hh // R), "mfma")
+        kernels["ulysses_heads_to_seq"] = ("relayout.hip", 2 * n * HD * 2, "hbm")
+
+        def run(mark):
+            for r in range(R):
+                mark("ulysses_seq_to_heads", lambda: tp.tp_ulysses_seq_to_heads(chunks, Hh, d, 3, r, hv))
+                if splits > 1:
+                    mark("attention", lambda: tp.tp_attn_heads_split(shard, T, hv, op, lp))
+                    mark("attn_merge", lambda: tp.tp_attn_merge(list(op), list(lp), o_heads[r],
+                                                                Hh // R, d))
+                else:
+                    mark("attention", lambda: tp.tp_attn_heads(shard, T, hv, o_heads[r]))
+            for s in range(R):
+                mark("ulysses_heads_to_seq", lambda: tp.tp_ulysses_heads_to_seq(o_heads, Hh, d, s,
+                                                                                back[s]))
+
+    def close():
+        torch.cuda.synchronize()
+        shard.close()
+
+    config = {"workload": w.name, "tokens": T, "num_heads": Hh, "head_dim": d, "cp": w.cp,
+              "cp_degree": R, "ranks_per_step": R,
+              "step": f"{w.cp} attention of all {Hh} heads over {R} simulated GPUs"}
+    return Setup(kernels, run, 4 * T * T * d * Hh, config, close)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="block_bf16_T16384_D6144_H48_F18432_P4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before warmup, run a plain 512 MiB device-to-device copy twice so a "
+                         "counter run can scale FETCH_SIZE / WRITE_SIZE by a kernel of known traffic")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the shard's ranks are "
+              "simulated one after another on a single MI355X; there is no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tp_inputs
+
+    w = tp_inputs.WORKLOADS[args.workload]
+    log(f"[bench] generating inputs for {w.name}")
+    t0 = time.time()
+    st = setup_cp(w) if w.cp else setup_block(w)
+    kernels = st.kernels
+    log(f"[bench] setup {time.time() - t0:.1f} s")
+
+    stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step(ev=None):
+        def mark(name, fn):
+            if ev is None:
+                fn()
+                return
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev.setdefault(name, []).append((a, b))
+
+        st.run(mark)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -278,7 +402,7 @@ def main():
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
-    value = step_flops(w, T) * P / (ms_per_step * 1e-3) / 1e12
+    value = st.flops / (ms_per_step * 1e-3) / 1e12
 
     per_kernel = {}
     for name, (src, work, bound) in kernels.items():
@@ -309,9 +433,7 @@ def main():
     roof["kernel"] = dom
     roof["traffic"] = load_traffic(dom, src)
 
-    torch.cuda.synchronize()
-    for s in shards:
-        s.close()
+    st.close()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -333,10 +455,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) activations, N(0,0.02) weights, N(0,0.01) biases, bf16 RNE",
         "mfma_peak_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
-        "config": {"workload": w.name, "tokens": T, "hidden": D, "num_heads": w.num_heads,
-                   "head_dim": d, "ffn": w.ffn, "tp_degree": P, "ranks_per_step": P,
-                   "mlp_act": w.mlp_act, "packed_checkpoint": packed,
-                   "step": step_text(w)},
+        "config": st.config,
         "roofline": roof,
         "kernels": per_kernel,
         "cpu_baseline": cpu,

@@ -299,6 +299,37 @@ TP_API tp_status tp_rowwise_split_input_partial(tp_block_shard *shard, tp_layer 
                                                 const void *x_full, int64_t ldx, float *partial,
                                                 int64_t ldp, int accumulate, void *stream);
 
+/* The two all-to-alls of Ulysses Attention [CP page, §Ulysses Attention],
+ * simulated with all `degree` (= u) ranks' buffers on one device.  H heads of
+ * head_dim d, W = (H / u) * d; rank r owns heads [r*H/u, (r+1)*H/u) after the
+ * first all-to-all and tokens [r*n, (r+1)*n) before it (n = tokens_per_rank).
+ *
+ * tp_ulysses_seq_to_heads -- rank `rank`'s view after the first all-to-all:
+ *   out[s*n + t, b*W + c] = chunks[s][t, b*H*d + rank*W + c]
+ * for every source rank s < u, column block b < blocks (1: one tensor [n, H*d];
+ * 3: a packed Q | K | V [n, 3*H*d], giving a packed [u*n, 3*W] buffer that
+ * tp_attn_heads reads directly), t < n, c < W.  chunks: HOST array of u
+ * DEVICE pointers, row stride ld_in >= blocks*H*d; out: device, ldo >= blocks*W.
+ *
+ * tp_ulysses_heads_to_seq -- rank `rank`'s view after the second all-to-all:
+ *   out[t, r*W + c] = parts[r][rank*n + t, c]
+ * parts: HOST array of u DEVICE pointers to [u*n, W] (ld_in >= W); out:
+ * device [n, H*d], ldo >= H*d.
+ *
+ * Both: element type dtype; 1 <= degree <= 16 (TP_ERR_ARG / TP_ERR_UNSUPPORTED);
+ * u must divide H (TP_ERR_DIVISIBILITY; the sequence divides by construction,
+ * u*n tokens); W*element size a multiple of 16 bytes (TP_ERR_UNSUPPORTED);
+ * pointers and rows 16-byte aligned; out must not overlap the inputs.  Exact
+ * copies; tokens_per_rank == 0 is a no-op. */
+TP_API tp_status tp_ulysses_seq_to_heads(const void *const *chunks, int32_t degree, int64_t ld_in,
+                                         int64_t tokens_per_rank, int64_t heads, int64_t head_dim,
+                                         int32_t blocks, int32_t rank, tp_dtype dtype, void *out,
+                                         int64_t ldo, void *stream);
+TP_API tp_status tp_ulysses_heads_to_seq(const void *const *parts, int32_t degree, int64_t ld_in,
+                                         int64_t tokens_per_rank, int64_t heads, int64_t head_dim,
+                                         int32_t rank, tp_dtype dtype, void *out, int64_t ldo,
+                                         void *stream);
+
 /* The layer-boundary AllReduce of the TP page's intro, on one GPU: all
  * simulated ranks' partials summed in rank order, then the rowwise biases:
  *   out[t, c] = ((partials[0][t, c] + partials[1][t, c]) + ...) + biases[0][c] + ...

@@ -15,4 +15,5 @@ from .binding import (  # noqa: F401
     tp_block_shard_create, tp_block_shard_destroy, tp_colwise_linear,
     tp_colwise_qkv_up, tp_last_error_detail, tp_partial_reduce,
     tp_rowwise_linear_partial, tp_rowwise_split_input_partial, tp_status_string,
+    tp_ulysses_heads_to_seq, tp_ulysses_seq_to_heads,
 )

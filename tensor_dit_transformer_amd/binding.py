@@ -42,7 +42,8 @@ EXPORTED = (
     "tp_colwise_qkv_up", "tp_attn_heads", "tp_rowwise_linear_partial",
     "tp_partial_reduce", "tp_status_string", "tp_last_error_detail",
     "tp_rowwise_split_input_partial", "tp_attn_heads_block", "tp_attn_merge",
-    "tp_attn_heads_split", "tp_attn_split_hint",
+    "tp_attn_heads_split", "tp_attn_split_hint", "tp_ulysses_seq_to_heads",
+    "tp_ulysses_heads_to_seq",
 )
 
 
@@ -95,6 +96,10 @@ def lib() -> ctypes.CDLL:
                                                      ctypes.c_int, vp]
         L.tp_attn_heads_block.argtypes = [vp, i64, vp, i64, i64, vp, i64, vp, i64, vp, i64, vp]
         L.tp_attn_heads_split.argtypes = [vp, i64, vp, i64, i32, vp, i64, i64, vp, i64, i64, vp]
+        L.tp_ulysses_seq_to_heads.argtypes = [ctypes.POINTER(vp), i32, i64, i64, i64, i64, i32, i32,
+                                              ctypes.c_int, vp, i64, vp]
+        L.tp_ulysses_heads_to_seq.argtypes = [ctypes.POINTER(vp), i32, i64, i64, i64, i64, i32,
+                                              ctypes.c_int, vp, i64, vp]
         L.tp_attn_split_hint.argtypes = [vp, i64]
         L.tp_attn_split_hint.restype = ctypes.c_int32
         L.tp_attn_merge.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, i64, i64, i64,
@@ -104,7 +109,7 @@ def lib() -> ctypes.CDLL:
         for f in ("tp_block_shard_create", "tp_colwise_linear", "tp_colwise_qkv_up",
                   "tp_attn_heads", "tp_rowwise_linear_partial", "tp_partial_reduce",
                   "tp_rowwise_split_input_partial", "tp_attn_heads_block", "tp_attn_merge",
-                  "tp_attn_heads_split"):
+                  "tp_attn_heads_split", "tp_ulysses_seq_to_heads", "tp_ulysses_heads_to_seq"):
             getattr(L, f).restype = ctypes.c_int
         L.tp_status_string.argtypes = [ctypes.c_int]
         L.tp_status_string.restype = ctypes.c_char_p
@@ -322,6 +327,42 @@ def tp_attn_heads_split(shard: TpBlockShard, tokens: int, qkv, o_parts, lse_part
 
 def tp_attn_split_hint(shard: TpBlockShard, tokens: int) -> int:
     return int(lib().tp_attn_split_hint(shard.handle, tokens))
+
+
+def _same_ld(mats, name):
+    lds = {ld for _, ld in mats}
+    if len(lds) != 1:
+        raise ValueError(f"{name} must share one row stride")
+    return mats[0][1]
+
+
+def tp_ulysses_seq_to_heads(chunks: Sequence, heads: int, head_dim: int, blocks: int, rank: int,
+                            out, stream=None) -> None:
+    """Rank `rank`'s buffer after Ulysses' first all-to-all, from every rank's
+    token chunk ([n, blocks*H*d] each) into out [u*n, blocks*W]."""
+    u, n = len(chunks), chunks[0].shape[0]
+    dt = _dtype_code(out)
+    mats = [_mat(c, "chunk", n, blocks * heads * head_dim, dt) for c in chunks]
+    ld = _same_ld(mats, "chunks")
+    op, ldo = _mat(out, "out", u * n, blocks * heads // u * head_dim, dt)
+    C = (ctypes.c_void_p * u)(*[p for p, _ in mats])
+    _check(lib().tp_ulysses_seq_to_heads(C, u, ld, n, heads, head_dim, blocks, rank, dt, op, ldo,
+                                         _stream(stream)))
+
+
+def tp_ulysses_heads_to_seq(parts: Sequence, heads: int, head_dim: int, rank: int, out,
+                            stream=None) -> None:
+    """Rank `rank`'s token chunk after Ulysses' second all-to-all, from every
+    rank's head-block output ([u*n, W] each) into out [n, H*d]."""
+    u = len(parts)
+    n = parts[0].shape[0] // u
+    dt = _dtype_code(out)
+    mats = [_mat(p, "part", u * n, heads // u * head_dim, dt) for p in parts]
+    ld = _same_ld(mats, "parts")
+    op, ldo = _mat(out, "out", n, heads * head_dim, dt)
+    Pp = (ctypes.c_void_p * u)(*[p for p, _ in mats])
+    _check(lib().tp_ulysses_heads_to_seq(Pp, u, ld, n, heads, head_dim, rank, dt, op, ldo,
+                                         _stream(stream)))
 
 
 def tp_attn_merge(o_parts: Sequence, lse_parts: Sequence, o, heads: int, head_dim: int,

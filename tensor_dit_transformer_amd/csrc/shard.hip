@@ -600,6 +600,105 @@ TP_API tp_status tp_rowwise_split_input_partial(tp_block_shard* s, tp_layer laye
   return TP_OK;
 }
 
+namespace {
+
+constexpr int kMaxUlysses = 16;
+
+// Shared checks of the two Ulysses re-layouts: degree, heads, dtype and the
+// 16-byte granularity of one head block W = (heads / degree) * head_dim.
+tp_status check_ulysses(int32_t degree, int32_t rank, int64_t n, int64_t heads, int64_t head_dim,
+                        tp_dtype dt, size_t* es, int64_t* W) {
+  if (degree < 1 || degree > kMaxUlysses)
+    return fail(degree < 1 ? TP_ERR_ARG : TP_ERR_UNSUPPORTED, "degree %d not in [1, %d]", degree,
+                kMaxUlysses);
+  if (rank < 0 || rank >= degree) return fail(TP_ERR_ARG, "rank %d not in [0, %d)", rank, degree);
+  if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_ARG, "unknown dtype");
+  tp_status st = check_tokens(n);
+  if (st != TP_OK) return st;
+  if (n * degree > INT32_MAX) return fail(TP_ERR_UNSUPPORTED, "sequence longer than 2^31-1");
+  if (heads < 1 || head_dim < 1) return fail(TP_ERR_ARG, "heads and head_dim must be positive");
+  if (heads % degree)
+    return fail(TP_ERR_DIVISIBILITY, "ulysses degree %d does not divide %lld heads", degree,
+                (long long)heads);
+  *es = dt == TP_BF16 ? 2 : 4;
+  *W = heads / degree * head_dim;
+  if ((*W * (int64_t)*es) % 16)
+    return fail(TP_ERR_UNSUPPORTED, "a head block must be a multiple of 16 bytes");
+  return TP_OK;
+}
+
+tp_status copy(const tpk::CopyBlocksArgs& a, hipStream_t stream) {
+  const hipError_t e = tpk::launch_copy_blocks(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "re-layout launch");
+  return TP_OK;
+}
+
+}  // namespace
+
+TP_API tp_status tp_ulysses_seq_to_heads(const void* const* chunks, int32_t degree, int64_t ld_in,
+                                         int64_t tokens_per_rank, int64_t heads, int64_t head_dim,
+                                         int32_t blocks, int32_t rank, tp_dtype dtype, void* out,
+                                         int64_t ldo, void* stream) {
+  size_t es;
+  int64_t W;
+  tp_status st = check_ulysses(degree, rank, tokens_per_rank, heads, head_dim, dtype, &es, &W);
+  if (st != TP_OK) return st;
+  if (!chunks) return fail(TP_ERR_ARG, "chunks is NULL");
+  if (blocks < 1 || blocks > 3) return fail(TP_ERR_ARG, "blocks (%d) not in [1, 3]", blocks);
+  const int64_t HD = heads * head_dim, n = tokens_per_rank;
+  for (int i = 0; i < degree; ++i)
+    if ((st = check_matrix("chunks[i]", chunks[i], ld_in, blocks * HD, es)) != TP_OK) return st;
+  if ((st = check_matrix("out", out, ldo, blocks * W, es)) != TP_OK) return st;
+  if (n == 0) return TP_OK;
+  const int64_t ob = span_bytes(n * degree, ldo, blocks * W, es);
+  for (int i = 0; i < degree; ++i)
+    if (overlap(out, ob, chunks[i], span_bytes(n, ld_in, blocks * HD, es)))
+      return fail(TP_ERR_ARG, "out overlaps chunks[%d]", i);
+  tpk::CopyBlocksArgs a{};
+  a.rows = (int)n;
+  a.chunks = (int)(W * (int64_t)es / 16);
+  a.src_ld = ld_in * (int64_t)es;
+  a.dst_ld = ldo * (int64_t)es;
+  for (int sr = 0; sr < degree; ++sr)
+    for (int b = 0; b < blocks; ++b) {
+      a.src[a.n] = static_cast<const char*>(chunks[sr]) + (b * HD + rank * W) * (int64_t)es;
+      a.dst[a.n] = static_cast<char*>(out) + (sr * n * ldo + b * W) * (int64_t)es;
+      ++a.n;
+    }
+  return copy(a, static_cast<hipStream_t>(stream));
+}
+
+TP_API tp_status tp_ulysses_heads_to_seq(const void* const* parts, int32_t degree, int64_t ld_in,
+                                         int64_t tokens_per_rank, int64_t heads, int64_t head_dim,
+                                         int32_t rank, tp_dtype dtype, void* out, int64_t ldo,
+                                         void* stream) {
+  size_t es;
+  int64_t W;
+  tp_status st = check_ulysses(degree, rank, tokens_per_rank, heads, head_dim, dtype, &es, &W);
+  if (st != TP_OK) return st;
+  if (!parts) return fail(TP_ERR_ARG, "parts is NULL");
+  const int64_t n = tokens_per_rank;
+  for (int i = 0; i < degree; ++i)
+    if ((st = check_matrix("parts[i]", parts[i], ld_in, W, es)) != TP_OK) return st;
+  if ((st = check_matrix("out", out, ldo, heads * head_dim, es)) != TP_OK) return st;
+  if (n == 0) return TP_OK;
+  const int64_t ob = span_bytes(n, ldo, heads * head_dim, es);
+  for (int i = 0; i < degree; ++i)
+    if (overlap(out, ob, parts[i], span_bytes(n * degree, ld_in, W, es)))
+      return fail(TP_ERR_ARG, "out overlaps parts[%d]", i);
+  tpk::CopyBlocksArgs a{};
+  a.rows = (int)n;
+  a.chunks = (int)(W * (int64_t)es / 16);
+  a.src_ld = ld_in * (int64_t)es;
+  a.dst_ld = ldo * (int64_t)es;
+  for (int r = 0; r < degree; ++r) {
+    a.src[a.n] = static_cast<const char*>(parts[r]) + rank * n * ld_in * (int64_t)es;
+    a.dst[a.n] = static_cast<char*>(out) + r * W * (int64_t)es;
+    ++a.n;
+  }
+  return copy(a, static_cast<hipStream_t>(stream));
+}
+
 TP_API tp_status tp_partial_reduce(const float* const* partials, int32_t n_partials, int64_t ldp,
                                    const float* const* biases, int32_t n_biases, int64_t tokens,
                                    int64_t hidden, float* out, int64_t ldo, void* stream) {

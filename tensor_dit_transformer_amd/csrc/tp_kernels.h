@@ -112,6 +112,19 @@ struct MergeArgs {
 };
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t stream);
 
+// Up to kMaxCopies equal-shaped 2-D block copies in one launch: block c
+// copies `rows` rows of `chunks` 16-byte chunks from src[c] (row stride
+// src_ld bytes) to dst[c] (row stride dst_ld bytes).  All 16-byte aligned.
+constexpr int kMaxCopies = 48;
+struct CopyBlocksArgs {
+  const char* src[kMaxCopies];
+  char* dst[kMaxCopies];
+  int n;
+  int rows, chunks;
+  int64_t src_ld, dst_ld;
+};
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
+
 constexpr int kMaxReducePartials = 16;
 constexpr int kMaxReduceBiases = 4;
 

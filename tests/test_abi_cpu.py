@@ -342,3 +342,25 @@ def test_block_attention_and_merge_validation_without_device(L):
 def test_split_attention_rejects_null_shard(L):
     vp = ctypes.c_void_p(0x10000)
     assert L.tp_attn_heads_split(None, 8, vp, 384, 2, vp, 128, 1024, vp, 1, 8, None) == tp.TP_ERR_ARG
+
+
+def test_ulysses_validation_without_device(L):
+    a, b, o = 0x100000, 0x200000, 0x900000     # never dereferenced
+    C = (ctypes.c_void_p * 2)(a, b)
+
+    def s2h(degree=2, ld=3 * 4 * 128, n=0, heads=4, hd=128, blocks=3, rank=0, dt=tp.TP_BF16, out=o,
+            ldo=3 * 2 * 128):
+        return L.tp_ulysses_seq_to_heads(C, degree, ld, n, heads, hd, blocks, rank, dt, out, ldo, None)
+
+    assert s2h() == tp.TP_OK                            # no tokens: no-op
+    assert s2h(heads=3) == tp.TP_ERR_DIVISIBILITY       # degree does not divide the heads
+    assert s2h(degree=0) == tp.TP_ERR_ARG
+    assert s2h(degree=17) == tp.TP_ERR_UNSUPPORTED
+    assert s2h(rank=2) == tp.TP_ERR_ARG
+    assert s2h(blocks=4) == tp.TP_ERR_ARG
+    assert s2h(hd=2) == tp.TP_ERR_UNSUPPORTED           # head block 2 heads x 2 bf16 = 8 bytes
+    assert s2h(ldo=100) == tp.TP_ERR_ARG
+    assert s2h(n=4, out=a) == tp.TP_ERR_ARG             # output on top of a chunk
+    Pp = (ctypes.c_void_p * 2)(a, b)
+    assert L.tp_ulysses_heads_to_seq(Pp, 2, 256, 0, 4, 128, 0, tp.TP_BF16, o, 512, None) == tp.TP_OK
+    assert L.tp_ulysses_heads_to_seq(Pp, 2, 256, 0, 5, 128, 0, tp.TP_BF16, o, 640, None) == tp.TP_ERR_DIVISIBILITY

@@ -179,3 +179,73 @@ def test_single_launch_key_split_then_merge(T, heads_r, S):
         assert torch.equal(out, mono)
     torch.cuda.synchronize()
     s.close()
+
+
+def _dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("u,heads,blocks,n", [(2, 4, 3, 100), (4, 8, 1, 33), (3, 6, 3, 64), (1, 2, 3, 5)])
+def test_ulysses_relayouts_are_exact(u, heads, blocks, n):
+    """Both all-to-alls against the oracle's placements, bit for bit."""
+    d = 128
+    chunks_v, chunks_d = [], []
+    for s in range(u):
+        v, b = tp_inputs.random_matrix((n, blocks * heads * d), seed=90 + s)
+        chunks_v.append(v)
+        chunks_d.append(_dev_bf16(b))
+    W = heads // u * d
+    outs = []
+    for r in range(u):
+        out = torch.empty((u * n, blocks * W), dtype=torch.bfloat16, device="cuda")
+        tp.tp_ulysses_seq_to_heads(chunks_d, heads, d, blocks, r, out)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for b in range(blocks):
+        ref = O.ulysses_seq_to_heads([c[:, b * heads * d:(b + 1) * heads * d] for c in chunks_v], heads, d)
+        for r in range(u):
+            assert np.array_equal(H.as_f64(outs[r][:, b * W:(b + 1) * W]), ref[r])
+    # back: the Q block of every rank's head view returns to the token chunks
+    parts = [o[:, :W].contiguous() for o in outs]
+    ref_back = O.ulysses_heads_to_seq([H.as_f64(p) for p in parts], heads, d)
+    for s in range(u):
+        back = torch.empty((n, heads * d), dtype=torch.bfloat16, device="cuda")
+        tp.tp_ulysses_heads_to_seq(parts, heads, d, s, back)
+        torch.cuda.synchronize()
+        assert np.array_equal(H.as_f64(back), ref_back[s])
+        assert np.array_equal(H.as_f64(back), chunks_v[s][:, :heads * d])
+
+
+@pytest.mark.parametrize("u,T,heads", [(2, 1024, 4), (4, 4096, 8)])
+def test_ulysses_attention_equals_attention(u, T, heads):
+    """Token-chunked packed qkv -> first all-to-all -> each rank's attention
+    over its H/u heads (tp_attn_heads on the re-laid-out packed buffer) ->
+    second all-to-all, against attention over all heads."""
+    d, n = 128, T // u
+    qv, qb = tp_inputs.random_matrix((T, 3 * heads * d), seed=95, std=1.5)
+    chunks = [_dev_bf16(qb[s * n:(s + 1) * n]) for s in range(u)]
+    s_ = attn_shard(heads // u, P=u)
+    W = heads // u * d
+    o_heads = []
+    for r in range(u):
+        hv = torch.empty((T, 3 * W), dtype=torch.bfloat16, device="cuda")
+        tp.tp_ulysses_seq_to_heads(chunks, heads, d, 3, r, hv)
+        o = torch.empty((T, W), dtype=torch.bfloat16, device="cuda")
+        tp.tp_attn_heads(s_, T, hv, o)
+        o_heads.append(o)
+    outs = []
+    for s in range(u):
+        back = torch.empty((n, heads * d), dtype=torch.bfloat16, device="cuda")
+        tp.tp_ulysses_heads_to_seq(o_heads, heads, d, s, back)
+        outs.append(back)
+    torch.cuda.synchronize()
+    q64 = qv.astype(np.float64)
+    HD = heads * d
+    rows = tp_inputs.sample_rows(T, 48, seed=9)
+    ref = O.to_bf16_rne(O.attention_rows(q64[rows, :HD], q64[:, HD:2 * HD], q64[:, 2 * HD:], heads, d))
+    got = torch.cat(outs)[rows]
+    e = H.rel_err(H.as_f64(got), ref)
+    say(f"ulysses u={u} T={T} heads={heads}: {e:.2e}")
+    assert e <= H.TOL["bf16"]
+    torch.cuda.synchronize()
+    s_.close()

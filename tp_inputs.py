@@ -57,6 +57,8 @@ class Workload:
     mlp_act: str = "gelu_tanh"   # or "swiglu" (packed gate/up, blocks [1, 1])
     mod_rows: int = 0            # rows R of the replicated modulation input
     mod_out: int = 0             # N_mod, output features of the modulation projection
+    cp: str = ""                 # context-parallel attention only: "ring" or "ulysses"
+    cp_degree: int = 0
 
     @property
     def has_attn(self) -> bool:
@@ -105,7 +107,23 @@ C8 = Workload("adaln_mod_bf16_R8_D6144_N36864_P4", 0, 6144, 0, 0, 0, 4, "bf16",
               "bf16 AdaLN modulation projection, all 4 rank shards then partial reduce",
               mod_rows=8, mod_out=36864)
 
-WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5_P4, C5_P2, C6, C7, C8)}
+# Context-parallel attention of the CP page's benchmark model size (a
+# 1024x1024 FLUX.1-like image: 4096 latents + 512 text tokens, 24 heads of
+# 128) across 4 simulated GPUs; the attention input is a seeded packed qkv
+# (std 1.5, like the projections' output), drawn by cp_qkv.
+C9 = Workload("cp_ring_bf16_T4608_H24_R4", 4608, 3072, 24, 128, 0, 1, "bf16",
+              "Ring Attention over 4 simulated GPUs", cp="ring", cp_degree=4)
+C10 = Workload("cp_ulysses_bf16_T4608_H24_U4", 4608, 3072, 24, 128, 0, 1, "bf16",
+               "Ulysses Attention over 4 simulated GPUs", cp="ulysses", cp_degree=4)
+
+WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5_P4, C5_P2, C6, C7, C8, C9, C10)}
+
+
+def cp_qkv(w: Workload, seed: int = 0, tokens: Optional[int] = None):
+    """The packed [T, 3 H d] attention input of a context-parallel workload
+    (values, bits)."""
+    T = w.tokens if tokens is None else tokens
+    return random_matrix((T, 3 * w.num_heads * w.head_dim), seed=seed, std=1.5)
 
 
 def _shapes(w: Workload) -> Dict[str, tuple]:
