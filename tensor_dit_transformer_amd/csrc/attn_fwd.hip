@@ -56,11 +56,14 @@ constexpr int kD = 128;            // head dim
 constexpr int kBKV = 64;           // keys per tile
 constexpr int kRowChunks = kD / 8; // 16-byte chunks per K or V row (256 bytes)
 
-// LDS position of 16-byte chunk c of K/V tile row r: c ^ f(r), with f a
-// bijection on 16 consecutive rows (conflict-free K reads: 16 rows, one
-// chunk) that also gives 4 aligned rows distinct values of one parity
-// (conflict-free transposed V reads: 4 rows, two adjacent chunks).
-__device__ __forceinline__ int swz(int r) { return ((r << 1) | ((r >> 3) & 1)) & 15; }
+// LDS position of 16-byte chunk c of K/V tile row r: c ^ f(r), rows being
+// 256 bytes (all 64 banks), so a chunk's banks depend on its position only.
+// f is a bijection on 16 consecutive rows (conflict-free K reads: 16 lanes
+// read one chunk of 16 rows) with f(4 a + b) = 4 b + a: a transposed V read
+// serves 32 lanes at once, two 16-lane groups each reading 4 aligned rows at
+// chunks {2 j, 2 j + 1} and {2 j + 2, 2 j + 3}; XOR with {0, 4, 8, 12} (+ a
+// constant) sends the two groups to disjoint halves of the banks.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // Slack (log2 domain) the running max may trail the true row max before the
 // accumulator is rescaled.  Softmax is invariant to the reference value, so
