@@ -77,7 +77,8 @@ typedef enum tp_status {
                                 or num_heads*head_dim != hidden */
   TP_ERR_UNSUPPORTED = -3,   /* a valid request this library does not build */
   TP_ERR_HIP = -4,           /* a HIP runtime call or kernel launch failed */
-  TP_ERR_OOM = -5            /* device allocation failed */
+  TP_ERR_OOM = -5,           /* device allocation failed */
+  TP_ERR_IO = -6             /* a weight file is missing, unreadable or too short */
 } tp_status;
 
 typedef enum tp_dtype {
@@ -169,6 +170,34 @@ typedef struct tp_block_shard tp_block_shard;  /* opaque; owns the device weight
  * (or everything allocated so far is freed). */
 TP_API tp_status tp_block_shard_create(const tp_block_config *cfg, const tp_block_weights *w,
                                 tp_block_shard **out);
+
+/* One UNSHARDED weight in a raw file: the array exactly as in tp_block_weights
+ * (row-major, config dtype, bf16 as 16-bit little-endian patterns), element
+ * [0, 0] at byte `offset`.  path == NULL: the weight is absent. */
+typedef struct tp_weight_file {
+  const char *path;
+  int64_t offset;
+} tp_weight_file;
+
+typedef struct tp_block_weight_files {
+  tp_weight_file w_q, w_k, w_v, b_q, b_k, b_v, w_o, w_up, b_up, w_down, w_mod;
+  int64_t ld_o, ld_down;     /* as in tp_block_weights (0 = dense) */
+} tp_block_weight_files;
+
+/* tp_block_shard_create reading the weights from files, shard-on-read
+ * [TP page, §Carregar um modelo fragmentado: each rank reads only its own
+ * slice of each weight, so no rank ever holds a full weight; §Desempenho de
+ * carregamento: this is what bounds the per-rank CPU memory]: only rank
+ * cfg->rank's byte ranges are read (pread), through one pinned host staging
+ * buffer of staging_bytes (>= 1 MiB, else TP_ERR_ARG) split in two halves,
+ * each copied to the device while the other is filled.  Host memory used:
+ * the staging buffer plus the fp32 colwise bias (3*D_r + 2*F_r floats at
+ * most), whatever the weights' size.  The resulting shard is identical to
+ * tp_block_shard_create's for the same weights.  Same validation, in the same
+ * order, before any file is opened; then TP_ERR_IO for a file that cannot be
+ * opened or read or is too short. */
+TP_API tp_status tp_block_shard_load(const tp_block_config *cfg, const tp_block_weight_files *files,
+                                     int64_t staging_bytes, tp_block_shard **out);
 
 /* Free the shard's device memory.  The caller must have synchronised every
  * stream that still uses it.  NULL is ignored. */

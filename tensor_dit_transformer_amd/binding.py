@@ -23,6 +23,7 @@ TP_ERR_DIVISIBILITY = -2
 TP_ERR_UNSUPPORTED = -3
 TP_ERR_HIP = -4
 TP_ERR_OOM = -5
+TP_ERR_IO = -6
 # tp_dtype
 TP_F32 = 0
 TP_BF16 = 1
@@ -43,7 +44,7 @@ EXPORTED = (
     "tp_partial_reduce", "tp_status_string", "tp_last_error_detail",
     "tp_rowwise_split_input_partial", "tp_attn_heads_block", "tp_attn_merge",
     "tp_attn_heads_split", "tp_attn_split_hint", "tp_ulysses_seq_to_heads",
-    "tp_ulysses_heads_to_seq",
+    "tp_ulysses_heads_to_seq", "tp_block_shard_load",
 )
 
 
@@ -62,6 +63,15 @@ _WEIGHT_FIELDS = ("w_q", "w_k", "w_v", "b_q", "b_k", "b_v", "w_o", "w_up", "b_up
 class TpBlockWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS[:10]] + [
         ("ld_o", ctypes.c_int64), ("ld_down", ctypes.c_int64), ("w_mod", ctypes.c_void_p)]
+
+
+class TpWeightFile(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_char_p), ("offset", ctypes.c_int64)]
+
+
+class TpBlockWeightFiles(ctypes.Structure):
+    _fields_ = [(n, TpWeightFile) for n in _WEIGHT_FIELDS] + [
+        ("ld_o", ctypes.c_int64), ("ld_down", ctypes.c_int64)]
 
 
 class TpError(RuntimeError):
@@ -85,6 +95,8 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         L.tp_block_shard_create.argtypes = [ctypes.POINTER(TpBlockConfig),
                                             ctypes.POINTER(TpBlockWeights), ctypes.POINTER(vp)]
+        L.tp_block_shard_load.argtypes = [ctypes.POINTER(TpBlockConfig),
+                                          ctypes.POINTER(TpBlockWeightFiles), i64, ctypes.POINTER(vp)]
         L.tp_block_shard_destroy.argtypes = [vp]
         L.tp_block_shard_destroy.restype = None
         L.tp_colwise_linear.argtypes = [vp, ctypes.c_int, i64, vp, i64, vp, i64, vp]
@@ -106,7 +118,7 @@ def lib() -> ctypes.CDLL:
                                     i64, vp, i64, ctypes.c_int, vp, i64, vp]
         L.tp_partial_reduce.argtypes = [ctypes.POINTER(vp), i32, i64, ctypes.POINTER(vp), i32,
                                         i64, i64, vp, i64, vp]
-        for f in ("tp_block_shard_create", "tp_colwise_linear", "tp_colwise_qkv_up",
+        for f in ("tp_block_shard_create", "tp_block_shard_load", "tp_colwise_linear", "tp_colwise_qkv_up",
                   "tp_attn_heads", "tp_rowwise_linear_partial", "tp_partial_reduce",
                   "tp_rowwise_split_input_partial", "tp_attn_heads_block", "tp_attn_merge",
                   "tp_attn_heads_split", "tp_ulysses_seq_to_heads", "tp_ulysses_heads_to_seq"):
@@ -270,6 +282,22 @@ def tp_block_shard_create(cfg: TpBlockConfig, weights: Dict[str, np.ndarray]) ->
     st = lib().tp_block_shard_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(out))
     del keep
     _check(st)
+    return TpBlockShard(out.value, cfg)
+
+
+def tp_block_shard_load(cfg: TpBlockConfig, files: Dict[str, tuple], staging_bytes: int = 64 << 20,
+                        ld_o: int = 0, ld_down: int = 0) -> TpBlockShard:
+    """Create a shard reading only its slices from raw weight files: `files`
+    maps a weight name (w_q, ..., w_down, w_mod) to (path, byte offset)."""
+    f = TpBlockWeightFiles()
+    for name, (path, offset) in files.items():
+        if name not in _WEIGHT_FIELDS:
+            raise ValueError(f"unknown weight {name}")
+        setattr(f, name, TpWeightFile(str(path).encode(), int(offset)))
+    f.ld_o, f.ld_down = ld_o, ld_down
+    out = ctypes.c_void_p()
+    _check(lib().tp_block_shard_load(ctypes.byref(cfg), ctypes.byref(f), staging_bytes,
+                                     ctypes.byref(out)))
     return TpBlockShard(out.value, cfg)
 
 

@@ -7,9 +7,12 @@
 #include "tp_shard.h"
 #include "tp_kernels.h"
 
+#include <cerrno>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <fcntl.h>
+#include <unistd.h>
 #include <string>
 #include <vector>
 
@@ -93,20 +96,6 @@ tp_status check_tokens(int64_t tokens) {
   return TP_OK;
 }
 
-void widen_bias(std::vector<float>& dst, int64_t at, const void* src, int64_t from, int64_t n,
-                tp_dtype dt) {
-  if (!src) return;  // NULL bias = zero
-  if (dt == TP_F32) {
-    std::memcpy(dst.data() + at, static_cast<const float*>(src) + from, n * sizeof(float));
-  } else {
-    const uint16_t* b = static_cast<const uint16_t*>(src) + from;
-    for (int64_t i = 0; i < n; ++i) {
-      const uint32_t bits = (uint32_t)b[i] << 16;  // exact bf16 -> fp32 widening
-      std::memcpy(&dst[at + i], &bits, 4);
-    }
-  }
-}
-
 void free_shard(tp_block_shard* s) {
   if (!s) return;
   if (s->w_col) (void)hipFree(s->w_col);
@@ -150,15 +139,187 @@ tp_status colwise(const tp_block_shard* s, int64_t tokens, const void* x, int64_
                 s->cfg.dtype, stream);
 }
 
-}  // namespace
+// Where the unsharded weights come from.  Each weight is a row-major array;
+// copy2d moves `rows` rows of `width` bytes, row i starting at byte
+// off0 + i * pitch of that weight, to device rows of `dst_pitch` bytes.
+enum WeightId { W_Q, W_K, W_V, B_Q, B_K, B_V, W_O, W_UP, B_UP, W_DOWN, W_MOD, kNumWeights };
 
-extern "C" {
+struct WeightSource {
+  virtual ~WeightSource() = default;
+  virtual bool present(int which) const = 0;
+  virtual tp_status open() = 0;      // before any device work: files exist
+  virtual tp_status begin() = 0;     // after the device allocations
+  virtual tp_status copy2d(int which, int64_t off0, int64_t pitch, int64_t width, int64_t rows,
+                           char* dst, int64_t dst_pitch) = 0;
+  virtual tp_status read(int which, int64_t off, int64_t bytes, void* host) = 0;
+  virtual tp_status finish() { return TP_OK; }
+  virtual void drain() {}  // wait for copies in flight (error path), keeping the error detail
+};
 
-TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_block_weights* w,
-                                       tp_block_shard** out) {
-  if (!out) return fail(TP_ERR_ARG, "out is NULL");
-  *out = nullptr;
-  if (!cfg || !w) return fail(TP_ERR_ARG, "config or weights is NULL");
+// Caller's host arrays (tp_block_shard_create).
+struct HostSource final : WeightSource {
+  const void* p[kNumWeights];
+  explicit HostSource(const tp_block_weights& w)
+      : p{w.w_q, w.w_k, w.w_v, w.b_q, w.b_k, w.b_v, w.w_o, w.w_up, w.b_up, w.w_down, w.w_mod} {}
+  bool present(int which) const override { return p[which] != nullptr; }
+  tp_status open() override { return TP_OK; }
+  tp_status begin() override { return TP_OK; }
+  tp_status copy2d(int which, int64_t off0, int64_t pitch, int64_t width, int64_t rows, char* dst,
+                   int64_t dst_pitch) override {
+    const hipError_t e = hipMemcpy2D(dst, (size_t)dst_pitch, static_cast<const char*>(p[which]) + off0,
+                                     (size_t)pitch, (size_t)width, (size_t)rows, hipMemcpyHostToDevice);
+    return e == hipSuccess ? TP_OK : hip_fail(e, "weight slice upload");
+  }
+  tp_status read(int which, int64_t off, int64_t bytes, void* host) override {
+    std::memcpy(host, static_cast<const char*>(p[which]) + off, (size_t)bytes);
+    return TP_OK;
+  }
+};
+
+// Raw weight files (tp_block_shard_load): only the rank's byte ranges are
+// read, with pread, into one pinned staging buffer split in two halves; a
+// half is copied to the device asynchronously while the next is read, so host
+// memory stays at the staging size whatever the weights' size.
+struct FileSource final : WeightSource {
+  tp_weight_file f[kNumWeights];
+  int fd[kNumWeights];
+  int64_t staging_bytes;
+  char* staging = nullptr;
+  hipStream_t stream = nullptr;
+  hipEvent_t done[2] = {nullptr, nullptr};
+  bool busy[2] = {false, false};
+  int half = 0;
+
+  FileSource(const tp_block_weight_files& w, int64_t staging)
+      : f{w.w_q, w.w_k, w.w_v, w.b_q, w.b_k, w.b_v, w.w_o, w.w_up, w.b_up, w.w_down, w.w_mod},
+        staging_bytes(staging) {
+    for (int& x : fd) x = -1;
+  }
+  ~FileSource() override {
+    for (int i = 0; i < 2; ++i)
+      if (done[i]) {
+        (void)hipEventSynchronize(done[i]);
+        (void)hipEventDestroy(done[i]);
+      }
+    if (stream) (void)hipStreamDestroy(stream);
+    if (staging) (void)hipHostFree(staging);
+    for (int x : fd)
+      if (x >= 0) close(x);
+  }
+  bool present(int which) const override { return f[which].path != nullptr; }
+  tp_status open() override {
+    for (int i = 0; i < kNumWeights; ++i) {
+      if (!f[i].path) continue;
+      if (f[i].offset < 0) return fail(TP_ERR_ARG, "negative file offset for weight %d", i);
+      fd[i] = ::open(f[i].path, O_RDONLY);
+      if (fd[i] < 0) return fail(TP_ERR_IO, "cannot open %s: %s", f[i].path, strerror(errno));
+    }
+    return TP_OK;
+  }
+  tp_status begin() override {
+    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&staging), (size_t)staging_bytes,
+                                 hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "staging buffer");
+    if ((e = hipStreamCreate(&stream)) != hipSuccess) return hip_fail(e, "staging stream");
+    for (int i = 0; i < 2; ++i)
+      if ((e = hipEventCreateWithFlags(&done[i], hipEventDisableTiming)) != hipSuccess)
+        return hip_fail(e, "staging event");
+    return TP_OK;
+  }
+  tp_status pread_all(int which, int64_t off, int64_t bytes, char* dst) {
+    int64_t got = 0;
+    while (got < bytes) {
+      const ssize_t n = ::pread(fd[which], dst + got, (size_t)(bytes - got), f[which].offset + off + got);
+      if (n < 0 && errno == EINTR) continue;
+      if (n < 0) return fail(TP_ERR_IO, "read of %s failed: %s", f[which].path, strerror(errno));
+      if (n == 0)
+        return fail(TP_ERR_IO, "%s is too short: need byte %lld", f[which].path,
+                    (long long)(f[which].offset + off + bytes));
+      got += n;
+    }
+    return TP_OK;
+  }
+  // The next free staging half (waits for its previous copy to finish).
+  tp_status take(char** buf) {
+    half ^= 1;
+    if (busy[half]) {
+      const hipError_t e = hipEventSynchronize(done[half]);
+      if (e != hipSuccess) return hip_fail(e, "staging copy");
+      busy[half] = false;
+    }
+    *buf = staging + half * (staging_bytes / 2);
+    return TP_OK;
+  }
+  tp_status send(const char* buf, int64_t width, int64_t rows, char* dst, int64_t dst_pitch) {
+    hipError_t e = hipMemcpy2DAsync(dst, (size_t)dst_pitch, buf, (size_t)width, (size_t)width,
+                                    (size_t)rows, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipEventRecord(done[half], stream);
+    if (e != hipSuccess) return hip_fail(e, "staging copy");
+    busy[half] = true;
+    return TP_OK;
+  }
+  tp_status copy2d(int which, int64_t off0, int64_t pitch, int64_t width, int64_t rows, char* dst,
+                   int64_t dst_pitch) override {
+    const int64_t cap = staging_bytes / 2;
+    tp_status st = TP_OK;
+    if (width > cap) {  // long rows: stream each row in pieces
+      for (int64_t i = 0; i < rows && st == TP_OK; ++i)
+        for (int64_t c = 0; c < width && st == TP_OK; c += cap) {
+          const int64_t n = width - c < cap ? width - c : cap;
+          char* buf;
+          if ((st = take(&buf)) == TP_OK && (st = pread_all(which, off0 + i * pitch + c, n, buf)) == TP_OK)
+            st = send(buf, n, 1, dst + i * dst_pitch + c, n);
+        }
+      return st;
+    }
+    const int64_t per = cap / width;  // rows per staging half
+    for (int64_t i = 0; i < rows && st == TP_OK; i += per) {
+      const int64_t n = rows - i < per ? rows - i : per;
+      char* buf;
+      if ((st = take(&buf)) != TP_OK) break;
+      if (pitch == width) {
+        st = pread_all(which, off0 + i * pitch, n * width, buf);
+      } else {
+        for (int64_t j = 0; j < n && st == TP_OK; ++j)
+          st = pread_all(which, off0 + (i + j) * pitch, width, buf + j * width);
+      }
+      if (st == TP_OK) st = send(buf, width, n, dst + i * dst_pitch, dst_pitch);
+    }
+    return st;
+  }
+  tp_status read(int which, int64_t off, int64_t bytes, void* host) override {
+    return pread_all(which, off, bytes, static_cast<char*>(host));
+  }
+  tp_status finish() override {
+    const hipError_t e = hipStreamSynchronize(stream);
+    return e == hipSuccess ? TP_OK : hip_fail(e, "staging copy");
+  }
+  void drain() override {
+    if (stream) (void)hipStreamSynchronize(stream);
+  }
+};
+
+constexpr int64_t kMinStaging = (int64_t)1 << 20;
+
+// fp32 copy of bias elements [from, from + n) into dst[at..]; absent = zero.
+tp_status read_bias(WeightSource& src, int which, std::vector<float>& dst, int64_t at, int64_t from,
+                    int64_t n, tp_dtype dt) {
+  if (!src.present(which)) return TP_OK;
+  if (dt == TP_F32) return src.read(which, from * 4, n * 4, dst.data() + at);
+  std::vector<uint16_t> b((size_t)n);
+  tp_status st = src.read(which, from * 2, n * 2, b.data());
+  if (st != TP_OK) return st;
+  for (int64_t i = 0; i < n; ++i) {
+    const uint32_t bits = (uint32_t)b[i] << 16;  // exact bf16 -> fp32 widening
+    std::memcpy(&dst[at + i], &bits, 4);
+  }
+  return TP_OK;
+}
+
+// Validation, allocation and slice upload shared by create (host arrays) and
+// load (files): every check runs before any weight byte is read.
+tp_status create_from(const tp_block_config* cfg, WeightSource& src, int64_t w_ld_o,
+                      int64_t w_ld_down, tp_block_shard** out) {
   if (cfg->dtype != TP_F32 && cfg->dtype != TP_BF16)
     return fail(TP_ERR_ARG, "unknown dtype %d", (int)cfg->dtype);
   if (cfg->mlp_act != TP_MLP_GELU_TANH && cfg->mlp_act != TP_MLP_SWIGLU)
@@ -200,17 +361,20 @@ TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_bloc
   if (swiglu && Fr % 32)
     return fail(TP_ERR_UNSUPPORTED, "SwiGLU needs ffn/tp (%lld) to be a multiple of 32",
                 (long long)Fr);
-  if (H > 0 && (!w->w_q || !w->w_k || !w->w_v || !w->w_o))
+  if (H > 0 && (!src.present(W_Q) || !src.present(W_K) || !src.present(W_V) || !src.present(W_O)))
     return fail(TP_ERR_ARG, "attention configured but w_q/w_k/w_v/w_o missing");
-  if (F > 0 && (!w->w_up || !w->w_down))
+  if (F > 0 && (!src.present(W_UP) || !src.present(W_DOWN)))
     return fail(TP_ERR_ARG, "MLP configured but w_up/w_down missing");
-  if (Mo > 0 && !w->w_mod) return fail(TP_ERR_ARG, "modulation configured but w_mod missing");
-  const int64_t ld_o = w->ld_o ? w->ld_o : H * d, ld_dn = w->ld_down ? w->ld_down : F;
+  if (Mo > 0 && !src.present(W_MOD)) return fail(TP_ERR_ARG, "modulation configured but w_mod missing");
+  const int64_t ld_o = w_ld_o ? w_ld_o : H * d, ld_dn = w_ld_down ? w_ld_down : F;
   if (H > 0 && ld_o < H * d)
     return fail(TP_ERR_ARG, "ld_o (%lld) < num_heads*head_dim (%lld)", (long long)ld_o,
                 (long long)(H * d));
   if (F > 0 && ld_dn < F)
     return fail(TP_ERR_ARG, "ld_down (%lld) < ffn (%lld)", (long long)ld_dn, (long long)F);
+
+  tp_status st = src.open();
+  if (st != TP_OK) return st;
 
   tp_block_shard* s = new tp_block_shard();
   s->cfg = *cfg;
@@ -239,64 +403,94 @@ TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_bloc
     return hip_fail(e, "hipMalloc of the modulation slice");
   }
 
+  if ((st = src.begin()) != TP_OK) {
+    free_shard(s);
+    return st;
+  }
   // Colwise slices: contiguous blocks of dim-0 rows, one per packed block.
   std::vector<float> bias((size_t)s->n_col, 0.0f);
   char* wc = static_cast<char*>(s->w_col);
-  const size_t row_bytes = (size_t)D * es;
-  auto put_rows = [&](const void* src, int64_t src_row0, int64_t nrows, int64_t dst_row0) {
-    return hipMemcpy(wc + dst_row0 * row_bytes,
-                     static_cast<const char*>(src) + src_row0 * row_bytes, nrows * row_bytes,
-                     hipMemcpyHostToDevice);
+  const int64_t row_bytes = D * (int64_t)es;
+  auto put_rows = [&](int which, int64_t src_row0, int64_t nrows, int64_t dst_row0) {
+    return src.copy2d(which, src_row0 * row_bytes, nrows * row_bytes, nrows * row_bytes, 1,
+                      wc + dst_row0 * row_bytes, nrows * row_bytes);
   };
   if (s->attn) {
-    const void* ws[3] = {w->w_q, w->w_k, w->w_v};
-    const void* bs[3] = {w->b_q, w->b_k, w->b_v};
-    for (int b = 0; b < 3 && e == hipSuccess; ++b) {
-      e = put_rows(ws[b], r * Dr, Dr, b * Dr);
-      widen_bias(bias, b * Dr, bs[b], r * Dr, Dr, cfg->dtype);
+    const int ws[3] = {W_Q, W_K, W_V}, bs[3] = {B_Q, B_K, B_V};
+    for (int b = 0; b < 3 && st == TP_OK; ++b) {
+      st = put_rows(ws[b], r * Dr, Dr, b * Dr);
+      if (st == TP_OK) st = read_bias(src, bs[b], bias, b * Dr, r * Dr, Dr, cfg->dtype);
     }
   }
-  if (e == hipSuccess && s->mlp && !swiglu) {
-    e = put_rows(w->w_up, r * Fr, Fr, s->up_row0);
-    widen_bias(bias, s->up_row0, w->b_up, r * Fr, Fr, cfg->dtype);
+  if (st == TP_OK && s->mlp && !swiglu) {
+    st = put_rows(W_UP, r * Fr, Fr, s->up_row0);
+    if (st == TP_OK) st = read_bias(src, B_UP, bias, s->up_row0, r * Fr, Fr, cfg->dtype);
   }
-  if (e == hipSuccess && swiglu) {
+  if (st == TP_OK && swiglu) {
     // [1, 1] blocks: the rank's gate rows C_r and up rows F + C_r, stored as
     // alternating 32-row blocks so the GEMM epilogue finds a gate column and
     // its up column in neighbouring 32-column MFMA tiles.
     const int64_t blk = 32, nblk = Fr / blk;
-    for (int half = 0; half < 2 && e == hipSuccess; ++half) {
+    for (int half = 0; half < 2 && st == TP_OK; ++half) {
       const int64_t src_row0 = half * F + r * Fr;
-      e = hipMemcpy2D(wc + (s->up_row0 + half * blk) * row_bytes, 2 * blk * row_bytes,
-                      static_cast<const char*>(w->w_up) + src_row0 * row_bytes, blk * row_bytes,
-                      blk * row_bytes, (size_t)nblk, hipMemcpyHostToDevice);
-      for (int64_t b = 0; b < nblk; ++b)
-        widen_bias(bias, s->up_row0 + 2 * blk * b + half * blk, w->b_up, src_row0 + blk * b, blk,
-                   cfg->dtype);
+      st = src.copy2d(W_UP, src_row0 * row_bytes, blk * row_bytes, blk * row_bytes, nblk,
+                      wc + (s->up_row0 + half * blk) * row_bytes, 2 * blk * row_bytes);
+      for (int64_t b = 0; b < nblk && st == TP_OK; ++b)
+        st = read_bias(src, B_UP, bias, s->up_row0 + 2 * blk * b + half * blk, src_row0 + blk * b,
+                       blk, cfg->dtype);
     }
   }
-  if (e == hipSuccess && block)
-    e = hipMemcpy(s->b_col, bias.data(), bias.size() * sizeof(float), hipMemcpyHostToDevice);
+  if (st == TP_OK && block) {
+    const hipError_t e2 = hipMemcpy(s->b_col, bias.data(), bias.size() * sizeof(float),
+                                    hipMemcpyHostToDevice);
+    if (e2 != hipSuccess) st = hip_fail(e2, "bias upload");
+  }
   // Rowwise slices: dim-1 column blocks, copied as strided 2-D regions.
   char* wr = static_cast<char*>(s->w_row);
-  const size_t dpitch = (size_t)s->k_row * es;
-  if (e == hipSuccess && s->attn)
-    e = hipMemcpy2D(wr, dpitch, static_cast<const char*>(w->w_o) + r * Dr * es, (size_t)ld_o * es,
-                    (size_t)Dr * es, (size_t)D, hipMemcpyHostToDevice);
-  if (e == hipSuccess && s->mlp)
-    e = hipMemcpy2D(wr + s->dn_col0 * es, dpitch, static_cast<const char*>(w->w_down) + r * Fr * es,
-                    (size_t)ld_dn * es, (size_t)Fr * es, (size_t)D, hipMemcpyHostToDevice);
+  const int64_t dpitch = s->k_row * (int64_t)es;
+  if (st == TP_OK && s->attn)
+    st = src.copy2d(W_O, r * Dr * (int64_t)es, ld_o * (int64_t)es, Dr * (int64_t)es, D, wr, dpitch);
+  if (st == TP_OK && s->mlp)
+    st = src.copy2d(W_DOWN, r * Fr * (int64_t)es, ld_dn * (int64_t)es, Fr * (int64_t)es, D,
+                    wr + s->dn_col0 * (int64_t)es, dpitch);
   // Modulation slice ("rowwise_split_input"): dim-1 columns M_r.
-  if (e == hipSuccess && s->mod)
-    e = hipMemcpy2D(s->w_mod, (size_t)s->mod_kr * es,
-                    static_cast<const char*>(w->w_mod) + r * s->mod_kr * es, (size_t)Mi * es,
-                    (size_t)s->mod_kr * es, (size_t)Mo, hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
+  if (st == TP_OK && s->mod)
+    st = src.copy2d(W_MOD, r * s->mod_kr * (int64_t)es, Mi * (int64_t)es, s->mod_kr * (int64_t)es,
+                    Mo, static_cast<char*>(s->w_mod), s->mod_kr * (int64_t)es);
+  if (st == TP_OK) st = src.finish();
+  if (st != TP_OK) {
+    src.drain();
     free_shard(s);
-    return hip_fail(e, "weight slice upload");
+    return st;
   }
   *out = s;
   return TP_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+TP_API tp_status tp_block_shard_create(const tp_block_config* cfg, const tp_block_weights* w,
+                                       tp_block_shard** out) {
+  if (!out) return fail(TP_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (!cfg || !w) return fail(TP_ERR_ARG, "config or weights is NULL");
+  HostSource src(*w);
+  return create_from(cfg, src, w->ld_o, w->ld_down, out);
+}
+
+TP_API tp_status tp_block_shard_load(const tp_block_config* cfg, const tp_block_weight_files* files,
+                                     int64_t staging_bytes, tp_block_shard** out) {
+  if (!out) return fail(TP_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (!cfg || !files) return fail(TP_ERR_ARG, "config or files is NULL");
+  if (staging_bytes < kMinStaging)
+    return fail(TP_ERR_ARG, "staging_bytes (%lld) < %lld", (long long)staging_bytes,
+                (long long)kMinStaging);
+  FileSource src(*files, staging_bytes);
+  return create_from(cfg, src, files->ld_o, files->ld_down, out);
 }
 
 TP_API void tp_block_shard_destroy(tp_block_shard* shard) { free_shard(shard); }
@@ -757,6 +951,7 @@ TP_API const char* tp_status_string(tp_status status) {
     case TP_ERR_UNSUPPORTED: return "TP_ERR_UNSUPPORTED: combination not built";
     case TP_ERR_HIP: return "TP_ERR_HIP: HIP runtime error";
     case TP_ERR_OOM: return "TP_ERR_OOM: device allocation failed";
+    case TP_ERR_IO: return "TP_ERR_IO: weight file missing, unreadable or too short";
   }
   return "unknown tp_status";
 }

@@ -364,3 +364,53 @@ def test_ulysses_validation_without_device(L):
     Pp = (ctypes.c_void_p * 2)(a, b)
     assert L.tp_ulysses_heads_to_seq(Pp, 2, 256, 0, 4, 128, 0, tp.TP_BF16, o, 512, None) == tp.TP_OK
     assert L.tp_ulysses_heads_to_seq(Pp, 2, 256, 0, 5, 128, 0, tp.TP_BF16, o, 640, None) == tp.TP_ERR_DIVISIBILITY
+
+
+def _files(L, cfg, files, staging=1 << 20, ld_o=0, ld_down=0):
+    f = binding.TpBlockWeightFiles()
+    for k, v in files.items():
+        setattr(f, k, binding.TpWeightFile(str(v[0]).encode(), v[1]))
+    f.ld_o, f.ld_down = ld_o, ld_down
+    out = ctypes.c_void_p(777)
+    st = L.tp_block_shard_load(ctypes.byref(cfg), ctypes.byref(f), staging, ctypes.byref(out))
+    return st, out.value
+
+
+def test_load_validates_before_opening_any_file(L, tmp_path):
+    missing = tmp_path / "does_not_exist.bin"
+    attn = {k: (missing, 0) for k in ("w_q", "w_k", "w_v", "w_o")}
+    # config errors win over the missing file: nothing is opened before the checks
+    st, out = _files(L, tp.make_config(5, 0, 192, 24, 8, 0, tp.TP_BF16), attn)
+    assert st == tp.TP_ERR_DIVISIBILITY and out is None
+    st, out = _files(L, tp.make_config(2, 0, 32, 4, 8, 0, tp.TP_BF16), {"w_q": (missing, 0)})
+    assert st == tp.TP_ERR_ARG and "missing" in tp.tp_last_error_detail()
+    st, out = _files(L, tp.make_config(2, 0, 32, 4, 8, 0, tp.TP_BF16), attn, staging=1000)
+    assert st == tp.TP_ERR_ARG and "staging" in tp.tp_last_error_detail()
+    # a valid config whose file does not exist: TP_ERR_IO, before any device work
+    st, out = _files(L, tp.make_config(2, 0, 32, 4, 8, 0, tp.TP_BF16), attn)
+    assert st == tp.TP_ERR_IO and out is None and "cannot open" in tp.tp_last_error_detail()
+    real = tmp_path / "w.bin"
+    real.write_bytes(b"\0" * 64)
+    st, out = _files(L, tp.make_config(2, 0, 32, 4, 8, 0, tp.TP_BF16),
+                     {**{k: (real, 0) for k in ("w_q", "w_k", "w_v", "w_o")}, "w_q": (real, -2)})
+    assert st == tp.TP_ERR_ARG and "offset" in tp.tp_last_error_detail()
+    assert L.tp_block_shard_load(None, None, 1 << 20, None) == tp.TP_ERR_ARG
+    assert "TP_ERR_IO" in tp.tp_status_string(tp.TP_ERR_IO)
+
+
+def test_weight_files_struct_matches_the_header(tmp_path):
+    src = tmp_path / "files.c"
+    names = list(binding._WEIGHT_FIELDS) + ["ld_o", "ld_down"]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tp_shard.h"', 'int main(void) {',
+             'printf("%zu %zu\\n", sizeof(tp_weight_file), sizeof(tp_block_weight_files));']
+    lines += [f'printf("%zu\\n", offsetof(tp_block_weight_files, {n}));' for n in names]
+    lines += ['return 0; }']
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "files"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [ctypes.sizeof(binding.TpWeightFile), ctypes.sizeof(binding.TpBlockWeightFiles)]
+    want += [getattr(binding.TpBlockWeightFiles, n).offset for n in names]
+    assert got == want

@@ -43,6 +43,20 @@ def packed_host_weights(inp: tp_inputs.Inputs) -> Dict[str, np.ndarray]:
             "w_out": np.ascontiguousarray(np.concatenate([h["w_o"], h["w_down"]], axis=1))}
 
 
+def write_weights(path, weights: Dict[str, np.ndarray]) -> Dict[str, tuple]:
+    """Append the arrays to one raw file (a checkpoint of unsharded weights,
+    each row-major in the workload's dtype) and return {name: (path, byte
+    offset)} for the shard-on-read loader.  Data movement only."""
+    out, off = {}, 0
+    with open(path, "wb") as f:
+        for name, a in weights.items():
+            a = np.ascontiguousarray(a)
+            out[name] = (str(path), off)
+            f.write(a.tobytes())
+            off += a.nbytes
+    return out
+
+
 def create_shards(w: tp_inputs.Workload, inp: tp_inputs.Inputs, ranks=None,
                   packed: bool = False) -> List[tp.TpBlockShard]:
     hw = packed_host_weights(inp) if packed else host_weights(inp)
