@@ -13,7 +13,9 @@
 #include <cstring>
 #include <fcntl.h>
 #include <unistd.h>
+#include <algorithm>
 #include <string>
+#include <thread>
 #include <vector>
 
 struct tp_block_shard {
@@ -139,6 +141,8 @@ tp_status colwise(const tp_block_shard* s, int64_t tokens, const void* x, int64_
                 s->cfg.dtype, stream);
 }
 
+constexpr int kReadThreads = 8;
+
 // Where the unsharded weights come from.  Each weight is a row-major array;
 // copy2d moves `rows` rows of `width` bytes, row i starting at byte
 // off0 + i * pitch of that weight, to device rows of `dst_pitch` bytes.
@@ -179,7 +183,9 @@ struct HostSource final : WeightSource {
 // Raw weight files (tp_block_shard_load): only the rank's byte ranges are
 // read, with pread, into one pinned staging buffer split in two halves; a
 // half is copied to the device asynchronously while the next is read, so host
-// memory stays at the staging size whatever the weights' size.
+// memory stays at the staging size whatever the weights' size.  A half is
+// filled by up to kReadThreads threads (one copy from the page cache per
+// thread is what limits a single reader).
 struct FileSource final : WeightSource {
   tp_weight_file f[kNumWeights];
   int fd[kNumWeights];
@@ -226,17 +232,49 @@ struct FileSource final : WeightSource {
         return hip_fail(e, "staging event");
     return TP_OK;
   }
-  tp_status pread_all(int which, int64_t off, int64_t bytes, char* dst) {
+  // Reads [off, off + bytes) of weight `which`: 0, or -errno, or 1 if the file ends first.
+  int read_range(int which, int64_t off, int64_t bytes, char* dst) const {
     int64_t got = 0;
     while (got < bytes) {
       const ssize_t n = ::pread(fd[which], dst + got, (size_t)(bytes - got), f[which].offset + off + got);
       if (n < 0 && errno == EINTR) continue;
-      if (n < 0) return fail(TP_ERR_IO, "read of %s failed: %s", f[which].path, strerror(errno));
-      if (n == 0)
-        return fail(TP_ERR_IO, "%s is too short: need byte %lld", f[which].path,
-                    (long long)(f[which].offset + off + bytes));
+      if (n < 0) return -errno;
+      if (n == 0) return 1;
       got += n;
     }
+    return 0;
+  }
+  tp_status report(int which, int rc, int64_t end) const {
+    if (rc == 0) return TP_OK;
+    if (rc > 0)
+      return fail(TP_ERR_IO, "%s is too short: need byte %lld", f[which].path,
+                  (long long)(f[which].offset + end));
+    return fail(TP_ERR_IO, "read of %s failed: %s", f[which].path, strerror(-rc));
+  }
+  tp_status pread_all(int which, int64_t off, int64_t bytes, char* dst) {
+    return report(which, read_range(which, off, bytes, dst), off + bytes);
+  }
+  // `n` row segments of `width` bytes, segment j at off0 + j * pitch, packed
+  // into dst, read by up to kReadThreads threads.
+  tp_status read_rows(int which, int64_t off0, int64_t pitch, int64_t width, int64_t n, char* dst) {
+    const int64_t bytes = n * width;
+    const int nt = (int)std::min<int64_t>(kReadThreads, std::max<int64_t>(1, bytes >> 22));
+    std::vector<int> rc(nt, 0);
+    auto work = [&](int t) {
+      if (pitch == width) {  // one contiguous range: split it
+        const int64_t a = bytes * t / nt, b = bytes * (t + 1) / nt;
+        rc[t] = read_range(which, off0 + a, b - a, dst + a);
+      } else {
+        for (int64_t j = n * t / nt; j < n * (t + 1) / nt && rc[t] == 0; ++j)
+          rc[t] = read_range(which, off0 + j * pitch, width, dst + j * width);
+      }
+    };
+    std::vector<std::thread> pool;
+    for (int t = 1; t < nt; ++t) pool.emplace_back(work, t);
+    work(0);
+    for (auto& th : pool) th.join();
+    for (int t = 0; t < nt; ++t)
+      if (rc[t]) return report(which, rc[t], off0 + (n - 1) * pitch + width);
     return TP_OK;
   }
   // The next free staging half (waits for its previous copy to finish).
@@ -267,7 +305,7 @@ struct FileSource final : WeightSource {
         for (int64_t c = 0; c < width && st == TP_OK; c += cap) {
           const int64_t n = width - c < cap ? width - c : cap;
           char* buf;
-          if ((st = take(&buf)) == TP_OK && (st = pread_all(which, off0 + i * pitch + c, n, buf)) == TP_OK)
+          if ((st = take(&buf)) == TP_OK && (st = read_rows(which, off0 + i * pitch + c, n, n, 1, buf)) == TP_OK)
             st = send(buf, n, 1, dst + i * dst_pitch + c, n);
         }
       return st;
@@ -277,12 +315,7 @@ struct FileSource final : WeightSource {
       const int64_t n = rows - i < per ? rows - i : per;
       char* buf;
       if ((st = take(&buf)) != TP_OK) break;
-      if (pitch == width) {
-        st = pread_all(which, off0 + i * pitch, n * width, buf);
-      } else {
-        for (int64_t j = 0; j < n && st == TP_OK; ++j)
-          st = pread_all(which, off0 + (i + j) * pitch, width, buf + j * width);
-      }
+      st = read_rows(which, off0 + i * pitch, pitch, width, n, buf);
       if (st == TP_OK) st = send(buf, width, n, dst + i * dst_pitch, dst_pitch);
     }
     return st;

@@ -116,7 +116,12 @@ C9 = Workload("cp_ring_bf16_T4608_H24_R4", 4608, 3072, 24, 128, 0, 1, "bf16",
 C10 = Workload("cp_ulysses_bf16_T4608_H24_U4", 4608, 3072, 24, 128, 0, 1, "bf16",
                "Ulysses Attention over 4 simulated GPUs", cp="ulysses", cp_degree=4)
 
-WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5_P4, C5_P2, C6, C7, C8, C9, C10)}
+# Shard-on-read loading of the full block's weights (a 755 MB bf16
+# checkpoint) by all 4 ranks, each reading only its slices.
+C11 = Workload("load_block_bf16_D6144_H48_F18432_P4", 0, 6144, 48, 128, 18432, 4, "bf16",
+               "every rank of tp_degree 4 loads its slices from one raw checkpoint file")
+
+WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5_P4, C5_P2, C6, C7, C8, C9, C10, C11)}
 
 
 def cp_qkv(w: Workload, seed: int = 0, tokens: Optional[int] = None):
