@@ -371,20 +371,34 @@ attn_fwd_pipe(AttnIO io) {
   }
 
   const int nkt = (T + kBKV - 1) / kBKV;
+  const int nfull = T / kBKV;   // tiles with every key valid
   // Load n (0..31) of tile kt: K rows (n < 16) or V rows 4 (n & 15) .. + 3;
-  // wave w issues loads PER_WAVE w .. PER_WAVE (w + 1) - 1.
+  // wave w issues loads PER_WAVE w .. PER_WAVE (w + 1) - 1.  A load's
+  // address is a wave-uniform tile base plus a loop-invariant per-lane 32-bit
+  // offset (row within the tile, chunk); a partial last tile uses offsets
+  // with its rows past T clamped to T - 1.
+  uint32_t loff[PER_WAVE], loff_last[PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int n = PER_WAVE * wave + j;
+    const int rr = 4 * (n & 15) + (lane >> 4);
+    const int c = (lane & 15) ^ swz(rr);
+    const int rlast = min(nfull * kBKV + rr, T - 1) - nfull * kBKV;
+    loff[j] = (uint32_t)((int64_t)rr * io.ldkv * 2 + 16 * c);
+    loff_last[j] = (uint32_t)((int64_t)rlast * io.ldkv * 2 + 16 * c);
+  }
+  const int64_t tile_bytes = (int64_t)kBKV * io.ldkv * 2;
   auto load_tile = [&](int kt) {
     const int buf = kt % NSTAGE;
     const int tt = min(kt, nkt - 1);
+    const bool full = tt < nfull;
+    const int64_t toff = (int64_t)tt * tile_bytes;
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int n = PER_WAVE * wave + j;
-      const int blk = n & 15;
-      const int rr = 4 * blk + (lane >> 4);
-      const int c = (lane & 15) ^ swz(rr);
-      const int64_t row = min(tt * kBKV + rr, T - 1);
-      const bf16* src = (n < 16 ? Kg : Vg) + row * io.ldkv + 8 * c;
-      u32x4* dst = (n < 16 ? sK[buf] : sV[buf]) + 64 * blk;
+      const char* src = reinterpret_cast<const char*>(n < 16 ? Kg : Vg) + toff +
+                        (full ? loff[j] : loff_last[j]);
+      u32x4* dst = (n < 16 ? sK[buf] : sV[buf]) + 64 * (n & 15);
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                        (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
     }
