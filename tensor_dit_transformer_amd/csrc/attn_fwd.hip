@@ -65,6 +65,13 @@ constexpr int kRowChunks = kD / 8; // 16-byte chunks per K or V row (256 bytes)
 // constant) sends the two groups to disjoint halves of the banks.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// x of lane l ^ 32: one v_permlane32_swap (lanes 32-63 of the first operand
+// trade places with lanes 0-31 of the second) instead of an LDS permute.
+__device__ __forceinline__ float other_half(float x, int half) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(half ? r[0] : r[1]);
+}
+
 // Slack (log2 domain) the running max may trail the true row max before the
 // accumulator is rescaled.  Softmax is invariant to the reference value, so
 // this only lets the unnormalised weights grow to at most 2^8; it skips almost
@@ -99,7 +106,7 @@ template <bool LSE>
 __device__ __forceinline__ void store_rows(const AttnIO& a, int head, int q, int half,
                                            const f32x16 (&acc_o)[kD / 32], float m_ref,
                                            float l_run) {
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = l_run + other_half(l_run, half);
   const float inv = 1.0f / l_tot;
   if (q >= a.Tq) return;
   if constexpr (LSE) {
@@ -171,12 +178,12 @@ __device__ __forceinline__ void attn_tile(const u32x4* __restrict__ sK, const u3
       }
   }
   // tile max of this lane's 32 scores, then of the other half-wave's 32
-  float mloc = s[0][0];
+  float mloc = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-  for (int e = 1; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s[0][e], s[0][e + 1]));
+  for (int e = 2; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s[0][e], s[0][e + 1]));
 #pragma unroll
   for (int e = 0; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s[1][e], s[1][e + 1]));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;
+  mloc = fmaxf(mloc, other_half(mloc, half)) * scale_log2;
   // rescale only when some row's max outgrew the reference by the slack
   if (__builtin_amdgcn_ballot_w64(mloc > m_ref + kRescaleSlack)) {
     const float m_new = fmaxf(m_ref, mloc);
@@ -443,6 +450,34 @@ attn_fwd_pipe(AttnIO io) {
   const int off8 = (dsub & 7) * 2;
   const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
 
+  // O^T += V^T P^T for one tile.  The LDS pointer is __restrict__ (as in
+  // scores) so the compiler can tell these reads from the LDS-bound loads in
+  // flight and adds no wait for them: the vmcnt wait before each barrier
+  // already orders every tile's loads before its reads, and a tile's loads
+  // get two iterations to land.
+  auto pv = [&](const u32x4* __restrict__ sVb, const bf16x8 (&pb)[NQ][2][2]) {
+#pragma unroll
+    for (int t = 0; t < kD / 32; ++t) {
+      const int lchunk = (32 * t + dsub) >> 3;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int kb = 32 * c + 16 * u;
+          const char* pa = reinterpret_cast<const char*>(sVb + (kb + keyA) * kRowChunks + (lchunk ^ fA)) + off8;
+          const char* pbp = reinterpret_cast<const char*>(sVb + (kb + keyB) * kRowChunks + (lchunk ^ fB)) + off8;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(pa));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(pbp));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int a = 0; a < NQ; ++a)
+            acc_o[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[a][c][u], acc_o[a][t], 0, 0, 0);
+        }
+    }
+  };
+
   // One key tile: s_cur holds raw scores of tile kt; issues scores of kt + 1.
   auto step = [&](int kt, f32x16 (&s_cur)[NQ][2], f32x16 (&s_nxt)[NQ][2]) {
     if (kt * kBKV + kBKV > T) {  // last, partial tile: mask keys past T
@@ -463,12 +498,12 @@ attn_fwd_pipe(AttnIO io) {
     bool rescale = false;
 #pragma unroll
     for (int a = 0; a < NQ; ++a) {
-      float mloc = s_cur[a][0][0];
+      float mloc = fmaxf(s_cur[a][0][0], s_cur[a][0][1]);
 #pragma unroll
-      for (int e = 1; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s_cur[a][0][e], s_cur[a][0][e + 1]));
+      for (int e = 2; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s_cur[a][0][e], s_cur[a][0][e + 1]));
 #pragma unroll
       for (int e = 0; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s_cur[a][1][e], s_cur[a][1][e + 1]));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;
+      mloc = fmaxf(mloc, other_half(mloc, half)) * scale_log2;
       const bool need = __builtin_amdgcn_ballot_w64(mloc > m_ref[a] + kRescaleSlack) != 0;
       const float m_new = need ? fmaxf(m_ref[a], mloc) : m_ref[a];
       alpha[a] = __builtin_amdgcn_exp2f(m_ref[a] - m_new);
@@ -505,28 +540,7 @@ attn_fwd_pipe(AttnIO io) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) acc_o[a][t][e] *= alpha[a];
     }
-    // O^T += V^T P^T for tile kt
-    const u32x4* sVb = sV[kt % NSTAGE];
-#pragma unroll
-    for (int t = 0; t < kD / 32; ++t) {
-      const int lchunk = (32 * t + dsub) >> 3;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int kb = 32 * c + 16 * u;
-          const char* pa = reinterpret_cast<const char*>(sVb + (kb + keyA) * kRowChunks + (lchunk ^ fA)) + off8;
-          const char* pbp = reinterpret_cast<const char*>(sVb + (kb + keyB) * kRowChunks + (lchunk ^ fB)) + off8;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(pa));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(pbp));
-          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int a = 0; a < NQ; ++a)
-            acc_o[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[a][c][u], acc_o[a][t], 0, 0, 0);
-        }
-    }
+    pv(sV[kt % NSTAGE], pb);
     barrier_keep_newest_loads<PER_WAVE>();
   };
 
