@@ -60,6 +60,8 @@ def close(shards):
     (64, 512, 1536, "bf16"),                                  # few-row kernel
     (8, 512, 1552, "bf16"),                                   # N % 32 != 0: one row group
     (8, 160, 1536, "bf16"),                                   # K_r = 40: a k-block tail
+    (8, 512, 16 * 773, "bf16"),                               # 773 row groups: more than the
+                                                              # workgroup slots, so a few loop twice
     (65, 512, 1536, "bf16"), (200, 512, 1536, "bf16"),        # GEMM
     (8, 512, 264, "bf16"),                                    # N % 16 != 0: GEMM
     (8, 256, 512, "f32"), (70, 256, 512, "f32"),              # fp32 GEMM
