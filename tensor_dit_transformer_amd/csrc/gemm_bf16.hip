@@ -227,15 +227,22 @@ gemm_bf16_nt(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
 // (global_load_lds_dwordx4: each wave instruction fills 1 KB = 8 tile rows),
 // so no registers stage them and no ds_write is issued; K % 64 == 0 (no
 // zero-fill on this path).  Waves 0-3 (group 0) own C rows 0-127 and waves
-// 4-7 (group 1) rows 128-255.  The groups run one phase
-// apart, separated by workgroup barriers: while one group reads a whole K
-// tile of operand fragments from LDS into registers (24 x 16 bytes per
-// lane), the other issues the 32 MFMAs of the tile it read in the previous
-// phase.  Phase 2k: group 0 reads tile k, group 1 multiplies tile k-1;
-// phase 2k+1: group 0 multiplies tile k, group 1 reads tile k.  Tile k+1 is
-// fetched global -> LDS during phase 2k into the stage that held tile k-1
-// (group 0 after its LDS reads, group 1 spread through its MFMAs) and waited
-// for at the end of phase 2k+1.
+// 4-7 (group 1) rows 128-255.  The groups run one phase apart, separated by
+// workgroup barriers: while one group reads a whole K tile of operand
+// fragments from LDS into registers (24 x 16 bytes per lane), the other
+// issues the 32 MFMAs of the tile it read in the previous phase.  Phase 2k:
+// group 0 reads tile k, group 1 multiplies tile k-1; phase 2k+1: group 0
+// multiplies tile k, group 1 reads tile k.
+//
+// A wave that waits to issue a global load issues no MFMA meanwhile, so
+// loads are issued only in read phases: group 0, after reading tile k in
+// phase 2k, fetches the whole B tile k+1; group 1, after reading tile k in
+// phase 2k+1, fetches the whole A tile k+2.  A has three LDS stages and B
+// two (96 + 64 KB): the B tile k+1 goes into the stage of tile k-1 (last
+// read in phase 2k-1) and is waited for by group 0 at the end of phase 2k+1;
+// the A tile k+2 goes into the stage of tile k-1 too and is waited for by
+// group 1 at the end of phase 2k+3.  Tile 0 and A tile 1 are fetched before
+// the loop.
 __device__ __forceinline__ void wg_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
@@ -248,15 +255,23 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// all but the newest 8 loads of this wave have landed
+__device__ __forceinline__ void wait_vmem_keep8() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <OutKind KIND, int GROUP_SHIFT>
 __global__ void __launch_bounds__(512)
 gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
   constexpr int BM = 256, BN = 256;
   constexpr int TM = 4, TN = 2;                 // 128 x 64 per wave
   constexpr int KS = kBK / 16;                  // 4 MFMA k-steps per tile
-  constexpr int BUF = (BM + BN) * kRowChunks;   // 16-byte chunks per stage
+  constexpr int A_STAGE = BM * kRowChunks;      // 16-byte chunks per A stage
+  constexpr int B_STAGE = BN * kRowChunks;
 
-  __shared__ u32x4 smem[2 * BUF];
+  __shared__ u32x4 smem[3 * A_STAGE + 2 * B_STAGE];   // 160 KB
 
   const int nb = gridDim.x, bid = blockIdx.x;
   const int xcd = bid & 7, per = nb >> 3, rem = nb & 7;
@@ -276,37 +291,35 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
   const bf16* __restrict__ A = static_cast<const bf16*>(p.A);
   const bf16* __restrict__ B = static_cast<const bf16*>(p.B);
 
-  // global -> LDS.  Wave q's instruction pair i (one for A, one for B)
-  // covers 8 rows from 64 q + 8 i; group 0 fetches i < 4, group 1 i >= 4.
-  // Rows 64 q + 8 i + (lane >> 3): the swizzle depends only on i & 1.
+  auto stage_a = [&](int kt) { return smem + (kt % 3) * A_STAGE; };
+  auto stage_b = [&](int kt) { return smem + 3 * A_STAGE + (kt & 1) * B_STAGE; };
+
+  // global -> LDS: wave q of the fetching group covers operand rows
+  // 64 q + 8 i + (lane >> 3), i = 0..7, one instruction each; the swizzle
+  // of a row depends only on i & 1.
   const int row0 = 64 * q + (lane >> 3);
   const int kc_even = swizzle(row0, lane & 7) * 8, kc_odd = swizzle(row0 + 8, lane & 7) * 8;
-  auto issue = [&](int kt, int first, int count) {
+  auto fetch = [&](const bf16* __restrict__ src, int ld, int first_row, int rows, int kt, u32x4* dst) {
     const int k = kt * kBK;
-    u32x4* sa = smem + (kt & 1) * BUF;
-    u32x4* sb = sa + BM * kRowChunks;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (i < first || i >= first + count) continue;
       const int kc = (i & 1) ? kc_odd : kc_even;
-      const int a_off = min(m0 + row0 + 8 * i, p.M - 1) * (int)p.lda + kc + k;
-      const int b_off = min(n0 + row0 + 8 * i, p.N - 1) * (int)p.ldb + kc + k;
+      const int off = min(first_row + row0 + 8 * i, rows - 1) * ld + kc + k;
       __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(A + a_off),
-          (void __attribute__((address_space(3)))*)(sa + (64 * q + 8 * i) * kRowChunks), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(B + b_off),
-          (void __attribute__((address_space(3)))*)(sb + (64 * q + 8 * i) * kRowChunks), 16, 0, 0);
+          (const void __attribute__((address_space(1)))*)(src + off),
+          (void __attribute__((address_space(3)))*)(dst + (64 * q + 8 * i) * kRowChunks), 16, 0, 0);
     }
   };
+  auto fetch_a = [&](int kt) { fetch(A, (int)p.lda, m0, p.M, kt, stage_a(kt)); };
+  auto fetch_b = [&](int kt) { fetch(B, (int)p.ldb, n0, p.N, kt, stage_b(kt)); };
 
   const int a_row = 128 * g + (lane & 31);
   const int b_row = 64 * q + (lane & 31);
   const int khalf = lane >> 5;
   bf16x8 fa[KS][TM], fb[KS][TN];
   auto read_tile = [&](int kt) {
-    const u32x4* sa = smem + (kt & 1) * BUF;
-    const u32x4* sb = sa + BM * kRowChunks;
+    const u32x4* sa = stage_a(kt);
+    const u32x4* sb = stage_b(kt);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int kc = 2 * s + khalf;
@@ -325,27 +338,23 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  // The MFMAs of one tile; with load_kt >= 0, this wave's half of that
-  // tile's global -> LDS loads is issued one row block after each k-step, so
-  // a load that waits at issue holds up at most 8 MFMAs.
-  auto multiply = [&](int load_kt) {
+  auto multiply = [&]() {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
-      if (load_kt >= 0) {
-        __builtin_amdgcn_sched_barrier(0);
-        issue(load_kt, 4 + s, 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
   };
 
   const int nk = p.K / kBK;
-  issue(0, 4 * g, 4);                     // first tile: each group half of it
+  if (g == 0) {
+    fetch_b(0);
+  } else {
+    fetch_a(0);
+    if (nk > 1) fetch_a(1);
+  }
   wait_vmem();
   wg_barrier();
   if (g == 0) {
@@ -353,24 +362,28 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
       const bool more = kt + 1 < nk;
       read_tile(kt);
       __builtin_amdgcn_sched_barrier(0);
-      if (more) issue(kt + 1, 0, 4);      // group 0's half, after its LDS reads
+      if (more) fetch_b(kt + 1);
       wg_barrier();                       // end of phase 2 kt
-      multiply(-1);
-      if (more) wait_vmem();
+      multiply();
+      if (more) wait_vmem();              // B tile kt + 1
       wg_barrier();                       // end of phase 2 kt + 1
     }
     wg_barrier();
   } else {
     for (int kt = 0; kt < nk; ++kt) {
-      const bool more = kt + 1 < nk;
-      if (kt > 0) multiply(more ? kt + 1 : -1);   // tile kt - 1, loading tile kt + 1
-      else if (more) issue(kt + 1, 4, 4);
+      if (kt > 0) multiply();             // tile kt - 1
       wg_barrier();                       // end of phase 2 kt
       read_tile(kt);
-      if (more) wait_vmem();
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 2 < nk) {
+        fetch_a(kt + 2);
+        wait_vmem_keep8();                // A tile kt + 1
+      } else {
+        wait_vmem();
+      }
       wg_barrier();                       // end of phase 2 kt + 1
     }
-    multiply(-1);
+    multiply();
     wg_barrier();
   }
 
