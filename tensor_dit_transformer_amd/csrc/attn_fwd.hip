@@ -24,9 +24,11 @@
 //     ds_read_b64_tr_b16 (in each 16-lane group, source lane 4 r + c points
 //     at V[k + r][d + 4 c] and lane i receives V[k + e][d + i], e = 0..3).
 //   * K and V tiles of 64 keys go global -> LDS directly
-//     (global_load_lds_dwordx4), one tile ahead, into a double-buffered LDS
-//     with 256-byte rows and an XOR chunk swizzle that keeps both the K reads
-//     and the transposed V reads conflict-free; one barrier per tile.
+//     (global_load_lds_dwordx4) into LDS rows of 256 bytes with an XOR chunk
+//     swizzle that keeps both the K reads and the transposed V reads
+//     conflict-free; one barrier per tile.  The 4-wave kernel double-buffers
+//     one tile ahead, the long-sequence kernel keeps four stages and fetches
+//     three tiles ahead.
 //   * Softmax runs in the exp2 domain with few vector instructions per
 //     score: one FMA (scale folded in) and one exp2; the row sum is a bf16
 //     dot2 over the packed weights; the accumulator is rescaled by
@@ -328,9 +330,11 @@ attn_fwd_bf16_d128(AttnIO a) {
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined form.  One wave per SIMD (4 waves, up to 512 registers
-// per lane), NQ sub-tiles of 32 queries per wave (K and V operands are read
-// once per wave and feed NQ MFMAs).  Within key tile j a wave issues the
+// Software-pipelined form for long query sets, launched as NW = 8 waves (two
+// per SIMD, <= 256 VGPRs each) of NQ = 1 sub-tile of 32 queries.  (With NQ
+// sub-tiles a K or V fragment read from LDS would feed NQ MFMAs, but the
+// state of NQ = 2 does not fit the registers of two waves per SIMD, and at
+// one wave per SIMD the compiler spills.)  Within key tile j a wave issues the
 // score MFMAs of tile j+1 in the same straight-line block as the softmax of
 // tile j, interleaved about one MFMA per seven vector instructions, so the
 // matrix core and the vector ALU work at the same time inside one wave; then
