@@ -8,21 +8,26 @@
 // weight slice is an nn.Linear [out, in] matrix, so both operands are
 // K-contiguous and the kernel is one "NT" GEMM with different epilogues.
 //
-// Design (gfx950, 64-wide waves, 160 KB LDS per CU):
+// Design (gfx950, 64-wide waves, 160 KB LDS per CU).  Two kernels: a
+// 4-wave register-staged one for small and ragged shapes, and the 8-wave
+// ping-pong kernel further down for large ones (at least 128 tiles of
+// 256x256, K % 64 == 0).  The 4-wave kernel:
 //   * 256 threads = 4 waves in a WM x WN grid; each wave owns a
 //     (BM/WM) x (BN/WN) block of C held in accumulation registers as
 //     32x32 tiles of v_mfma_f32_32x32x16_bf16.
 //   * K advances 64 elements (128 bytes per row) per tile.  A and B tiles are
 //     fetched with 16-byte global loads into registers one tile ahead, then
 //     written to a double-buffered LDS tile; one barrier per K tile.
+// Both kernels:
 //   * LDS rows are 128 bytes; the 16-byte chunk of k-group kc of row r lives
 //     at chunk kc ^ (r & 7) ^ ((r >> 3) & 1), so the rows read by one
 //     ds_read_b128 phase fall in distinct banks.
 //   * Workgroup ids are renumbered so each of the 8 XCDs (own L2) walks a
 //     contiguous stretch of a grouped tile order (8 tile rows per group), and
 //     the A/B panels it streams are shared by its neighbours in L2.
-//   * Rows past M / N are clamped on load and masked on store; a K that is not
-//     a multiple of 64 zero-fills the chunks past K (K must be a multiple of 8).
+//   * Rows past M / N are clamped on load and masked on store.  In the 4-wave
+//     kernel a K that is not a multiple of 64 zero-fills the chunks past K
+//     (K must be a multiple of 8).
 #include "tp_kernels.h"
 
 namespace tpk {
