@@ -307,20 +307,29 @@ def setup_cp(w):
     shard = H.create_shards(hw, tp_inputs.make_inputs(hw, seed=0), ranks=(0,))[0]
     kernels = {}
     if w.cp == "ring":
-        o_parts = [torch.empty((n, HD), dtype=torch.float32, device="cuda") for _ in range(R)]
-        l_parts = [torch.empty((n, Hh), dtype=torch.float32, device="cuda") for _ in range(R)]
+        # a step's chunks may be too short to fill the GPU: then each step
+        # runs as S key ranges in one launch and the merge takes R * S parts
+        S = key_splits = tp.tp_attn_split_hint(shard, n)
+        o_parts = torch.empty((R, S, n, HD), dtype=torch.float32, device="cuda")
+        l_parts = torch.empty((R, S, n, Hh), dtype=torch.float32, device="cuda")
+        o_list, l_list = list(o_parts.flatten(0, 1)), list(l_parts.flatten(0, 1))
         out = torch.empty((T, HD), dtype=torch.bfloat16, device="cuda")
         kernels["attention_block"] = ("attn_fwd.hip", 4 * n * n * d * Hh, "mfma")
-        kernels["attn_merge"] = ("attn_merge.hip", R * n * (HD + Hh) * 4 + n * HD * 2, "hbm")
+        kernels["attn_merge"] = ("attn_merge.hip", R * S * n * (HD + Hh) * 4 + n * HD * 2, "hbm")
+
+        def step(t, q, kv):
+            if S == 1:
+                tp.tp_attn_heads_block(shard, n, q, n, kv, o_parts[t, 0], l_parts[t, 0])
+            else:
+                tp.tp_attn_heads_block_split(shard, n, q, n, kv, o_parts[t], l_parts[t])
 
         def run(mark):
             for c in range(R):
                 for t in range(R):
                     j = (c - t) % R
-                    mark("attention_block", lambda: tp.tp_attn_heads_block(
-                        shard, n, qkv[c * n:(c + 1) * n], n, qkv[j * n:(j + 1) * n], o_parts[t],
-                        l_parts[t]))
-                mark("attn_merge", lambda: tp.tp_attn_merge(o_parts, l_parts, out[c * n:(c + 1) * n],
+                    mark("attention_block", lambda: step(t, qkv[c * n:(c + 1) * n],
+                                                         qkv[j * n:(j + 1) * n]))
+                mark("attn_merge", lambda: tp.tp_attn_merge(o_list, l_list, out[c * n:(c + 1) * n],
                                                             Hh, d))
     else:
         W = HD // R
@@ -328,7 +337,7 @@ def setup_cp(w):
         hv = torch.empty((T, 3 * W), dtype=torch.bfloat16, device="cuda")
         o_heads = [torch.empty((T, W), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
         back = [torch.empty((n, HD), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
-        splits = tp.tp_attn_split_hint(shard, T)
+        splits = key_splits = tp.tp_attn_split_hint(shard, T)
         if splits > 1:
             op = torch.empty((splits, T, W), dtype=torch.float32, device="cuda")
             lp = torch.empty((splits, T, Hh // R), dtype=torch.float32, device="cuda")
@@ -355,7 +364,7 @@ def setup_cp(w):
         shard.close()
 
     config = {"workload": w.name, "tokens": T, "num_heads": Hh, "head_dim": d, "cp": w.cp,
-              "cp_degree": R, "ranks_per_step": R,
+              "cp_degree": R, "ranks_per_step": R, "key_splits": key_splits,
               "step": f"{w.cp} attention of all {Hh} heads over {R} simulated GPUs"}
     return Setup(kernels, run, 4 * T * T * d * Hh, config, close)
 

@@ -275,6 +275,27 @@ TP_API tp_status tp_attn_heads_split(tp_block_shard *shard, int64_t tokens, cons
                                      int64_t o_part_stride, float *lse_parts, int64_t ld_lse,
                                      int64_t lse_part_stride, void *stream);
 
+/* tp_attn_heads_block with the block's keys cut into n_splits contiguous
+ * ranges [floor(z*kv_tokens/n_splits), floor((z+1)*kv_tokens/n_splits)) in
+ * ONE launch -- one Ring Attention step [CP page, §Ring Attention] whose
+ * query and key chunks are too short to fill the GPU in one piece.  Range z
+ * writes its (o, lse) like tp_attn_heads_block at
+ *   o_parts + z * o_part_stride     fp32 [q_tokens, D_r], row stride ldo
+ *   lse_parts + z * lse_part_stride fp32 [q_tokens, H/P], row stride ld_lse
+ * (strides in elements, o_part_stride a multiple of 4; the parts must not
+ * overlap each other or the inputs).  The ranges are disjoint key blocks, so
+ * tp_attn_merge over them (with the parts of the other ring steps) gives the
+ * attention over all keys.  1 <= n_splits <= 16 (else TP_ERR_ARG /
+ * TP_ERR_UNSUPPORTED), n_splits <= kv_tokens when q_tokens > 0; n_splits == 1
+ * is tp_attn_heads_block.  tp_attn_split_hint(shard, q_tokens) gives a split
+ * count that fills the GPU. */
+TP_API tp_status tp_attn_heads_block_split(tp_block_shard *shard, int64_t q_tokens,
+                                           const void *q_qkv, int64_t ldq, int64_t kv_tokens,
+                                           const void *kv_qkv, int64_t ldkv, int32_t n_splits,
+                                           float *o_parts, int64_t ldo, int64_t o_part_stride,
+                                           float *lse_parts, int64_t ld_lse,
+                                           int64_t lse_part_stride, void *stream);
+
 /* Host-only query: the n_splits (1..4) at which tp_attn_heads_split over
  * `tokens` tokens fills the GPU with its long-sequence kernel -- 1 when
  * tp_attn_heads already does (or the shard has no attention, or tokens < 1).

@@ -44,7 +44,7 @@ EXPORTED = (
     "tp_partial_reduce", "tp_status_string", "tp_last_error_detail",
     "tp_rowwise_split_input_partial", "tp_attn_heads_block", "tp_attn_merge",
     "tp_attn_heads_split", "tp_attn_split_hint", "tp_ulysses_seq_to_heads",
-    "tp_ulysses_heads_to_seq", "tp_block_shard_load",
+    "tp_ulysses_heads_to_seq", "tp_block_shard_load", "tp_attn_heads_block_split",
 )
 
 
@@ -108,6 +108,8 @@ def lib() -> ctypes.CDLL:
                                                      ctypes.c_int, vp]
         L.tp_attn_heads_block.argtypes = [vp, i64, vp, i64, i64, vp, i64, vp, i64, vp, i64, vp]
         L.tp_attn_heads_split.argtypes = [vp, i64, vp, i64, i32, vp, i64, i64, vp, i64, i64, vp]
+        L.tp_attn_heads_block_split.argtypes = [vp, i64, vp, i64, i64, vp, i64, i32, vp, i64, i64,
+                                                vp, i64, i64, vp]
         L.tp_ulysses_seq_to_heads.argtypes = [ctypes.POINTER(vp), i32, i64, i64, i64, i64, i32, i32,
                                               ctypes.c_int, vp, i64, vp]
         L.tp_ulysses_heads_to_seq.argtypes = [ctypes.POINTER(vp), i32, i64, i64, i64, i64, i32,
@@ -121,7 +123,8 @@ def lib() -> ctypes.CDLL:
         for f in ("tp_block_shard_create", "tp_block_shard_load", "tp_colwise_linear", "tp_colwise_qkv_up",
                   "tp_attn_heads", "tp_rowwise_linear_partial", "tp_partial_reduce",
                   "tp_rowwise_split_input_partial", "tp_attn_heads_block", "tp_attn_merge",
-                  "tp_attn_heads_split", "tp_ulysses_seq_to_heads", "tp_ulysses_heads_to_seq"):
+                  "tp_attn_heads_split", "tp_attn_heads_block_split", "tp_ulysses_seq_to_heads",
+                  "tp_ulysses_heads_to_seq"):
             getattr(L, f).restype = ctypes.c_int
         L.tp_status_string.argtypes = [ctypes.c_int]
         L.tp_status_string.restype = ctypes.c_char_p
@@ -336,6 +339,24 @@ def tp_attn_heads_block(shard: TpBlockShard, q_tokens: int, q_qkv, kv_tokens: in
     lp, ldl = _mat(lse, "lse", q_tokens, shard.heads_r, TP_F32)
     _check(lib().tp_attn_heads_block(shard.handle, q_tokens, qp, ldq, kv_tokens, kp, ldk, op, ldo,
                                      lp, ldl, _stream(stream)))
+
+
+def tp_attn_heads_block_split(shard: TpBlockShard, q_tokens: int, q_qkv, kv_tokens: int, kv_qkv,
+                              o_parts, lse_parts, stream=None) -> None:
+    """tp_attn_heads_block with the block's keys split len-wise into
+    o_parts.shape[0] ranges in one launch: o_parts fp32 [S, q_tokens, D_r],
+    lse_parts fp32 [S, q_tokens, H/P] (3-D device tensors; each part a 2-D
+    row-major slice)."""
+    S = o_parts.shape[0]
+    if o_parts.dim() != 3 or lse_parts.dim() != 3 or lse_parts.shape[0] != S:
+        raise ValueError("o_parts / lse_parts must be 3-D with one part per split")
+    qp, ldq = _mat(q_qkv, "q_qkv", q_tokens, shard.d_r, shard.dtype)
+    kp, ldk = _mat(kv_qkv, "kv_qkv", kv_tokens, 3 * shard.d_r, shard.dtype)
+    op, ldo = _mat(o_parts[0], "o_parts[0]", q_tokens, shard.d_r, TP_F32)
+    lp, ldl = _mat(lse_parts[0], "lse_parts[0]", q_tokens, shard.heads_r, TP_F32)
+    _check(lib().tp_attn_heads_block_split(shard.handle, q_tokens, qp, ldq, kv_tokens, kp, ldk, S,
+                                           op, ldo, o_parts.stride(0), lp, ldl, lse_parts.stride(0),
+                                           _stream(stream)))
 
 
 def tp_attn_heads_split(shard: TpBlockShard, tokens: int, qkv, o_parts, lse_parts,

@@ -599,10 +599,15 @@ TP_API tp_status tp_attn_heads(tp_block_shard* s, int64_t tokens, const void* qk
   return TP_OK;
 }
 
-TP_API tp_status tp_attn_heads_block(tp_block_shard* s, int64_t q_tokens, const void* q_qkv,
-                                     int64_t ldq, int64_t kv_tokens, const void* kv_qkv,
-                                     int64_t ldkv, float* o, int64_t ldo, float* lse,
-                                     int64_t ld_lse, void* stream) {
+// Queries of q_qkv against the keys and values of kv_qkv, the keys cut into
+// n_splits balanced ranges in one launch; range z writes its normalised fp32
+// output at o + z o_stride and its log-sum-exp at lse + z lse_stride.
+// tp_attn_heads_block (one range), tp_attn_heads_split (q_qkv == kv_qkv) and
+// tp_attn_heads_block_split share it.
+static tp_status attn_parts(tp_block_shard* s, int64_t q_tokens, const void* q_qkv, int64_t ldq,
+                            int64_t kv_tokens, const void* kv_qkv, int64_t ldkv, int32_t n_splits,
+                            float* o, int64_t ldo, int64_t o_stride, float* lse, int64_t ld_lse,
+                            int64_t lse_stride, void* stream) {
   tp_status st = check_shard(s);
   if (st != TP_OK) return st;
   if (!s->attn) return fail(TP_ERR_ARG, "shard has no attention layers");
@@ -610,72 +615,64 @@ TP_API tp_status tp_attn_heads_block(tp_block_shard* s, int64_t q_tokens, const 
   if (s->d != 128) return fail(TP_ERR_UNSUPPORTED, "attention is built for head_dim 128 only");
   if ((st = check_tokens(q_tokens)) != TP_OK) return st;
   if ((st = check_tokens(kv_tokens)) != TP_OK) return st;
-  if (q_tokens > 0 && kv_tokens < 1) return fail(TP_ERR_ARG, "kv_tokens must be >= 1");
+  if (n_splits < 1) return fail(TP_ERR_ARG, "n_splits (%d) < 1", n_splits);
+  if (n_splits > tpk::kMaxMergeParts)
+    return fail(TP_ERR_UNSUPPORTED, "n_splits (%d) > %d", n_splits, tpk::kMaxMergeParts);
   const int64_t Dr = s->Dr, Hr = s->Hr;
   if ((st = check_matrix("q_qkv", q_qkv, ldq, Dr, s->es)) != TP_OK) return st;
   if ((st = check_matrix("kv_qkv", kv_qkv, ldkv, 3 * Dr, s->es)) != TP_OK) return st;
   if ((st = check_matrix("o", o, ldo, Dr, sizeof(float))) != TP_OK) return st;
+  if (o_stride % 4) return fail(TP_ERR_ARG, "the o part stride must keep parts 16-byte aligned");
   if (!lse) return fail(TP_ERR_ARG, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(TP_ERR_ARG, "lse is not 4-byte aligned");
   if (ld_lse < Hr) return fail(TP_ERR_ARG, "ld_lse (%lld) < local heads %lld", (long long)ld_lse,
                                (long long)Hr);
   if (q_tokens == 0) return TP_OK;
+  if (kv_tokens < n_splits)
+    return fail(TP_ERR_ARG, n_splits == 1 ? "kv_tokens must be >= 1" : "fewer keys than key splits");
   const int64_t ob = span_bytes(q_tokens, ldo, Dr, sizeof(float));
   const int64_t lb = span_bytes(q_tokens, ld_lse, Hr, sizeof(float));
+  if (n_splits > 1 && (o_stride * (int64_t)sizeof(float) < ob || lse_stride * (int64_t)sizeof(float) < lb))
+    return fail(TP_ERR_ARG, "part strides shorter than one part (parts would overlap)");
+  const int64_t o_all = (n_splits - 1) * o_stride * (int64_t)sizeof(float) + ob;
+  const int64_t l_all = (n_splits - 1) * lse_stride * (int64_t)sizeof(float) + lb;
   const int64_t qb = span_bytes(q_tokens, ldq, Dr, s->es);
   const int64_t kb = span_bytes(kv_tokens, ldkv, 3 * Dr, s->es);
-  if (overlap(o, ob, q_qkv, qb) || overlap(o, ob, kv_qkv, kb) || overlap(lse, lb, q_qkv, qb) ||
-      overlap(lse, lb, kv_qkv, kb) || overlap(o, ob, lse, lb))
-    return fail(TP_ERR_ARG, "o / lse overlap each other or the inputs");
+  if (overlap(o, o_all, q_qkv, qb) || overlap(o, o_all, kv_qkv, kb) || overlap(lse, l_all, q_qkv, qb) ||
+      overlap(lse, l_all, kv_qkv, kb) || overlap(o, o_all, lse, l_all))
+    return fail(TP_ERR_ARG, "o / lse parts overlap each other or the inputs");
   const char* kv = static_cast<const char*>(kv_qkv);
   const tpk::AttnBlockArgs a{q_qkv, ldq, kv + Dr * s->es, kv + 2 * Dr * s->es, ldkv,
-                             (int)q_tokens, (int)kv_tokens, (int)Hr, o, ldo, lse, ld_lse, 1, 0, 0};
+                             (int)q_tokens, (int)kv_tokens, (int)Hr, o, ldo, lse, ld_lse,
+                             n_splits, o_stride, lse_stride};
   const hipError_t e = tpk::launch_attn_block_bf16_d128(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return TP_OK;
+}
+
+TP_API tp_status tp_attn_heads_block(tp_block_shard* s, int64_t q_tokens, const void* q_qkv,
+                                     int64_t ldq, int64_t kv_tokens, const void* kv_qkv,
+                                     int64_t ldkv, float* o, int64_t ldo, float* lse,
+                                     int64_t ld_lse, void* stream) {
+  return attn_parts(s, q_tokens, q_qkv, ldq, kv_tokens, kv_qkv, ldkv, 1, o, ldo, 0, lse, ld_lse, 0,
+                    stream);
+}
+
+TP_API tp_status tp_attn_heads_block_split(tp_block_shard* s, int64_t q_tokens, const void* q_qkv,
+                                           int64_t ldq, int64_t kv_tokens, const void* kv_qkv,
+                                           int64_t ldkv, int32_t n_splits, float* o_parts,
+                                           int64_t ldo, int64_t o_part_stride, float* lse_parts,
+                                           int64_t ld_lse, int64_t lse_part_stride, void* stream) {
+  return attn_parts(s, q_tokens, q_qkv, ldq, kv_tokens, kv_qkv, ldkv, n_splits, o_parts, ldo,
+                    o_part_stride, lse_parts, ld_lse, lse_part_stride, stream);
 }
 
 TP_API tp_status tp_attn_heads_split(tp_block_shard* s, int64_t tokens, const void* qkv,
                                      int64_t ldqkv, int32_t n_splits, float* o_parts, int64_t ldo,
                                      int64_t o_part_stride, float* lse_parts, int64_t ld_lse,
                                      int64_t lse_part_stride, void* stream) {
-  tp_status st = check_shard(s);
-  if (st != TP_OK) return st;
-  if (!s->attn) return fail(TP_ERR_ARG, "shard has no attention layers");
-  if (s->cfg.dtype != TP_BF16) return fail(TP_ERR_UNSUPPORTED, "attention is built for bf16 only");
-  if (s->d != 128) return fail(TP_ERR_UNSUPPORTED, "attention is built for head_dim 128 only");
-  if ((st = check_tokens(tokens)) != TP_OK) return st;
-  if (n_splits < 1) return fail(TP_ERR_ARG, "n_splits (%d) < 1", n_splits);
-  if (n_splits > tpk::kMaxMergeParts)
-    return fail(TP_ERR_UNSUPPORTED, "n_splits (%d) > %d", n_splits, tpk::kMaxMergeParts);
-  const int64_t Dr = s->Dr, Hr = s->Hr;
-  if ((st = check_matrix("qkv", qkv, ldqkv, 3 * Dr, s->es)) != TP_OK) return st;
-  if ((st = check_matrix("o_parts", o_parts, ldo, Dr, sizeof(float))) != TP_OK) return st;
-  if (o_part_stride % 4) return fail(TP_ERR_ARG, "o_part_stride must keep parts 16-byte aligned");
-  if (!lse_parts || (reinterpret_cast<uintptr_t>(lse_parts) & 3u))
-    return fail(TP_ERR_ARG, "lse_parts is NULL or not 4-byte aligned");
-  if (ld_lse < Hr) return fail(TP_ERR_ARG, "ld_lse (%lld) < local heads %lld", (long long)ld_lse,
-                               (long long)Hr);
-  if (tokens == 0) return TP_OK;
-  if (tokens < n_splits) return fail(TP_ERR_ARG, "fewer tokens than key splits");
-  const int64_t ob = span_bytes(tokens, ldo, Dr, sizeof(float));
-  const int64_t lb = span_bytes(tokens, ld_lse, Hr, sizeof(float));
-  if (n_splits > 1 && (o_part_stride * (int64_t)sizeof(float) < ob ||
-                       lse_part_stride * (int64_t)sizeof(float) < lb))
-    return fail(TP_ERR_ARG, "part strides shorter than one part (parts would overlap)");
-  const int64_t o_all = (n_splits - 1) * o_part_stride * (int64_t)sizeof(float) + ob;
-  const int64_t l_all = (n_splits - 1) * lse_part_stride * (int64_t)sizeof(float) + lb;
-  const int64_t qb = span_bytes(tokens, ldqkv, 3 * Dr, s->es);
-  if (overlap(o_parts, o_all, qkv, qb) || overlap(lse_parts, l_all, qkv, qb) ||
-      overlap(o_parts, o_all, lse_parts, l_all))
-    return fail(TP_ERR_ARG, "the parts overlap each other or qkv");
-  const char* base = static_cast<const char*>(qkv);
-  const tpk::AttnBlockArgs a{qkv, ldqkv, base + Dr * s->es, base + 2 * Dr * s->es, ldqkv,
-                             (int)tokens, (int)tokens, (int)Hr, o_parts, ldo, lse_parts, ld_lse,
-                             n_splits, o_part_stride, lse_part_stride};
-  const hipError_t e = tpk::launch_attn_block_bf16_d128(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
-  return TP_OK;
+  return attn_parts(s, tokens, qkv, ldqkv, tokens, qkv, ldqkv, n_splits, o_parts, ldo, o_part_stride,
+                    lse_parts, ld_lse, lse_part_stride, stream);
 }
 
 TP_API int32_t tp_attn_split_hint(const tp_block_shard* s, int64_t tokens) {

@@ -342,6 +342,8 @@ def test_block_attention_and_merge_validation_without_device(L):
 def test_split_attention_rejects_null_shard(L):
     vp = ctypes.c_void_p(0x10000)
     assert L.tp_attn_heads_split(None, 8, vp, 384, 2, vp, 128, 1024, vp, 1, 8, None) == tp.TP_ERR_ARG
+    assert L.tp_attn_heads_block_split(None, 8, vp, 384, 8, vp, 384, 2, vp, 128, 1024, vp, 1, 8,
+                                       None) == tp.TP_ERR_ARG
 
 
 def test_ulysses_validation_without_device(L):

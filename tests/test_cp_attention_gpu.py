@@ -1,10 +1,11 @@
 """GPU parity of context-parallel attention against the float64 oracle
 (Diffusers CP page, §Ring Attention): the block attention call (fp32
 normalised output and log-sum-exp) on both attention kernels, ragged and
-single-token blocks; the merge on seeded partials (1..16 parts, bf16 and
-fp32 output, optional lse); and Ring Attention simulated on one GPU -- every
-ring rank's steps plus the merge -- against attention over the whole
-sequence, also at the full 16384-token, 12-head rank shape on sampled rows.
+single-token blocks, and its key ranges split in one launch; the merge on
+seeded partials (1..16 parts, bf16 and fp32 output, optional lse); and Ring
+Attention simulated on one GPU -- every ring rank's steps (whole or as key
+ranges) plus the merge -- against attention over the whole sequence, also at
+the full 16384-token, 12-head rank shape on sampled rows.
 Tolerances: outputs 2e-2 of max|ref| (bf16 operands, bf16 P); log-sum-exp
 5e-3 absolute (the only rounding is the bf16 P summed in fp32, relative
 2^-9 per term, so ln of the sum moves by at most ~2e-3)."""
@@ -93,27 +94,33 @@ def test_merge_on_seeded_partials(n, out_dtype, with_lse):
         assert float(np.max(np.abs(H.as_f64(lse_out) - l_ref))) <= 1e-5
 
 
-def ring_on_one_gpu(s, qkv, T, R):
+def ring_on_one_gpu(s, qkv, T, R, splits=1):
     """Every ring rank c: step t attends its query chunk to K/V chunk
-    (c - t) mod R, then merges its R partials into its output chunk."""
+    (c - t) mod R -- with splits > 1 as that many key ranges in one launch --
+    then merges its R * splits partials into its output chunk."""
     n, Dr, Hr = T // R, s.d_r, s.heads_r
     out = torch.empty((T, Dr), dtype=torch.bfloat16, device="cuda")
-    o_parts = [torch.empty((n, Dr), dtype=torch.float32, device="cuda") for _ in range(R)]
-    l_parts = [torch.empty((n, Hr), dtype=torch.float32, device="cuda") for _ in range(R)]
+    o_parts = torch.empty((R, splits, n, Dr), dtype=torch.float32, device="cuda")
+    l_parts = torch.empty((R, splits, n, Hr), dtype=torch.float32, device="cuda")
     for c in range(R):
         for t in range(R):
             j = (c - t) % R
-            tp.tp_attn_heads_block(s, n, qkv[c * n:(c + 1) * n], n, qkv[j * n:(j + 1) * n],
-                                   o_parts[t], l_parts[t])
-        tp.tp_attn_merge(o_parts, l_parts, out[c * n:(c + 1) * n], Hr, 128)
+            q, kv = qkv[c * n:(c + 1) * n], qkv[j * n:(j + 1) * n]
+            if splits == 1:
+                tp.tp_attn_heads_block(s, n, q, n, kv, o_parts[t, 0], l_parts[t, 0])
+            else:
+                tp.tp_attn_heads_block_split(s, n, q, n, kv, o_parts[t], l_parts[t])
+        tp.tp_attn_merge(list(o_parts.flatten(0, 1)), list(l_parts.flatten(0, 1)),
+                         out[c * n:(c + 1) * n], Hr, 128)
     return out
 
 
-@pytest.mark.parametrize("T,heads_r,R", [(4096, 2, 4), (1200, 3, 3), (2048, 2, 1)])
-def test_ring_attention_equals_attention(T, heads_r, R):
+@pytest.mark.parametrize("T,heads_r,R,splits", [(4096, 2, 4, 1), (1200, 3, 3, 1), (2048, 2, 1, 1),
+                                                (4096, 2, 4, 2), (1200, 3, 3, 4)])
+def test_ring_attention_equals_attention(T, heads_r, R, splits):
     s = attn_shard(heads_r)
     qv, qd = seeded_qkv(T, heads_r, seed=60)
-    out = ring_on_one_gpu(s, qd, T, R)
+    out = ring_on_one_gpu(s, qd, T, R, splits)
     mono = torch.empty((T, s.d_r), dtype=torch.bfloat16, device="cuda")
     tp.tp_attn_heads(s, T, qd, mono)
     torch.cuda.synchronize()
@@ -121,18 +128,20 @@ def test_ring_attention_equals_attention(T, heads_r, R):
     ref = O.to_bf16_rne(O.attention_heads(q, k, v, heads_r, 128))
     e = H.rel_err(H.as_f64(out), ref)
     e_m = H.rel_err(H.as_f64(out), H.as_f64(mono))
-    say(f"ring T={T} heads={heads_r} R={R}: vs oracle {e:.2e}, vs one-call attention {e_m:.2e}")
+    say(f"ring T={T} heads={heads_r} R={R} splits={splits}: vs oracle {e:.2e}, vs one call {e_m:.2e}")
     assert e <= H.TOL["bf16"] and e_m <= H.TOL["bf16"]
     torch.cuda.synchronize()
     s.close()
 
 
-def test_ring_attention_full_rank_shape():
-    """16384 tokens, 12 local heads, ring of 4: sampled rows of two heads."""
+@pytest.mark.parametrize("splits", [1, 2])
+def test_ring_attention_full_rank_shape(splits):
+    """16384 tokens, 12 local heads, ring of 4 (steps whole or as two key
+    ranges): sampled rows of two heads."""
     T, heads_r, R = 16384, 12, 4
     s = attn_shard(heads_r, P=4)
     qv, qd = seeded_qkv(T, heads_r, seed=61)
-    out = ring_on_one_gpu(s, qd, T, R)
+    out = ring_on_one_gpu(s, qd, T, R, splits)
     torch.cuda.synchronize()
     rows = tp_inputs.sample_rows(T, 32, seed=7)
     Dr = s.d_r
@@ -141,7 +150,7 @@ def test_ring_attention_full_rank_shape():
         ref = O.to_bf16_rne(O.attention_rows(qv[rows, c], qv[:, Dr + j * 128:Dr + (j + 1) * 128],
                                              qv[:, 2 * Dr + j * 128:2 * Dr + (j + 1) * 128], 1, 128))
         e = H.rel_err(H.as_f64(out[rows, c]), ref)
-        say(f"ring T=16384 R=4 head {j}: {e:.2e}")
+        say(f"ring T=16384 R=4 splits={splits} head {j}: {e:.2e}")
         assert e <= H.TOL["bf16"]
     s.close()
 
@@ -177,6 +186,40 @@ def test_single_launch_key_split_then_merge(T, heads_r, S):
     assert e <= H.TOL["bf16"] and e_m <= H.TOL["bf16"]
     if S == 1:
         assert torch.equal(out, mono)
+    torch.cuda.synchronize()
+    s.close()
+
+
+@pytest.mark.parametrize("Tq,Tkv,heads_r,S", [(1152, 1152, 6, 2), (777, 333, 2, 3), (65, 4000, 3, 4),
+                                              (8192, 1000, 6, 2), (300, 16, 1, 16), (40, 50, 2, 1)])
+def test_block_key_split_parts(Tq, Tkv, heads_r, S):
+    """Queries of one buffer against a key block of another, the block's
+    keys cut into S ranges in one launch: each part against the oracle's
+    block attention over its keys; one range is bitwise the block call."""
+    s = attn_shard(heads_r)
+    Dr = s.d_r
+    qv, qd = seeded_qkv(Tq, heads_r, seed=90)
+    kv, kd = seeded_qkv(Tkv, heads_r, seed=91)
+    op = torch.empty((S, Tq, Dr), dtype=torch.float32, device="cuda")
+    lp = torch.empty((S, Tq, heads_r), dtype=torch.float32, device="cuda")
+    tp.tp_attn_heads_block_split(s, Tq, qd, Tkv, kd, op, lp)
+    torch.cuda.synchronize()
+    q = qkv_parts(qv, Dr)[0]
+    _, k, v = qkv_parts(kv, Dr)
+    rows = tp_inputs.sample_rows(Tq, 48, seed=9) if Tq > 512 else np.arange(Tq)
+    for z in range(S):
+        a, b = (z * Tkv) // S, ((z + 1) * Tkv) // S
+        o_ref, l_ref = O.attention_block(q[rows], k[a:b], v[a:b], heads_r, 128)
+        e_o = H.rel_err(H.as_f64(op[z][rows]), o_ref)
+        e_l = float(np.max(np.abs(H.as_f64(lp[z][rows]) - l_ref)))
+        assert e_o <= H.TOL["bf16"] and e_l <= LSE_ATOL, f"part {z}: o {e_o:.2e} lse {e_l:.2e}"
+    say(f"block split Tq={Tq} Tkv={Tkv} heads={heads_r} S={S}: {S} parts within tolerance")
+    if S == 1:
+        o1 = torch.empty((Tq, Dr), dtype=torch.float32, device="cuda")
+        l1 = torch.empty((Tq, heads_r), dtype=torch.float32, device="cuda")
+        tp.tp_attn_heads_block(s, Tq, qd, Tkv, kd, o1, l1)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, op[0]) and torch.equal(l1, lp[0])
     torch.cuda.synchronize()
     s.close()
 
