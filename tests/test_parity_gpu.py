@@ -193,6 +193,23 @@ def test_large_rowwise_store_and_accumulate_paths():
     close_all(shards)
 
 
+@pytest.mark.parametrize("w", [
+    # up-projection N = 8288 = 32 x 256 + 96: 9 x 33 tiles on the 8-wave kernel,
+    # the last tile column partly past N
+    Workload("ragged_up_T2125_D1024_F8288_P1", 2125, 1024, 0, 0, 8288, 1, "bf16"),
+    # down-projection N = 8352 = 32 x 256 + 160 on the 8-wave kernel; the
+    # up-projection's K = 8352 is not a multiple of 64 (zero-filled tail)
+    Workload("ragged_down_T2125_D8352_F1024_P1", 2125, 8352, 0, 0, 1024, 1, "bf16"),
+], ids=lambda w: w.name)
+def test_large_ragged_n_paths(w):
+    inp = tp_inputs.make_inputs(w, seed=23)
+    ranks, y_ref = full_oracle(w, inp)
+    shards, outs, y = run_all_ranks(w, inp)
+    check_rank(w, outs[0], ranks[0], H.TOL["bf16"], w.name)
+    assert H.rel_err(H.as_f64(y), y_ref) <= H.TOL["bf16"]
+    close_all(shards)
+
+
 @pytest.mark.parametrize("T,heads", [(5500, 24), (4608, 6)])
 def test_attention_long_sequences_both_workgroup_shapes(T, heads):
     """T=5500 x 24 heads takes the 256-query (8-wave) workgroups with a
