@@ -224,6 +224,39 @@ def test_block_key_split_parts(Tq, Tkv, heads_r, S):
     s.close()
 
 
+def test_block_key_split_errors():
+    """More key ranges than keys, more than 16 ranges, and overlapping parts
+    are rejected before any launch; no queries is a no-op."""
+    s = attn_shard(2)
+    Dr = s.d_r
+    _, qd = seeded_qkv(40, 2, seed=92)
+    _, kd = seeded_qkv(3, 2, seed=93)
+
+    def parts(S, T=40):
+        return (torch.empty((S, T, Dr), dtype=torch.float32, device="cuda"),
+                torch.empty((S, T, 2), dtype=torch.float32, device="cuda"))
+
+    op, lp = parts(4)
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_attn_heads_block_split(s, 40, qd, 3, kd, op, lp)      # 4 ranges over 3 keys
+    assert e.value.status == tp.TP_ERR_ARG
+    op, lp = parts(17)
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_attn_heads_block_split(s, 40, qd, 3, kd, op, lp)
+    assert e.value.status == tp.TP_ERR_UNSUPPORTED
+    o_all = torch.empty((2 * 40 * Dr,), dtype=torch.float32, device="cuda")
+    l_all = torch.empty((2 * 40 * 2,), dtype=torch.float32, device="cuda")
+    short = o_all.as_strided((2, 40, Dr), (40 * Dr - 4, Dr, 1))    # part 1 starts inside part 0
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_attn_heads_block_split(s, 40, qd, 3, kd, short, l_all.view(2, 40, 2))
+    assert e.value.status == tp.TP_ERR_ARG
+    op, lp = parts(5)
+    tp.tp_attn_heads_block_split(s, 0, qd, 3, kd, op, lp)           # no queries: nothing to do,
+                                                                     # even with 5 ranges over 3 keys
+    torch.cuda.synchronize()
+    s.close()
+
+
 def _dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
