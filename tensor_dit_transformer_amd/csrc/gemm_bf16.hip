@@ -48,29 +48,97 @@ __device__ __forceinline__ int swizzle(int row, int kc) {
 }
 
 // GELU, tanh form: 0.5 u (1 + tanh(z)) = u * sigmoid(2 z) = u / (1 + exp(-2 z)),
-// z = sqrt(2/pi) (u + 0.044715 u^3).
+// z = sqrt(2/pi) (u + 0.044715 u^3).  With the constants folded,
+// exp(-2 z) = exp2(u (k1 + k2 u^2)), k1 = -2 sqrt(2/pi) log2(e),
+// k2 = 0.044715 k1: three FMA-class operations, one exp2 and one hardware
+// reciprocal (1 ulp), far below the bf16 rounding of the result.
 __device__ __forceinline__ float gelu_tanh(float u) {
-  const float c = 0.7978845608028654f;
-  const float z = c * fmaf(0.044715f * u, u * u, u);
-  return u / (1.0f + __expf(-2.0f * z));
+  const float k1 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+  const float k2 = 0.044715f * k1;
+  const float t = u * fmaf(k2, u * u, k1);
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
-// SiLU: u * sigmoid(u) = u / (1 + exp(-u)).
-__device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
+// SiLU: u * sigmoid(u) = u / (1 + exp(-u)) = u / (1 + exp2(-log2(e) u)).
+__device__ __forceinline__ float silu(float u) {
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * u));
+}
+
+// One 32-column block of a wave's accumulators: rows r(i, e) = 32 i + 8 (e / 4)
+// + (e % 4) past the lane's first row (lane: column lane & 31, first row
+// 4 (lane >> 5)), i.e. row steps +1, +1, +1, +5 repeating.  `p` points at
+// the lane's first row and advances by the row stride, so no element needs
+// a 64-bit multiply; `rows_left` (ROWCHECK only) bounds the rows stored.
+enum class Mode : int { PLAIN, GELU, GLU };
+
+template <OutKind KIND, Mode MODE, bool ROWCHECK, int TM, int TN>
+__device__ __forceinline__ void store_block(const f32x16 (&acc)[TM][TN], int j, char* p,
+                                            int64_t stride, int rows_left, float bias,
+                                            float bias_up) {
+  constexpr int ES = KIND == OutKind::BF16 ? 2 : 4;
+  const int64_t stride5 = 5 * stride;
+  if constexpr (KIND == OutKind::F32_ACC) {
+    // read the 16 rows of tile i first, then add and store: one wait per tile
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      float old[16];
+      char* q = p;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 32 * i + 8 * (e >> 2) + (e & 3);
+        old[e] = (!ROWCHECK || r < rows_left) ? *reinterpret_cast<const float*>(q) : 0.0f;
+        q += (e & 3) == 3 ? stride5 : stride;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 32 * i + 8 * (e >> 2) + (e & 3);
+        if (!ROWCHECK || r < rows_left) *reinterpret_cast<float*>(p) = old[e] + acc[i][j][e];
+        p += (e & 3) == 3 ? stride5 : stride;
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = 32 * i + 8 * (e >> 2) + (e & 3);
+      // keeps each row test at its store: hoisted, the 64 tests' masks would
+      // take registers the accumulators need
+      if constexpr (ROWCHECK) asm volatile("" : "+v"(rows_left));
+      if (!ROWCHECK || r < rows_left) {
+        float v = acc[i][j][e] + bias;
+        if constexpr (MODE == Mode::GLU) v = silu(v) * (acc[i][j | 1][e] + bias_up);
+        if constexpr (MODE == Mode::GELU) v = gelu_tanh(v);
+        if constexpr (ES == 2)
+          *reinterpret_cast<bf16*>(p) = static_cast<bf16>(v);
+        else
+          *reinterpret_cast<float*>(p) = v;
+      }
+      p += (e & 3) == 3 ? stride5 : stride;
+    }
+  }
+}
 
 // Writes one wave's TM x TN accumulator tiles: tile (i, j) holds C rows
 // row0 + 32 i + [0, 32) and columns col0 + 32 j + [0, 32) in the 32x32 MFMA
 // layout (lane: column lane & 31, rows 8 (e / 4) + 4 (lane >> 5) + (e % 4)).
-// col0 is a multiple of 64, so under SWIGLU tile j (even) is a gate block and
-// tile j + 1 its up block: the pair is combined in registers and stored as
-// 32 output columns.
-template <OutKind KIND, int TM, int TN>
+// Each store instruction writes 32 adjacent columns of two rows.  With
+// FULL_ROWS_FAST, a wave whose rows all lie below M (row0 is wave-uniform)
+// takes a copy without the row test (the 4-wave kernels, whose accumulators
+// fill the register file, keep the one tested copy).  col0 is a multiple of
+// 64, so under SWIGLU tile j (even) is a gate block and tile j + 1 its up
+// block: the pair is combined in registers and stored as 32 output columns.
+template <OutKind KIND, int TM, int TN, bool FULL_ROWS_FAST>
 __device__ __forceinline__ void store_tiles(const f32x16 (&acc)[TM][TN], const GemmProblem& p,
                                             const GemmEpilogue& ep, int row0, int col0,
                                             int lane) {
   static_assert(TN % 2 == 0, "SwiGLU pairs tile j with tile j + 1");
+  constexpr int ES = KIND == OutKind::BF16 ? 2 : 4;
   const int col_l = lane & 31;
   const int row_l = 4 * (lane >> 5);
+  const int rows_left = p.M - row0 - row_l;           // rows of this lane's half below M
+  const bool rows_full = row0 + 32 * TM <= p.M;       // wave-uniform
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int col = col0 + 32 * j + col_l;
@@ -90,29 +158,24 @@ __device__ __forceinline__ void store_tiles(const f32x16 (&acc)[TM][TN], const G
     const bool second = ocol >= ep.split;
     if (second) ocol -= ep.split;
     const int64_t ld = second ? ep.ld1 : ep.ld0;
-    void* out = second ? ep.out1 : ep.out0;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = row0 + 32 * i + 8 * (e >> 2) + row_l + (e & 3);
-        if (row >= p.M) continue;
-        const int64_t off = (int64_t)row * ld + ocol;
-        float v = acc[i][j][e];
-        if constexpr (KIND == OutKind::F32_ACC) {
-          float* o = static_cast<float*>(out) + off;
-          *o = *o + v;
-        } else {
-          v += bias;
-          if (glu) v = silu(v) * (acc[i][j | 1][e] + bias_up);
-          else if (gelu) v = gelu_tanh(v);
-          if constexpr (KIND == OutKind::BF16)
-            static_cast<bf16*>(out)[off] = static_cast<bf16>(v);
-          else
-            static_cast<float*>(out)[off] = v;
-        }
-      }
+    char* base = static_cast<char*>(second ? ep.out1 : ep.out0) +
+                 ((int64_t)(row0 + row_l) * ld + ocol) * ES;
+    const int64_t stride = ld * ES;
+#define TPK_STORE(MODE_)                                                                    \
+  do {                                                                                       \
+    if (FULL_ROWS_FAST && rows_full)                                                         \
+      store_block<KIND, MODE_, false>(acc, j, base, stride, rows_left, bias, bias_up);       \
+    else                                                                                     \
+      store_block<KIND, MODE_, true>(acc, j, base, stride, rows_left, bias, bias_up);        \
+  } while (0)
+    if constexpr (KIND == OutKind::F32_ACC) {
+      TPK_STORE(Mode::PLAIN);
+    } else {
+      if (glu) TPK_STORE(Mode::GLU);
+      else if (gelu) TPK_STORE(Mode::GELU);
+      else TPK_STORE(Mode::PLAIN);
     }
+#undef TPK_STORE
   }
 }
 
@@ -224,7 +287,7 @@ gemm_bf16_nt(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
     __syncthreads();
   }
 
-  store_tiles<KIND, TM, TN>(acc, p, ep, m0 + wm * WTM, n0 + wn * WTN, lane);
+  store_tiles<KIND, TM, TN, false>(acc, p, ep, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
 // 256x256 tile, 8 waves (2 per SIMD) in a ping-pong schedule; each wave owns
@@ -392,7 +455,7 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
     wg_barrier();
   }
 
-  store_tiles<KIND, TM, TN>(acc, p, ep, m0 + 128 * g, n0 + 64 * q, lane);
+  store_tiles<KIND, TM, TN, true>(acc, p, ep, m0 + 128 * g, n0 + 64 * q, lane);
 }
 
 hipError_t launch_256x256_8w(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
