@@ -178,6 +178,21 @@ def test_large_fused_colwise_and_attention_paths():
     close_all(shards)
 
 
+def test_large_ragged_rows_in_the_second_wave_group():
+    # T = 2248 = 8 x 256 + 200: in the last tile row of the 8-wave GEMM the
+    # first wave group (rows 0-127) is whole and takes the untested store
+    # copy, the second (rows 128-199 of 256) stores only its rows below M.
+    # Fused colwise (bf16 + GELU, split output) and packed rowwise (fp32).
+    w = Workload("big_fused_T2248_D1024_H8_F16384_P2", 2248, 1024, 8, 128, 16384, 2, "bf16")
+    inp = tp_inputs.make_inputs(w, seed=24)
+    ranks, y_ref = full_oracle(w, inp)
+    shards, outs, y = run_all_ranks(w, inp)
+    for r, (buf, ref) in enumerate(zip(outs, ranks)):
+        check_rank(w, buf, ref, H.TOL["bf16"], f"T2248 rank {r}")
+    assert H.rel_err(H.as_f64(y), y_ref) <= H.TOL["bf16"]
+    close_all(shards)
+
+
 def test_large_rowwise_store_and_accumulate_paths():
     # MLP-only, P = 1, hidden 8192: the down projection is N = 8192 -> 9 x 32 tiles
     w = Workload("big_down_T2125_D8192_F1024_P1", 2125, 8192, 0, 0, 1024, 1, "bf16")
