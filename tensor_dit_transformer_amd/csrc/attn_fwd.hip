@@ -84,7 +84,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Operands of one launch: head j's Q, K, V at columns j*128 of q, k, v.
-// Key split z = blockIdx.z of kv_splits covers keys
+// Key split z of kv_splits (the grid's z index; the pipelined kernel takes
+// it from its work order) covers keys
 // [floor(z Tkv / kv_splits), floor((z+1) Tkv / kv_splits)) -- never empty when
 // Tkv >= kv_splits -- and writes its partial result at o + z o_split,
 // lse + z lse_split.
@@ -105,14 +106,13 @@ struct AttnIO {
 // 32 t + 8 (e / 4) + 4 half + (e % 4)): normalise by the row sum, store bf16,
 // or fp32 plus the row's log-sum-exp.
 template <bool LSE>
-__device__ __forceinline__ void store_rows(const AttnIO& a, int head, int q, int half,
+__device__ __forceinline__ void store_rows(const AttnIO& a, int head, int z, int q, int half,
                                            const f32x16 (&acc_o)[kD / 32], float m_ref,
                                            float l_run) {
   const float l_tot = l_run + other_half(l_run, half);
   const float inv = 1.0f / l_tot;
   if (q >= a.Tq) return;
   if constexpr (LSE) {
-    const int z = blockIdx.z;
     float* orow = static_cast<float*>(a.o) + z * a.o_split + (int64_t)q * a.ldo + head * kD;
 #pragma unroll
     for (int t = 0; t < kD / 32; ++t)
@@ -326,7 +326,7 @@ attn_fwd_bf16_d128(AttnIO a) {
     __syncthreads();  // tile kt + 1 landed (this wave's DMA) and every wave is done with buf
   }
 
-  store_rows<LSE>(a, head, q0 + l32, half, acc_o, m_ref, l_run);
+  store_rows<LSE>(a, head, blockIdx.z, q0 + l32, half, acc_o, m_ref, l_run);
 }
 
 // ---------------------------------------------------------------------------
@@ -362,10 +362,19 @@ attn_fwd_pipe(AttnIO io) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int head = blockIdx.y;
-  const int q0 = blockIdx.x * BQ + wave * 32 * NQ;
-  const int k0 = (int)((int64_t)blockIdx.z * io.Tkv / io.kv_splits);
-  const int T = (int)((int64_t)(blockIdx.z + 1) * io.Tkv / io.kv_splits) - k0;   // >= 1
+  // Work order: workgroups are dispatched round-robin over the 8 XCDs (own
+  // L2 each) in linear id order, so the linear id is renumbered to give each
+  // XCD a contiguous run of (query block, head, key split) items, query block
+  // fastest: the workgroups an XCD runs at once are query blocks of one or
+  // two heads and share their K/V tiles in its L2.
+  const int nqb = gridDim.x, nh = gridDim.y, nb = nqb * nh * gridDim.z;
+  const int lin = blockIdx.x + nqb * (blockIdx.y + nh * blockIdx.z);
+  const int xcd = lin & 7, per = nb >> 3, rem = nb & 7;
+  const int w = xcd * per + min(xcd, rem) + (lin >> 3);
+  const int qb = w % nqb, head = (w / nqb) % nh, z = w / (nqb * nh);
+  const int q0 = qb * BQ + wave * 32 * NQ;
+  const int k0 = (int)((int64_t)z * io.Tkv / io.kv_splits);
+  const int T = (int)((int64_t)(z + 1) * io.Tkv / io.kv_splits) - k0;   // >= 1
   const bf16* Qg = io.q + head * kD;
   const bf16* Kg = io.k + head * kD + (int64_t)k0 * io.ldkv;
   const bf16* Vg = io.v + head * kD + (int64_t)k0 * io.ldkv;
@@ -563,7 +572,7 @@ attn_fwd_pipe(AttnIO io) {
 
 #pragma unroll
   for (int a = 0; a < NQ; ++a)
-    store_rows<LSE>(io, head, q0 + 32 * a + l32, half, acc_o[a], m_ref[a], l_run[a]);
+    store_rows<LSE>(io, head, z, q0 + 32 * a + l32, half, acc_o[a], m_ref[a], l_run[a]);
 }
 
 }  // namespace
