@@ -290,15 +290,17 @@ gemm_bf16_nt(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
   store_tiles<KIND, TM, TN, false>(acc, p, ep, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
-// 256x256 tile, 8 waves (2 per SIMD) in a ping-pong schedule; each wave owns
-// a 128x64 block of C.  A and B tiles go global -> LDS directly
-// (global_load_lds_dwordx4: each wave instruction fills 1 KB = 8 tile rows),
-// so no registers stage them and no ds_write is issued; K % 64 == 0 (no
-// zero-fill on this path).  Waves 0-3 (group 0) own C rows 0-127 and waves
-// 4-7 (group 1) rows 128-255.  The groups run one phase apart, separated by
-// workgroup barriers: while one group reads a whole K tile of operand
-// fragments from LDS into registers (24 x 16 bytes per lane), the other
-// issues the 32 MFMAs of the tile it read in the previous phase.  Phase 2k:
+// 256x256 tile (TM = 4; TM = 3 gives 192x256 for problems that one round
+// of 256-row tiles would leave CUs idle in), 8 waves (2 per SIMD) in a
+// ping-pong schedule; each wave owns a (32 TM)x64 block of C.  A and B tiles
+// go global -> LDS directly (global_load_lds_dwordx4: each wave instruction
+// fills 1 KB = 8 tile rows), so no registers stage them and no ds_write is
+// issued; K % 64 == 0 (no zero-fill on this path).  Waves 0-3 (group 0) own
+// C rows [0, 32 TM) and waves 4-7 (group 1) rows [32 TM, 64 TM).  The groups
+// run one phase apart, separated by workgroup barriers: while one group reads
+// a whole K tile of operand fragments from LDS into registers
+// ((TM + 2) x 4 x 16 bytes per lane), the other issues the 8 TM MFMAs of the
+// tile it read in the previous phase.  Phase 2k:
 // group 0 reads tile k, group 1 multiplies tile k-1; phase 2k+1: group 0
 // multiplies tile k, group 1 reads tile k.
 //
@@ -306,7 +308,7 @@ gemm_bf16_nt(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
 // loads are issued only in read phases: group 0, after reading tile k in
 // phase 2k, fetches the whole B tile k+1; group 1, after reading tile k in
 // phase 2k+1, fetches the whole A tile k+2.  A has three LDS stages and B
-// two (96 + 64 KB): the B tile k+1 goes into the stage of tile k-1 (last
+// two (96 + 64 KB at TM = 4): the B tile k+1 goes into the stage of tile k-1 (last
 // read in phase 2k-1) and is waited for by group 0 at the end of phase 2k+1;
 // the A tile k+2 goes into the stage of tile k-1 too and is waited for by
 // group 1 at the end of phase 2k+3.  Tile 0 and A tile 1 are fetched before
@@ -323,23 +325,28 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// all but the newest 8 loads of this wave have landed
-__device__ __forceinline__ void wait_vmem_keep8() {
+// all but the newest N loads of this wave have landed
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep() {
+  static_assert(N == 8 || N == 6, "instantiated counts");
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <OutKind KIND, int GROUP_SHIFT>
+template <OutKind KIND, int TM>
 __global__ void __launch_bounds__(512)
 gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
-  constexpr int BM = 256, BN = 256;
-  constexpr int TM = 4, TN = 2;                 // 128 x 64 per wave
+  static_assert(TM == 4 || TM == 3, "256- or 192-row tiles");
+  constexpr int BM = 64 * TM, BN = 256;
+  constexpr int TN = 2;                         // 32 TM x 64 per wave
   constexpr int KS = kBK / 16;                  // 4 MFMA k-steps per tile
   constexpr int A_STAGE = BM * kRowChunks;      // 16-byte chunks per A stage
   constexpr int B_STAGE = BN * kRowChunks;
+  constexpr int A_LOADS = 2 * TM;               // 8-row loads per wave per A tile
 
-  __shared__ u32x4 smem[3 * A_STAGE + 2 * B_STAGE];   // 160 KB
+  __shared__ u32x4 smem[3 * A_STAGE + 2 * B_STAGE];   // 160 KB (136 KB at BM 192)
 
   const int nb = gridDim.x, bid = blockIdx.x;
   const int xcd = bid & 7, per = nb >> 3, rem = nb & 7;
@@ -353,35 +360,35 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  // group of a wave: GROUP_SHIFT 2 -> waves 0-3 / 4-7, 0 -> even / odd waves
-  const int g = GROUP_SHIFT == 2 ? (wave >> 2) : (wave & 1);
-  const int q = GROUP_SHIFT == 2 ? (wave & 3) : (wave >> 1);
+  const int g = wave >> 2, q = wave & 3;   // wave group (0: waves 0-3), place in it
   const bf16* __restrict__ A = static_cast<const bf16*>(p.A);
   const bf16* __restrict__ B = static_cast<const bf16*>(p.B);
 
   auto stage_a = [&](int kt) { return smem + (kt % 3) * A_STAGE; };
   auto stage_b = [&](int kt) { return smem + 3 * A_STAGE + (kt & 1) * B_STAGE; };
 
-  // global -> LDS: wave q of the fetching group covers operand rows
-  // 64 q + 8 i + (lane >> 3), i = 0..7, one instruction each; the swizzle
-  // of a row depends only on i & 1.
-  const int row0 = 64 * q + (lane >> 3);
-  const int kc_even = swizzle(row0, lane & 7) * 8, kc_odd = swizzle(row0 + 8, lane & 7) * 8;
-  auto fetch = [&](const bf16* __restrict__ src, int ld, int first_row, int rows, int kt, u32x4* dst) {
+  // global -> LDS: wave q of the fetching group covers the operand rows
+  // 8 n q + 8 i + (lane >> 3), i = 0..n-1 (n = 8 for B, 2 TM for A), one
+  // instruction each; 8 n q is a multiple of 16, so the swizzle of a row
+  // depends only on i & 1.
+  const int kc_even = swizzle(lane >> 3, lane & 7) * 8, kc_odd = swizzle(8 + (lane >> 3), lane & 7) * 8;
+  auto fetch = [&](const bf16* __restrict__ src, int ld, int first_row, int rows, int kt, u32x4* dst,
+                   int n) {
     const int k = kt * kBK;
+    const int wrow = 8 * n * q;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < n; ++i) {
       const int kc = (i & 1) ? kc_odd : kc_even;
-      const int off = min(first_row + row0 + 8 * i, rows - 1) * ld + kc + k;
+      const int off = min(first_row + wrow + 8 * i + (lane >> 3), rows - 1) * ld + kc + k;
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1)))*)(src + off),
-          (void __attribute__((address_space(3)))*)(dst + (64 * q + 8 * i) * kRowChunks), 16, 0, 0);
+          (void __attribute__((address_space(3)))*)(dst + (wrow + 8 * i) * kRowChunks), 16, 0, 0);
     }
   };
-  auto fetch_a = [&](int kt) { fetch(A, (int)p.lda, m0, p.M, kt, stage_a(kt)); };
-  auto fetch_b = [&](int kt) { fetch(B, (int)p.ldb, n0, p.N, kt, stage_b(kt)); };
+  auto fetch_a = [&](int kt) { fetch(A, (int)p.lda, m0, p.M, kt, stage_a(kt), A_LOADS); };
+  auto fetch_b = [&](int kt) { fetch(B, (int)p.ldb, n0, p.N, kt, stage_b(kt), 8); };
 
-  const int a_row = 128 * g + (lane & 31);
+  const int a_row = 32 * TM * g + (lane & 31);
   const int b_row = 64 * q + (lane & 31);
   const int khalf = lane >> 5;
   bf16x8 fa[KS][TM], fb[KS][TN];
@@ -445,7 +452,7 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
       __builtin_amdgcn_sched_barrier(0);
       if (kt + 2 < nk) {
         fetch_a(kt + 2);
-        wait_vmem_keep8();                // A tile kt + 1
+        wait_vmem_keep<A_LOADS>();        // A tile kt + 1
       } else {
         wait_vmem();
       }
@@ -455,22 +462,24 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
     wg_barrier();
   }
 
-  store_tiles<KIND, TM, TN, true>(acc, p, ep, m0 + 128 * g, n0 + 64 * q, lane);
+  store_tiles<KIND, TM, TN, true>(acc, p, ep, m0 + 32 * TM * g, n0 + 64 * q, lane);
 }
 
-hipError_t launch_256x256_8w(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
-                             hipStream_t stream) {
-  const int tm = (p.M + 255) / 256, tn = (p.N + 255) / 256;
+// The 8-wave kernel with TM * 64-row tiles (TM 4: 256 x 256, TM 3: 192 x 256).
+template <int TM>
+hipError_t launch_8w(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
+                     hipStream_t stream) {
+  const int tm = (p.M + 64 * TM - 1) / (64 * TM), tn = (p.N + 255) / 256;
   const dim3 grid(tm * tn), block(512);
   switch (kind) {
     case OutKind::BF16:
-      hipLaunchKernelGGL((gemm_bf16_nt_pingpong<OutKind::BF16, 2>), grid, block, 0, stream, p, ep, tm, tn);
+      hipLaunchKernelGGL((gemm_bf16_nt_pingpong<OutKind::BF16, TM>), grid, block, 0, stream, p, ep, tm, tn);
       break;
     case OutKind::F32_STORE:
-      hipLaunchKernelGGL((gemm_bf16_nt_pingpong<OutKind::F32_STORE, 2>), grid, block, 0, stream, p, ep, tm, tn);
+      hipLaunchKernelGGL((gemm_bf16_nt_pingpong<OutKind::F32_STORE, TM>), grid, block, 0, stream, p, ep, tm, tn);
       break;
     case OutKind::F32_ACC:
-      hipLaunchKernelGGL((gemm_bf16_nt_pingpong<OutKind::F32_ACC, 2>), grid, block, 0, stream, p, ep, tm, tn);
+      hipLaunchKernelGGL((gemm_bf16_nt_pingpong<OutKind::F32_ACC, TM>), grid, block, 0, stream, p, ep, tm, tn);
       break;
   }
   return hipGetLastError();
@@ -503,14 +512,21 @@ hipError_t launch_tile(const GemmProblem& p, const GemmEpilogue& ep, OutKind kin
 
 hipError_t launch_gemm_bf16(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
                             hipStream_t stream) {
-  // 256x256 tiles when they fill at least half the 256 CUs (the 8-wave
-  // kernel beats four times as many 128x128 tiles even then); 128x128
-  // otherwise.
+  // 256x256 tiles (or 192x256, below) when they fill at least half the 256
+  // CUs (the 8-wave kernel beats four times as many 128x128 tiles even
+  // then); 128x128 otherwise.
   const long big = (long)((p.M + 255) / 256) * ((p.N + 255) / 256);
   // the 8-wave kernel indexes operands with 32-bit element offsets
   const bool fits32 = (int64_t)p.M * p.lda < ((int64_t)1 << 31) &&
                       (int64_t)p.N * p.ldb < ((int64_t)1 << 31);
-  if (big >= 128 && p.K % kBK == 0 && fits32) return launch_256x256_8w(p, ep, kind, stream);
+  if (big >= 128 && p.K % kBK == 0 && fits32) {
+    // One partial round of 256-row tiles leaves CUs idle (e.g. 162 tiles at
+    // M = 4608, N = 2304); if 192-row tiles still fit in one round, every
+    // busy CU has 3/4 of the work.
+    const long mid = (long)((p.M + 191) / 192) * ((p.N + 255) / 256);
+    if (big < 256 && mid <= 256) return launch_8w<3>(p, ep, kind, stream);
+    return launch_8w<4>(p, ep, kind, stream);
+  }
   if (big >= 256) return launch_tile<256, 256, 2, 2>(p, ep, kind, stream);
   return launch_tile<128, 128, 2, 2>(p, ep, kind, stream);
 }

@@ -193,6 +193,22 @@ def test_large_ragged_rows_in_the_second_wave_group():
     close_all(shards)
 
 
+def test_192_row_tiles_with_ragged_rows():
+    # M = 4000, N = 2304 (QKV of 6 heads of 128): 16 x 9 = 144 tiles of 256
+    # rows leave CUs idle in one round, so the GEMM takes 192-row tiles (21 x 9
+    # = 189); 4000 = 20 x 192 + 160, so in the last tile row group 0 (rows
+    # 0-95) is whole and group 1 stores 64 of its 96 rows.  The attention-out
+    # GEMM (N = 3072, K = 768) takes them too (21 x 12 = 252 tiles).
+    w = Workload("qkv_T4000_D3072_H24_P4", 4000, 3072, 24, 128, 0, 4, "bf16")
+    inp = tp_inputs.make_inputs(w, seed=25)
+    ranks, y_ref = full_oracle(w, inp)
+    shards, outs, y = run_all_ranks(w, inp)
+    for r, (buf, ref) in enumerate(zip(outs, ranks)):
+        check_rank(w, buf, ref, H.TOL["bf16"], f"T4000 rank {r}")
+    assert H.rel_err(H.as_f64(y), y_ref) <= H.TOL["bf16"]
+    close_all(shards)
+
+
 def test_large_rowwise_store_and_accumulate_paths():
     # MLP-only, P = 1, hidden 8192: the down projection is N = 8192 -> 9 x 32 tiles
     w = Workload("big_down_T2125_D8192_F1024_P1", 2125, 8192, 0, 0, 1024, 1, "bf16")
