@@ -511,6 +511,10 @@ def main():
                                 "step_share": 0.0}
         per_kernel[name]["step_share"] = round(avg_ms * per_kernel[name]["launches_per_step"]
                                                / ms_per_step, 4)
+        srt = sorted(times)
+        per_kernel[name]["median_ms"] = round(srt[len(srt) // 2] if len(srt) % 2
+                                              else 0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2]), 4)
+        per_kernel[name]["min_ms"] = round(srt[0], 4)
     dom = max(per_kernel, key=lambda n: per_kernel[n]["step_share"])
     src, work, bound = kernels[dom]
     k = per_kernel[dom]
