@@ -8,8 +8,10 @@
 //
 // HBM-bound: one thread per 4 consecutive output dims of one (t, j), so a
 // row's threads read each partial's row as contiguous float4s and write the
-// output row contiguously; the 32 threads of a head recompute the n weights
-// (n <= 16 exponentials, trivial next to the loads).
+// output row contiguously; the threads of a head recompute the n weights
+// (n <= 16 exponentials, trivial next to the loads).  The grid's x index is
+// the token and y the column block, so a thread finds its head with one
+// 32-bit division.
 #include "tp_kernels.h"
 
 namespace tpk {
@@ -20,12 +22,10 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 __global__ void __launch_bounds__(256) attn_merge(MergeArgs a) {
   const int groups = a.head_dim / 4;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)a.T * a.heads * groups) return;
-  const int c4 = (int)(idx % groups);
-  const int64_t th = idx / groups;
-  const int j = (int)(th % a.heads);
-  const int64_t t = th / a.heads;
+  const int col4 = blockIdx.y * blockDim.x + threadIdx.x;   // float4 column of the row
+  if (col4 >= a.heads * groups) return;
+  const int j = col4 / groups, c4 = col4 - j * groups;
+  const int64_t t = blockIdx.x;
 
   float l[kMaxMergeParts];
   float m = -INFINITY;
@@ -65,8 +65,10 @@ __global__ void __launch_bounds__(256) attn_merge(MergeArgs a) {
 }  // namespace
 
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t stream) {
-  const int64_t threads = (int64_t)a.T * a.heads * (a.head_dim / 4);
-  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  if (a.T <= 0) return hipSuccess;
+  const int row4 = a.heads * (a.head_dim / 4);   // float4 columns per token
+  const int threads = min(256, (row4 + 63) / 64 * 64);
+  const dim3 grid((unsigned)a.T, (unsigned)((row4 + threads - 1) / threads)), block(threads);
   hipLaunchKernelGGL(attn_merge, grid, block, 0, stream, a);
   return hipGetLastError();
 }

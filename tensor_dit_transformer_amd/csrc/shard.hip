@@ -695,7 +695,9 @@ TP_API tp_status tp_attn_merge(const float* const* o_parts, const float* const* 
   if (heads < 1 || head_dim < 4 || head_dim % 4)
     return fail(TP_ERR_ARG, "heads >= 1 and head_dim a positive multiple of 4 required");
   const int64_t W = heads * head_dim;
-  if (W > INT32_MAX) return fail(TP_ERR_UNSUPPORTED, "heads*head_dim too large");
+  // the merge grid's column blocks (256 threads of 4 dims each) must not exceed 65535
+  if (W > (int64_t)65535 * 256 * 4)
+    return fail(TP_ERR_UNSUPPORTED, "heads*head_dim (%lld) too large", (long long)W);
   if (ld_lse_parts < heads) return fail(TP_ERR_ARG, "ld_lse_parts < heads");
   tpk::MergeArgs a{};
   for (int i = 0; i < n_parts; ++i) {
