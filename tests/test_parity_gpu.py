@@ -241,11 +241,13 @@ def test_large_ragged_n_paths(w):
     close_all(shards)
 
 
-@pytest.mark.parametrize("T,heads", [(5500, 24), (4608, 6)])
+@pytest.mark.parametrize("T,heads", [(5500, 24), (4608, 11), (4608, 6)])
 def test_attention_long_sequences_both_workgroup_shapes(T, heads):
     """T=5500 x 24 heads takes the 256-query (8-wave) workgroups with a
-    ragged last tile; 4608 x 6 takes the 128-query ones.  Seeded packed qkv,
-    oracle on sampled query rows (each against all keys)."""
+    ragged last tile; 4608 x 11 takes them too, 198 workgroups, so the XCD
+    work order gives six XCDs one item more than the other two; 4608 x 6
+    takes the 128-query ones.  Seeded packed qkv, oracle on sampled query
+    rows (each against all keys)."""
     w = Workload(f"attn_T{T}_H{heads}", T, heads * 128, heads, 128, 0, 1, "bf16")
     inp = tp_inputs.make_inputs(w, seed=12, tokens=8)      # weights only matter for create
     s = H.create_shards(dataclass_tokens(w, 8), inp)[0]
