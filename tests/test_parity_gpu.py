@@ -206,6 +206,27 @@ def test_192_row_tiles_with_ragged_rows():
     for r, (buf, ref) in enumerate(zip(outs, ranks)):
         check_rank(w, buf, ref, H.TOL["bf16"], f"T4000 rank {r}")
     assert H.rel_err(H.as_f64(y), y_ref) <= H.TOL["bf16"]
+    # fp32 accumulate form of the same 192-row out-projection, twice onto zeros
+    p2 = torch.zeros_like(outs[0].partial)
+    o = outs[0].o
+    for _ in range(2):
+        tp.tp_rowwise_linear_partial(shards[0], tp.TP_ATTN_OUT, w.tokens, o, p2, accumulate=True)
+    torch.cuda.synchronize()
+    assert H.rel_err(H.as_f64(p2), 2 * ranks[0]["p_block"]) <= H.TOL["bf16"]
+    close_all(shards)
+
+
+def test_192_row_tiles_with_gelu_epilogue():
+    # MLP up-projection M = 4000, N = 9216 / 4 = 2304: 144 tiles of 256 rows,
+    # 189 of 192, so the GELU epilogue runs on 192-row tiles with a ragged
+    # last tile row.
+    w = Workload("mlp_T4000_D1024_F9216_P4", 4000, 1024, 0, 0, 9216, 4, "bf16")
+    inp = tp_inputs.make_inputs(w, seed=26)
+    ranks, y_ref = full_oracle(w, inp)
+    shards, outs, y = run_all_ranks(w, inp)
+    for r, (buf, ref) in enumerate(zip(outs, ranks)):
+        check_rank(w, buf, ref, H.TOL["bf16"], f"T4000 MLP rank {r}")
+    assert H.rel_err(H.as_f64(y), y_ref) <= H.TOL["bf16"]
     close_all(shards)
 
 
