@@ -161,6 +161,22 @@ def test_bf16_swiglu_block_on_the_8wave_path():
     close(shards)
 
 
+@pytest.mark.parametrize("T", [2100, 2300])
+def test_bf16_swiglu_8wave_ragged_rows(T):
+    """The same block at T = 2100 (9 x 22 = 198 tiles of 256 rows, 242 of
+    192: 192-row tiles, the second wave group of the last tile row holds 84
+    of its 96 rows) and T = 2300 (264 tiles of 192 rows would need two
+    rounds: 256-row tiles, 124 of 128 rows): the SwiGLU epilogue's row test."""
+    w = Workload(f"swiglu_block_T{T}_D1024_H8_F4096_P2", T, 1024, 8, 128, 4096, 2, "bf16",
+                 mlp_act="swiglu")
+    inp = tp_inputs.make_inputs(w, seed=11)
+    refs = rank_refs(w, inp)
+    shards, outs = run(w, inp)
+    for r, (b, ref) in enumerate(zip(outs, refs)):
+        check(b, ref, H.TOL["bf16"], f"SwiGLU T={T} rank {r}")
+    close(shards)
+
+
 def test_single_stream_from_packed_checkpoint():
     """Shards created from one fused input projection and one fused output
     projection (pointers into the blocks, the output projection's row
