@@ -70,7 +70,17 @@
 extern "C" {
 #endif
 
-typedef enum tp_status {
+/* Every enum below is an int on the ABI.  In C++ it gets int32_t as its fixed
+ * underlying type, so any int a C or Python caller passes is a value of the
+ * type (the library rejects the ones it does not know); without a fixed type
+ * an out-of-range value would be undefined behaviour in the library. */
+#ifdef __cplusplus
+#define TP_ENUM_INT : int32_t
+#else
+#define TP_ENUM_INT
+#endif
+
+typedef enum tp_status TP_ENUM_INT {
   TP_OK = 0,
   TP_ERR_ARG = -1,           /* NULL/misaligned pointer, bad size, wrong layer */
   TP_ERR_DIVISIBILITY = -2,  /* tp_degree does not divide heads / a packed block / ffn,
@@ -81,12 +91,12 @@ typedef enum tp_status {
   TP_ERR_IO = -6             /* a weight file is missing, unreadable or too short */
 } tp_status;
 
-typedef enum tp_dtype {
+typedef enum tp_dtype TP_ENUM_INT {
   TP_F32 = 0,                /* fp32 activations and weights */
   TP_BF16 = 1                /* bf16 activations and weights; fp32 accumulate */
 } tp_dtype;
 
-typedef enum tp_mlp_act {
+typedef enum tp_mlp_act TP_ENUM_INT {
   TP_MLP_GELU_TANH = 0,      /* h = GELU-tanh(x W_up^T + b_up); W_up is [F, D] */
   TP_MLP_SWIGLU = 1          /* h = silu(x W_gate^T + b_gate) * (x W_up^T + b_up); the
                                 in-projection packs [W_gate; W_up] as one [2F, D]
@@ -94,7 +104,7 @@ typedef enum tp_mlp_act {
                                 blocks [1, 1] */
 } tp_mlp_act;
 
-typedef enum tp_layer {
+typedef enum tp_layer TP_ENUM_INT {
   TP_QKV = 0,                /* colwise: packed [Q_r; K_r; V_r], blocks [1, 1, 1] */
   TP_MLP_UP = 1,             /* colwise: FFN in-projection, fused bias + activation */
   TP_ATTN_OUT = 2,           /* rowwise: to_out.0 (attention out-projection) */

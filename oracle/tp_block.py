@@ -50,6 +50,7 @@ __all__ = [
     "attention_rows", "colwise_rows_sampled", "silu", "swiglu", "MLP_ACTS",
     "mlp_hidden", "packed_rowwise_cols", "single_stream_block",
     "single_stream_rank", "single_stream_as_block", "split_input_rank",
+    "block_keys_values", "block_rows_sampled",
 ]
 
 
@@ -486,3 +487,63 @@ def attention_rows(q_rows, k, v, num_heads: int, head_dim: int) -> np.ndarray:
     """Attention for some query rows against all keys/values (each output row
     depends only on its own query row and on every key and value)."""
     return attention_heads(q_rows, k, v, num_heads, head_dim)
+
+
+def block_keys_values(x, wts: Dict[str, np.ndarray], bf16: bool):
+    """K and V of every token over all heads (unsharded), rounded where the
+    ABI stores them: what every sampled attention row reads.  Returned
+    separately so several tp_degrees can share one (costly) evaluation."""
+    rnd = to_bf16_rne if bf16 else (lambda a: np.asarray(a, dtype=np.float64))
+    x = np.asarray(x, dtype=np.float64)
+    return rnd(linear(x, wts["w_k"], wts["b_k"])), rnd(linear(x, wts["w_v"], wts["b_v"]))
+
+
+def block_rows_sampled(x, wts: Dict[str, np.ndarray], rows, tp_degree: int, num_heads: int,
+                       head_dim: int, bf16: bool, mlp_act: str = "gelu_tanh",
+                       kv=None) -> Dict[str, object]:
+    """``rank_forward`` for every rank and the reduce, on some token rows only.
+
+    Each output row of the block depends on its own input row, plus every
+    key and value for attention, so the rows are exact at any sequence
+    length.  Per rank r the stored activations are the column slices of the
+    unsharded ones (colwise shards concatenate to the unsharded output, and
+    attention is head-local: [TP page, §Colwise e rowwise]): qkv_r = [Q_r |
+    K_r | V_r], o_r = O[:, R_r], h_r = G[:, C_r]; the rank's partial is
+    o_r W_o[:, R_r]^T + h_r W_dn[:, C_r]^T (no bias), and y = sum over ranks
+    in order, plus the rowwise biases once ([TP page, intro]).
+
+    Returns {"ranks": [{"qkv_r", "o_r", "h_r", "p_block"} per rank, on the
+    rows], "y": [len(rows), D]}; ``kv`` = block_keys_values(...) if already
+    computed."""
+    rnd = to_bf16_rne if bf16 else (lambda a: np.asarray(a, dtype=np.float64))
+    rows = np.asarray(rows)
+    xr = np.asarray(x, dtype=np.float64)[rows]
+    P = tp_degree
+    has_attn = "w_q" in wts
+    has_mlp = "w_up" in wts
+    if has_attn:
+        HD = num_heads * head_dim
+        K, V = block_keys_values(x, wts, bf16) if kv is None else kv
+        Q = rnd(linear(xr, wts["w_q"], wts["b_q"]))
+        o = rnd(attention_heads(Q, K, V, num_heads, head_dim))
+        Kr, Vr = K[rows], V[rows]
+    if has_mlp:
+        F = np.asarray(wts["w_dn"]).shape[1]
+        g = rnd(mlp_hidden(xr, wts["w_up"], wts["b_up"], mlp_act))
+    ranks = []
+    for r in range(P):
+        res: Dict[str, np.ndarray] = {}
+        part = 0.0
+        if has_attn:
+            R = colwise_range(HD, P, r)
+            res["qkv_r"] = np.concatenate([Q[:, R], Kr[:, R], Vr[:, R]], axis=1)
+            res["o_r"] = o[:, R]
+            part = part + linear(res["o_r"], np.asarray(wts["w_o"])[:, rowwise_range(HD, P, r)])
+        if has_mlp:
+            C = colwise_range(F, P, r)
+            res["h_r"] = g[:, C]
+            part = part + linear(res["h_r"], np.asarray(wts["w_dn"])[:, rowwise_range(F, P, r)])
+        res["p_block"] = part
+        ranks.append(res)
+    y = partial_reduce([res["p_block"] for res in ranks], rowwise_bias(wts))
+    return {"ranks": ranks, "y": y}

@@ -14,7 +14,10 @@ from typing import Dict, Optional, Sequence
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtp_shard.so")
+# TP_SHARD_LIB names another build of the same library (the host-sanitizer
+# build the CPU tests run the ABI checks under); the default is the in-tree one.
+LIB_PATH = os.environ.get("TP_SHARD_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "libtp_shard.so")
 
 # tp_status
 TP_OK = 0

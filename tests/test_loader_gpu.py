@@ -1,12 +1,15 @@
 """Shard-on-read loading (Diffusers TP page, §Carregar um modelo fragmentado:
 each rank reads only its own slice of each weight; §Desempenho de
-carregamento: that is what bounds per-rank CPU memory).  A shard loaded from
-raw weight files must be identical to the shard created from the same host
-arrays -- every output of the hot path equal bit for bit -- for separate and
-packed checkpoints, GELU and SwiGLU, bf16 and fp32, with staging buffers small
-enough to force chunked and row-split reads; a short file fails with
-TP_ERR_IO; and a load adds no pageable host memory beyond a few pages (the
-staging buffer, pinned, is the only large host allocation), far below the
+carregamento: that is what bounds per-rank CPU memory).  Every output of the
+hot path of a shard loaded from raw weight files -- qkv_r, o_r, h_r, the fp32
+partial and the modulation partial -- matches the float64 oracle of that rank
+(rank_forward; the single-stream rank for packed SwiGLU checkpoints;
+split_input_rank for the modulation), for separate and packed checkpoints,
+GELU and SwiGLU, bf16 and fp32, with staging buffers small enough to force
+chunked and row-split reads; the loaded shard's outputs are also bitwise equal
+to those of the shard created from the same host arrays.  A short file fails
+with TP_ERR_IO, and a load adds no pageable host memory beyond a few pages
+(the staging buffer, pinned, is the only large host allocation), far below the
 rank's slice, measured in a fresh process."""
 import os
 import subprocess
@@ -17,6 +20,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle as O
 import tensor_dit_transformer_amd as tp
 import tp_harness as H
 import tp_inputs
@@ -57,13 +61,40 @@ CASES = [
     Workload("mlp_f32_T70_D256_F1024_P2", 70, 256, 0, 0, 1024, 2, "f32"),
     Workload("mod_gelu_T64_D512_H4_F1024_P2", 64, 512, 4, 128, 1024, 2, "bf16", mod_rows=8, mod_out=1536),
 ]
+# packed checkpoints fuse the attention and MLP projections: only cases with both
+LOAD_CASES = [(w, packed) for w in CASES for packed in (False, True) if w.has_attn or not packed]
 
 
-@pytest.mark.parametrize("w", CASES, ids=[c.name for c in CASES])
-@pytest.mark.parametrize("packed", [False, True])
-def test_loaded_shard_equals_created_shard(w, packed, tmp_path):
-    if packed and not w.has_attn:
-        pytest.skip("packed checkpoints fuse the attention and MLP projections")
+def check_against_oracle(w, inp, r, outs, packed, what):
+    """One rank's outputs against its float64 oracle."""
+    v = inp.values
+    bf16 = w.dtype == "bf16"
+    tol = H.TOL[w.dtype]
+    b, mod = outs
+    ref = O.rank_forward(v["x"], v, w.tp_degree, r, w.num_heads, w.head_dim, bf16, mlp_act=w.mlp_act)
+    got = {"partial_r": (b.partial, ref["p_block"])}
+    if b.qkv is not None:
+        got.update(qkv_r=(b.qkv, ref["qkv_r"]), o_r=(b.o, ref["o_r"]))
+    if b.h is not None:
+        got["h_r"] = (b.h, ref["h_r"])
+    if packed and w.mlp_act == "swiglu":
+        pk = H.packed_host_weights(inp)
+        vals = {k: tp_inputs.bits_to_f32(a) if bf16 else a for k, a in pk.items()}
+        ss = O.single_stream_rank(v["x"], vals["w_in"], vals["b_in"], vals["w_out"], w.tp_degree, r,
+                                  w.num_heads, w.head_dim, w.ffn, bf16)
+        got.update(ss_qkv_r=(b.qkv, ss["qkv_r"]), ss_o_r=(b.o, ss["o_r"]), ss_h_r=(b.h, ss["h_r"]),
+                   ss_partial=(b.partial, ss["partial"]))
+    if mod is not None:
+        got["mod_partial"] = (mod, O.split_input_rank(v["c"], v["w_mod"], w.tp_degree, r))
+    errs = {k: H.rel_err(H.as_f64(t), ref_) for k, (t, ref_) in got.items()}
+    say(what, {k: f"{e:.2e}" for k, e in errs.items()})
+    for k, e in errs.items():
+        assert e <= tol, f"{what} {k}: {e:.3e}"
+
+
+@pytest.mark.parametrize("w,packed", LOAD_CASES,
+                         ids=[f"{w.name}-{'packed' if p else 'separate'}" for w, p in LOAD_CASES])
+def test_loaded_shard_matches_oracle_and_created_shard(w, packed, tmp_path):
     inp = tp_inputs.make_inputs(w, seed=21)
     hw = H.packed_host_weights(inp) if packed else H.host_weights(inp)
     if w.has_mod:
@@ -93,10 +124,11 @@ def test_loaded_shard_equals_created_shard(w, packed, tmp_path):
         # 1 MiB staging: 512 KiB halves, so the larger slices need many chunks
         loaded = tp.tp_block_shard_load(cfg, files, staging_bytes=1 << 20, **ld)
         a, b = outputs(made, x, w.tokens, c), outputs(loaded, x, w.tokens, c)
+        check_against_oracle(w, inp, r, b, packed, f"{w.name} packed={packed} rank {r} (loaded)")
         same(a, b)
         made.close()
         loaded.close()
-    say(f"{w.name} packed={packed}: loaded == created on every rank")
+    say(f"{w.name} packed={packed}: loaded matches the oracle and equals created on every rank")
 
 
 def test_short_file_is_an_io_error(tmp_path):

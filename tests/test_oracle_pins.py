@@ -365,3 +365,41 @@ def test_oracle_drift_against_golden_summary():
         assert abs(got[k] - want[k]) <= 1e-9 * max(1.0, abs(want[k]))
     for (i, j, v), (i2, j2, v2) in zip(got["samples"], want["samples"]):
         assert (i, j) == (i2, j2) and abs(v - v2) <= 1e-12
+
+
+@pytest.mark.parametrize("P", [1, 2, 4])
+@pytest.mark.parametrize("mlp_act", ["gelu_tanh", "swiglu"])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_block_rows_sampled_equals_full_rank_forward_rows(P, mlp_act, bf16):
+    """The row-sampled whole block (every rank's stored activations and
+    partial, and the reduced y, on some rows) equals the rows of the full
+    per-rank forward and reduce, and y equals the unsharded block's rows:
+    each output row depends only on its own input row plus every key/value."""
+    rng = np.random.default_rng(31)
+    T, D, H, d, F = 40, 64, 4, 16, 96
+    w = dict(x=rng.standard_normal((T, D)))
+    for n in ("w_q", "w_k", "w_v", "w_o"):
+        w[n] = rng.standard_normal((D, D)) * 0.2
+    for n in ("b_q", "b_k", "b_v", "b_o", "b_dn"):
+        w[n] = rng.standard_normal(D) * 0.1
+    U = 2 * F if mlp_act == "swiglu" else F
+    w["w_up"] = rng.standard_normal((U, D)) * 0.2
+    w["b_up"] = rng.standard_normal(U) * 0.1
+    w["w_dn"] = rng.standard_normal((D, F)) * 0.2
+    if bf16:
+        w = {k: O.to_bf16_rne(v) for k, v in w.items()}
+    rows = np.array([0, 5, 17, 39])
+    got = O.block_rows_sampled(w["x"], w, rows, P, H, d, bf16, mlp_act=mlp_act)
+    full = [O.rank_forward(w["x"], w, P, r, H, d, bf16, mlp_act=mlp_act) for r in range(P)]
+    for r in range(P):
+        for k in ("qkv_r", "o_r", "h_r", "p_block"):
+            np.testing.assert_allclose(got["ranks"][r][k], full[r][k][rows], rtol=1e-12, atol=1e-12)
+    y = O.partial_reduce([f["p_block"] for f in full], O.rowwise_bias(w))
+    np.testing.assert_allclose(got["y"], y[rows], rtol=1e-12, atol=1e-12)
+    un = O.block_unsharded(w["x"], w, H, d, bf16, mlp_act=mlp_act)["y"]
+    np.testing.assert_allclose(got["y"], un[rows], rtol=1e-12, atol=1e-12)
+    # a misplaced head block (rank 0 reading rank 1's heads) must not pass
+    if P > 1:
+        wrong = O.linear(got["ranks"][1]["o_r"], w["w_o"][:, O.rowwise_range(D, P, 0)])
+        right = O.linear(got["ranks"][0]["o_r"], w["w_o"][:, O.rowwise_range(D, P, 0)])
+        assert np.max(np.abs(wrong - right)) > 1e-3

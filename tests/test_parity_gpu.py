@@ -245,6 +245,26 @@ def test_large_rowwise_store_and_accumulate_paths():
     close_all(shards)
 
 
+def test_four_wave_256_tiles_with_k_tail():
+    # hidden = ffn = 4104 = 64 x 64 + 8: K % 64 != 0 for both GEMMs, with
+    # 18 x 17 = 306 tiles of 256 x 256 (at least 256), so both take the 4-wave
+    # 256 x 256 register-staged kernel with the zero-filled K tail: the
+    # up-projection's GELU bf16 store, the down-projection's fp32 store, and
+    # the fp32 accumulate form.
+    w = Workload("ktail256_T4608_D4104_F4104_P1", 4608, 4104, 0, 0, 4104, 1, "bf16")
+    inp = tp_inputs.make_inputs(w, seed=27)
+    ranks, y_ref = full_oracle(w, inp)
+    shards, outs, y = run_all_ranks(w, inp)
+    check_rank(w, outs[0], ranks[0], H.TOL["bf16"], w.name)
+    assert H.rel_err(H.as_f64(y), y_ref) <= H.TOL["bf16"]
+    p2 = torch.zeros_like(outs[0].partial)
+    for _ in range(2):
+        tp.tp_rowwise_linear_partial(shards[0], tp.TP_MLP_DOWN, w.tokens, outs[0].h, p2, accumulate=True)
+    torch.cuda.synchronize()
+    assert H.rel_err(H.as_f64(p2), 2 * ranks[0]["p_block"]) <= H.TOL["bf16"]
+    close_all(shards)
+
+
 @pytest.mark.parametrize("w", [
     # up-projection N = 8288 = 32 x 256 + 96: 9 x 33 tiles on the 8-wave kernel,
     # the last tile column partly past N
@@ -338,7 +358,7 @@ def test_deterministic_repeats():
     inp = tp_inputs.make_inputs(w, seed=6)
     shards, first, y0 = run_all_ranks(w, inp)
     x = H.to_device(inp, "x")
-    for _ in range(5):
+    for _ in range(10):
         for s, b0 in zip(shards, first):
             b = H.RankBuffers(s, w.tokens)
             H.run_rank(s, x, b)

@@ -222,3 +222,52 @@ def sample_rows(tokens: int, n: int, seed: int = 1) -> np.ndarray:
     rows = set(rng.choice(tokens, size=n, replace=False).tolist())
     rows.update({0, tokens - 1})
     return np.array(sorted(rows), dtype=np.int64)
+
+
+# Structured packed qkv [T, 3 H d] for the attention edge cases (input
+# construction only; both sides read the same bf16 bits):
+#   "growing":  per head a random unit direction u; query row i has component
+#               beta_i * 4 along u (beta_i cycles 1, 0, 0.5, -1 with the row),
+#               key t has component 24 * (t // 64) along u, so for beta = 1 a
+#               row's scores rise by about 12 log2 units from one 64-key tile
+#               to the next (6 for beta = 0.5; flat or falling otherwise);
+#               plus N(0, 0.5^2) noise on q and N(0, 1) on k and v.
+#   "dominant": every query has component 4 along u; one key, at row
+#               5 T / 8 + 17, is 80 u, over 20 log2 units above every other
+#               score of every query; the rest N(0, 1.5^2).
+#   "zero_q":   Q = 0 (every score 0), K and V N(0, 1.5^2).
+EDGE_KINDS = ("growing", "dominant", "zero_q")
+
+
+def attention_edge_qkv(T: int, heads: int, kind: str, seed: int = 0, head_dim: int = 128):
+    if kind not in EDGE_KINDS:
+        raise ValueError(kind)
+    rng = np.random.default_rng(seed)
+    W = heads * head_dim
+    u = rng.standard_normal((heads, head_dim)).astype(np.float64)
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    u = u.reshape(W)
+    if kind == "growing":
+        q = 0.5 * rng.standard_normal((T, W))
+        k = rng.standard_normal((T, W))
+        v = rng.standard_normal((T, W))
+        beta = np.array([1.0, 0.0, 0.5, -1.0])[np.arange(T) % 4]
+        q += 4.0 * beta[:, None] * u[None, :]
+        k += 24.0 * (np.arange(T) // 64)[:, None] * u[None, :]
+    elif kind == "dominant":
+        q = 0.5 * rng.standard_normal((T, W)) + 4.0 * u[None, :]
+        k = 1.5 * rng.standard_normal((T, W))
+        v = 1.5 * rng.standard_normal((T, W))
+        k[dominant_key(T)] = 80.0 * u
+    else:
+        q = np.zeros((T, W))
+        k = 1.5 * rng.standard_normal((T, W))
+        v = 1.5 * rng.standard_normal((T, W))
+    a = np.concatenate([q, k, v], axis=1).astype(np.float32)
+    b = bf16_bits(a)
+    return bits_to_f32(b), b
+
+
+def dominant_key(T: int) -> int:
+    """Row of the dominant key in attention_edge_qkv(kind="dominant")."""
+    return min(T - 1, 5 * T // 8 + 17)
