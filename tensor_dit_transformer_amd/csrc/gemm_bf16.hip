@@ -25,9 +25,10 @@
 //   * Workgroup ids are renumbered so each of the 8 XCDs (own L2) walks a
 //     contiguous stretch of a grouped tile order (8 tile rows per group), and
 //     the A/B panels it streams are shared by its neighbours in L2.
-//   * Rows past M / N are clamped on load and masked on store.  In the 4-wave
-//     kernel a K that is not a multiple of 64 zero-fills the chunks past K
-//     (K must be a multiple of 8).
+//   * Rows past M / N are masked on store; on load the 4-wave kernel clamps
+//     them to the last row and the 8-wave kernel reads them as zero (past
+//     its buffer descriptors' range).  In the 4-wave kernel a K that is not a
+//     multiple of 64 zero-fills the chunks past K (K must be a multiple of 8).
 #include "tp_kernels.h"
 
 namespace tpk {
@@ -292,27 +293,34 @@ gemm_bf16_nt(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
 
 // 256x256 tile (TM = 4; TM = 3 gives 192x256 for problems that one round
 // of 256-row tiles would leave CUs idle in), 8 waves (2 per SIMD) in a
-// ping-pong schedule; each wave owns a (32 TM)x64 block of C.  A and B tiles
-// go global -> LDS directly (global_load_lds_dwordx4: each wave instruction
-// fills 1 KB = 8 tile rows), so no registers stage them and no ds_write is
-// issued; K % 64 == 0 (no zero-fill on this path).  Waves 0-3 (group 0) own
-// C rows [0, 32 TM) and waves 4-7 (group 1) rows [32 TM, 64 TM).  The groups
-// run one phase apart, separated by workgroup barriers: while one group reads
-// a whole K tile of operand fragments from LDS into registers
-// ((TM + 2) x 4 x 16 bytes per lane), the other issues the 8 TM MFMAs of the
-// tile it read in the previous phase.  Phase 2k:
+// ping-pong schedule; each wave owns a (32 TM)x64 block of C.  Waves 0-3
+// (group 0) own C rows [0, 32 TM) and waves 4-7 (group 1) rows
+// [32 TM, 64 TM).  The groups run one phase apart, separated by workgroup
+// barriers: while one group reads a whole K tile of operand fragments from
+// LDS into registers ((TM + 2) x 4 x 16 bytes per lane), the other issues
+// the 8 TM MFMAs of the tile it read in the previous phase.  Phase 2k:
 // group 0 reads tile k, group 1 multiplies tile k-1; phase 2k+1: group 0
 // multiplies tile k, group 1 reads tile k.
 //
-// A wave that waits to issue a global load issues no MFMA meanwhile, so
-// loads are issued only in read phases: group 0, after reading tile k in
-// phase 2k, fetches the whole B tile k+1; group 1, after reading tile k in
-// phase 2k+1, fetches the whole A tile k+2.  A has three LDS stages and B
-// two (96 + 64 KB at TM = 4): the B tile k+1 goes into the stage of tile k-1 (last
-// read in phase 2k-1) and is waited for by group 0 at the end of phase 2k+1;
-// the A tile k+2 goes into the stage of tile k-1 too and is waited for by
-// group 1 at the end of phase 2k+3.  Tile 0 and A tile 1 are fetched before
-// the loop.
+// A and B tiles go global -> LDS directly with buffer loads
+// (buffer_load_dwordx4 ... lds: each wave instruction fills 1 KB = 8 tile
+// rows), so no registers stage them and no ds_write is issued; K % 64 == 0.
+// A load's address is the operand's buffer descriptor, a per-lane 32-bit
+// offset fixed for the whole kernel (row within the tile, swizzled chunk) and
+// a wave-uniform K offset in a scalar register, so the loads of a tile cost
+// one VGPR each and no address arithmetic.  Rows past M (or N) lie past the
+// descriptor's byte range and read as zero (their results are not stored).
+//
+// Every wave fetches an equal share of every tile: the B tile k+1 (4 loads
+// per wave) in phase 2k and the A tile k+2 (BM/64 loads per wave) in phase
+// 2k+1.  The reading group issues its share after its fragment reads; the
+// multiplying group spreads its share among its first MFMAs (one load per
+// two), so a load that waits to issue delays only a few MFMAs.  A has three
+// LDS stages and B two (96 + 64 KB at TM = 4): B tile k+1 goes into the stage
+// of tile k-1 (last read in phase 2k-1) and A tile k+2 likewise; at the end
+// of phase 2k+1 every wave waits for its B tile k+1 loads (the A tile k+2
+// ones may stay in flight: they are needed two phases later), then the
+// barrier publishes the tile to both groups.
 __device__ __forceinline__ void wg_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
@@ -328,11 +336,26 @@ __device__ __forceinline__ void wait_vmem() {
 // all but the newest N loads of this wave have landed
 template <int N>
 __device__ __forceinline__ void wait_vmem_keep() {
-  static_assert(N == 8 || N == 6, "instantiated counts");
+  static_assert(N == 4 || N == 3, "instantiated counts");
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer descriptor over [base, base + bytes): offsets at or past `bytes`
+// read as zero.  Word 3 (0x00020000) selects 32-bit data with no swizzle.
+__device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from byte offset voff + soff of the buffer into LDS at
+// dst + 16 lane (dst wave-uniform).
+__device__ __forceinline__ void lds_dma(rsrc_t r, const u32x4* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)voff,
+                                           (int)soff, 0, 0);
 }
 
 template <OutKind KIND, int TM>
@@ -344,7 +367,8 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
   constexpr int KS = kBK / 16;                  // 4 MFMA k-steps per tile
   constexpr int A_STAGE = BM * kRowChunks;      // 16-byte chunks per A stage
   constexpr int B_STAGE = BN * kRowChunks;
-  constexpr int A_LOADS = 2 * TM;               // 8-row loads per wave per A tile
+  constexpr int AW = BM / 64;                   // 8-row A loads per wave per tile
+  constexpr int BW = BN / 64;                   // 8-row B loads per wave per tile
 
   __shared__ u32x4 smem[3 * A_STAGE + 2 * B_STAGE];   // 160 KB (136 KB at BM 192)
 
@@ -361,32 +385,43 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = wave >> 2, q = wave & 3;   // wave group (0: waves 0-3), place in it
-  const bf16* __restrict__ A = static_cast<const bf16*>(p.A);
-  const bf16* __restrict__ B = static_cast<const bf16*>(p.B);
 
+  // Descriptors end right after the last row's K elements.
+  const uint32_t lda2 = (uint32_t)p.lda * 2, ldb2 = (uint32_t)p.ldb * 2;
+  const rsrc_t ra = buffer_rsrc(p.A, (uint32_t)(p.M - 1) * lda2 + (uint32_t)p.K * 2);
+  const rsrc_t rb = buffer_rsrc(p.B, (uint32_t)(p.N - 1) * ldb2 + (uint32_t)p.K * 2);
+  // Wave w fetches tile rows [w BM/8, (w+1) BM/8) of A and [32 w, 32 w + 32)
+  // of B, 8 rows per load.  In the load of the 8 rows from R (R % 8 == 0)
+  // lane l reads row R + (l >> 3) and fills physical chunk l & 7 of it, which
+  // holds logical chunk (l & 7) ^ (l >> 3) ^ ((R >> 3) & 1) (the swizzle).
+  const int lr = lane >> 3, lc = lane & 7;
+  uint32_t voa[AW], vob[BW];
+#pragma unroll
+  for (int j = 0; j < AW; ++j) {
+    const int R = wave * (BM / 8) + 8 * j;
+    voa[j] = (uint32_t)(m0 + R + lr) * lda2 + (uint32_t)((lc ^ lr ^ ((R >> 3) & 1)) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < BW; ++j) {
+    const int R = wave * (BN / 8) + 8 * j;
+    vob[j] = (uint32_t)(n0 + R + lr) * ldb2 + (uint32_t)((lc ^ lr ^ ((R >> 3) & 1)) * 16);
+  }
   auto stage_a = [&](int kt) { return smem + (kt % 3) * A_STAGE; };
   auto stage_b = [&](int kt) { return smem + 3 * A_STAGE + (kt & 1) * B_STAGE; };
-
-  // global -> LDS: wave q of the fetching group covers the operand rows
-  // 8 n q + 8 i + (lane >> 3), i = 0..n-1 (n = 8 for B, 2 TM for A), one
-  // instruction each; 8 n q is a multiple of 16, so the swizzle of a row
-  // depends only on i & 1.
-  const int kc_even = swizzle(lane >> 3, lane & 7) * 8, kc_odd = swizzle(8 + (lane >> 3), lane & 7) * 8;
-  auto fetch = [&](const bf16* __restrict__ src, int ld, int first_row, int rows, int kt, u32x4* dst,
-                   int n) {
-    const int k = kt * kBK;
-    const int wrow = 8 * n * q;
-#pragma unroll
-    for (int i = 0; i < n; ++i) {
-      const int kc = (i & 1) ? kc_odd : kc_even;
-      const int off = min(first_row + wrow + 8 * i + (lane >> 3), rows - 1) * ld + kc + k;
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(src + off),
-          (void __attribute__((address_space(3)))*)(dst + (wrow + 8 * i) * kRowChunks), 16, 0, 0);
-    }
+  auto load_a = [&](int kt, int j) {
+    lds_dma(ra, stage_a(kt) + (wave * (BM / 8) + 8 * j) * kRowChunks, voa[j], (uint32_t)kt * (kBK * 2));
   };
-  auto fetch_a = [&](int kt) { fetch(A, (int)p.lda, m0, p.M, kt, stage_a(kt), A_LOADS); };
-  auto fetch_b = [&](int kt) { fetch(B, (int)p.ldb, n0, p.N, kt, stage_b(kt), 8); };
+  auto load_b = [&](int kt, int j) {
+    lds_dma(rb, stage_b(kt) + (wave * (BN / 8) + 8 * j) * kRowChunks, vob[j], (uint32_t)kt * (kBK * 2));
+  };
+  auto a_loads = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < AW; ++j) load_a(kt, j);
+  };
+  auto b_loads = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < BW; ++j) load_b(kt, j);
+  };
 
   const int a_row = 32 * TM * g + (lane & 31);
   const int b_row = 64 * q + (lane & 31);
@@ -413,52 +448,97 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  auto multiply = [&]() {
+  // The tile's MFMAs, with load(l), l < nl, issued after MFMA 2 l.
+  auto multiply = [&](auto&& load, int nl) {
+    int idx = 0;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+          if ((idx & 1) == 0 && (idx >> 1) < nl) {
+            __builtin_amdgcn_sched_barrier(0);
+            load(idx >> 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          ++idx;
+        }
   };
+  auto none = [](int) {};
 
+  // The loop bodies carry no branch on the loads: the last two tiles, which
+  // fetch less, are peeled by hand.
   const int nk = p.K / kBK;
-  if (g == 0) {
-    fetch_b(0);
-  } else {
-    fetch_a(0);
-    if (nk > 1) fetch_a(1);
-  }
+  b_loads(0);
+  a_loads(0);
+  if (nk > 1) a_loads(1);
   wait_vmem();
   wg_barrier();
   if (g == 0) {
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool more = kt + 1 < nk;
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) {
       read_tile(kt);
       __builtin_amdgcn_sched_barrier(0);
-      if (more) fetch_b(kt + 1);
+      b_loads(kt + 1);
       wg_barrier();                       // end of phase 2 kt
-      multiply();
-      if (more) wait_vmem();              // B tile kt + 1
+      multiply([&](int j) { load_a(kt + 2, j); }, AW);
+      wait_vmem_keep<AW>();               // B tile kt + 1 landed
       wg_barrier();                       // end of phase 2 kt + 1
     }
+    if (kt + 1 < nk) {                    // kt = nk - 2
+      read_tile(kt);
+      __builtin_amdgcn_sched_barrier(0);
+      b_loads(kt + 1);
+      wg_barrier();
+      multiply(none, 0);
+      wait_vmem();
+      wg_barrier();
+      ++kt;
+    }
+    read_tile(kt);                        // kt = nk - 1
+    wg_barrier();
+    multiply(none, 0);
+    wg_barrier();
     wg_barrier();
   } else {
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt > 0) multiply();             // tile kt - 1
+    if (nk > 1) b_loads(1);
+    wg_barrier();                         // end of phase 0
+    read_tile(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nk > 2) {
+      a_loads(2);
+      wait_vmem_keep<AW>();
+    } else {
+      wait_vmem();
+    }
+    wg_barrier();                         // end of phase 1
+    int kt = 1;
+    for (; kt + 2 < nk; ++kt) {
+      multiply([&](int j) { load_b(kt + 1, j); }, BW);   // tile kt - 1
       wg_barrier();                       // end of phase 2 kt
       read_tile(kt);
       __builtin_amdgcn_sched_barrier(0);
-      if (kt + 2 < nk) {
-        fetch_a(kt + 2);
-        wait_vmem_keep<A_LOADS>();        // A tile kt + 1
-      } else {
-        wait_vmem();
-      }
+      a_loads(kt + 2);
+      wait_vmem_keep<AW>();
       wg_barrier();                       // end of phase 2 kt + 1
     }
-    multiply();
+    if (kt + 1 < nk) {                    // kt = nk - 2 >= 1
+      multiply([&](int j) { load_b(kt + 1, j); }, BW);
+      wg_barrier();
+      read_tile(kt);
+      wait_vmem();
+      wg_barrier();
+      ++kt;
+    }
+    if (kt < nk) {                        // kt = nk - 1 >= 1
+      multiply(none, 0);
+      wg_barrier();
+      read_tile(kt);
+      wg_barrier();
+    }
+    multiply(none, 0);                    // tile nk - 1
     wg_barrier();
   }
 
@@ -516,9 +596,10 @@ hipError_t launch_gemm_bf16(const GemmProblem& p, const GemmEpilogue& ep, OutKin
   // CUs (the 8-wave kernel beats four times as many 128x128 tiles even
   // then); 128x128 otherwise.
   const long big = (long)((p.M + 255) / 256) * ((p.N + 255) / 256);
-  // the 8-wave kernel indexes operands with 32-bit element offsets
-  const bool fits32 = (int64_t)p.M * p.lda < ((int64_t)1 << 31) &&
-                      (int64_t)p.N * p.ldb < ((int64_t)1 << 31);
+  // the 8-wave kernel addresses operands with 32-bit byte offsets, also for
+  // the rows of a last partial tile (up to 256 past M or N)
+  const bool fits32 = (int64_t)(p.M + 256) * p.lda < ((int64_t)1 << 31) &&
+                      (int64_t)(p.N + 256) * p.ldb < ((int64_t)1 << 31);
   if (big >= 128 && p.K % kBK == 0 && fits32) {
     // One partial round of 256-row tiles leaves CUs idle (e.g. 162 tiles at
     // M = 4608, N = 2304); if 192-row tiles still fit in one round, every
