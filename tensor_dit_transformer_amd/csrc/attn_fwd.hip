@@ -336,9 +336,9 @@ attn_fwd_bf16_d128(AttnIO a) {
 // state of NQ = 2 does not fit the registers of two waves per SIMD, and at
 // one wave per SIMD the compiler spills.)  Within key tile j a wave issues the
 // score MFMAs of tile j+1 in the same straight-line block as the softmax of
-// tile j, interleaved about one MFMA per seven vector instructions, so the
-// matrix core and the vector ALU work at the same time inside one wave; then
-// the PV MFMAs of tile j.  Four LDS stages: iteration j reads K of tile j+1
+// tile j, one MFMA before each slice of the softmax, so the matrix core and
+// the vector ALU work at the same time inside one wave; then the PV MFMAs of
+// tile j.  Four LDS stages: iteration j reads K of tile j+1
 // and V of tile j, and fetches tile j+3 into the stage tile j-1 used, so
 // every tile's loads have two iterations to land.  Loads past the last tile
 // re-fetch the last tile (harmless, keeps the block branch-free), and the
@@ -354,6 +354,7 @@ __device__ __forceinline__ void barrier_keep_newest_loads() {
 template <int NQ, int NW, bool LSE>
 __global__ void __launch_bounds__(64 * NW, 1)
 attn_fwd_pipe(AttnIO io) {
+  static_assert(NQ == 1, "one 32-query sub-tile per wave");
   constexpr int NSTAGE = 4;
   constexpr int BQ = NW * 32 * NQ;
   constexpr int PER_WAVE = 32 / NW;   // 1 KB loads per wave per tile
@@ -463,97 +464,120 @@ attn_fwd_pipe(AttnIO io) {
   const int off8 = (dsub & 7) * 2;
   const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
 
-  // O^T += V^T P^T for one tile.  The LDS pointer is __restrict__ (as in
-  // scores) so the compiler can tell these reads from the LDS-bound loads in
-  // flight and adds no wait for them: the vmcnt wait before each barrier
-  // already orders every tile's loads before its reads, and a tile's loads
-  // get two iterations to land.
-  auto pv = [&](const u32x4* __restrict__ sVb, const bf16x8 (&pb)[NQ][2][2]) {
-#pragma unroll
-    for (int t = 0; t < kD / 32; ++t) {
-      const int lchunk = (32 * t + dsub) >> 3;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int kb = 32 * c + 16 * u;
-          const char* pa = reinterpret_cast<const char*>(sVb + (kb + keyA) * kRowChunks + (lchunk ^ fA)) + off8;
-          const char* pbp = reinterpret_cast<const char*>(sVb + (kb + keyB) * kRowChunks + (lchunk ^ fB)) + off8;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(pa));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(pbp));
-          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int a = 0; a < NQ; ++a)
-            acc_o[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[a][c][u], acc_o[a][t], 0, 0, 0);
-        }
-    }
+  // K operand of score MFMA i of a tile: key half c = i & 1, k-step
+  // st = i >> 1, so neighbouring MFMAs feed different accumulators.
+  auto kread = [&](const u32x4* __restrict__ sKb, int i) {
+    const int row = 32 * (i & 1) + l32;
+    return __builtin_bit_cast(bf16x8, sKb[row * kRowChunks + ((2 * (i >> 1) + half) ^ swz(row))]);
+  };
+  // V^T operand of PV MFMA (cu, t): keys 32 c + 16 u .. + 15 (cu = 2 c + u)
+  // of dims 32 t .. + 31, two transposing reads.
+  auto vread = [&](const u32x4* __restrict__ sVb, int cu, int t) {
+    const int lchunk = (32 * t + dsub) >> 3;
+    const int kb = 32 * (cu >> 1) + 16 * (cu & 1);
+    const char* pa = reinterpret_cast<const char*>(sVb + (kb + keyA) * kRowChunks + (lchunk ^ fA)) + off8;
+    const char* pbp = reinterpret_cast<const char*>(sVb + (kb + keyB) * kRowChunks + (lchunk ^ fB)) + off8;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pa));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pbp));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // One key tile: s_cur holds raw scores of tile kt; issues scores of kt + 1.
+  // One key tile: s_cur holds the raw scores of tile kt; the scores of tile
+  // kt + 1 go to s_nxt.  Score MFMA i (K read KPF MFMAs ahead) is followed by
+  // slice i of the softmax of tile kt: slices 0-1 the row max, 2 the
+  // reference update, 3-15 the exponentials, weights and row sum.  The
+  // scheduling fences keep that order, so the matrix core and the vector ALU
+  // of the wave work side by side.  Then the rare rescale of the accumulator
+  // and the PV MFMAs, in (key block, dim block) order with the V reads two
+  // key blocks ahead; the LDS pointers are __restrict__ so the compiler can
+  // tell these reads from the LDS-bound loads in flight and adds no wait for
+  // them (the vmcnt wait before each barrier orders every tile's loads before
+  // its reads, and a tile's loads get two iterations to land).
   auto step = [&](int kt, f32x16 (&s_cur)[NQ][2], f32x16 (&s_nxt)[NQ][2]) {
     if (kt * kBKV + kBKV > T) {  // last, partial tile: mask keys past T
 #pragma unroll
-      for (int a = 0; a < NQ; ++a)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = kt * kBKV + 32 * c + 8 * (e >> 2) + 4 * half + (e & 3);
-            if (key >= T) s_cur[a][c][e] = -INFINITY;
-          }
-    }
-    load_tile(kt + 3);
-    scores(sK[(kt + 1) % NSTAGE], s_nxt);
-    bf16x8 pb[NQ][2][2];
-    float alpha[NQ];
-    bool rescale = false;
-#pragma unroll
-    for (int a = 0; a < NQ; ++a) {
-      float mloc = fmaxf(s_cur[a][0][0], s_cur[a][0][1]);
-#pragma unroll
-      for (int e = 2; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s_cur[a][0][e], s_cur[a][0][e + 1]));
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s_cur[a][1][e], s_cur[a][1][e + 1]));
-      mloc = fmaxf(mloc, other_half(mloc, half)) * scale_log2;
-      const bool need = __builtin_amdgcn_ballot_w64(mloc > m_ref[a] + kRescaleSlack) != 0;
-      const float m_new = need ? fmaxf(m_ref[a], mloc) : m_ref[a];
-      alpha[a] = __builtin_amdgcn_exp2f(m_ref[a] - m_new);
-      m_ref[a] = m_new;
-      rescale |= need;
-      float l = l_run[a] * alpha[a];
-#pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[a][c][e], scale_log2, -m_new));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[a][c][e + 1], scale_log2, -m_new));
+        for (int e = 0; e < 16; ++e) {
+          const int key = kt * kBKV + 32 * c + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (key >= T) s_cur[0][c][e] = -INFINITY;
+        }
+    }
+    load_tile(kt + 3);
+    const u32x4* __restrict__ sKb = sK[(kt + 1) % NSTAGE];
+    constexpr int KPF = 6;
+    bf16x8 kf[16];
+#pragma unroll
+    for (int i = 0; i < KPF; ++i) kf[i] = kread(sKb, i);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s_nxt[0][c][e] = 0.0f;
+    float m0 = 0.0f, mloc = 0.0f, m_new = m_ref[0], alpha = 1.0f, l = l_run[0];
+    bool rescale = false;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s_nxt[0][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[0][i >> 1], s_nxt[0][i & 1], 0, 0, 0);
+      if (i + KPF < 16) kf[i + KPF] = kread(sKb, i + KPF);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i == 0) {
+        m0 = fmaxf(s_cur[0][0][0], s_cur[0][0][1]);
+#pragma unroll
+        for (int e = 2; e < 16; e += 2) m0 = fmaxf(m0, fmaxf(s_cur[0][0][e], s_cur[0][0][e + 1]));
+      } else if (i == 1) {
+        mloc = m0;
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s_cur[0][1][e], s_cur[0][1][e + 1]));
+      } else if (i == 2) {
+        // rescale only when some row's max outgrew the reference by the slack
+        mloc = fmaxf(mloc, other_half(mloc, half)) * scale_log2;
+        rescale = __builtin_amdgcn_ballot_w64(mloc > m_ref[0] + kRescaleSlack) != 0;
+        m_new = rescale ? fmaxf(m_ref[0], mloc) : m_ref[0];
+        alpha = __builtin_amdgcn_exp2f(m_ref[0] - m_new);
+        m_ref[0] = m_new;
+        l *= alpha;
+      } else {
+        // p = exp2(s * log2(e)/sqrt(d) - m_ref), packed to bf16 for the PV
+        // product; the row sum adds the bf16 values the product uses
+#pragma unroll
+        for (int q = ((i - 3) * 16) / 13; q < ((i - 2) * 16) / 13; ++q) {
+          const int c = q >> 3, e = 2 * (q & 7);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[0][c][e], scale_log2, -m_new));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[0][c][e + 1], scale_log2, -m_new));
           const bf16x2 pp = {static_cast<bf16>(p0), static_cast<bf16>(p1)};
           l = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l, false);
-          pb[a][c][e >> 3][e & 7] = pp[0];
-          pb[a][c][e >> 3][(e & 7) + 1] = pp[1];
+          pb[c][e >> 3][e & 7] = pp[0];
+          pb[c][e >> 3][(e & 7) + 1] = pp[1];
         }
-      l_run[a] = l;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // interleave: the loads and K reads first, then one score MFMA per ~7
-    // vector instructions of the softmax
-    __builtin_amdgcn_sched_group_barrier(0x020, PER_WAVE, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-#pragma unroll
-    for (int i = 0; i < 16 * NQ; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-    }
+    l_run[0] = l;
+    // the weights are used only after the rescale branch; without this, IR
+    // passes sink their computation into the PV block, away from the score
+    // MFMAs it is interleaved with
+    asm volatile("" :: "v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]), "v"(l));
     if (rescale) {
 #pragma unroll
-      for (int a = 0; a < NQ; ++a)
+      for (int t = 0; t < kD / 32; ++t)
 #pragma unroll
-        for (int t = 0; t < kD / 32; ++t)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc_o[a][t][e] *= alpha[a];
+        for (int e = 0; e < 16; ++e) acc_o[0][t][e] *= alpha;
     }
-    pv(sV[kt % NSTAGE], pb);
+    // O^T += V^T P^T
+    const u32x4* __restrict__ sVb = sV[kt % NSTAGE];
+    bf16x8 vf[4][kD / 32];
+#pragma unroll
+    for (int cu = 0; cu < 2; ++cu)
+#pragma unroll
+      for (int t = 0; t < kD / 32; ++t) vf[cu][t] = vread(sVb, cu, t);
+#pragma unroll
+    for (int cu = 0; cu < 4; ++cu)
+#pragma unroll
+      for (int t = 0; t < kD / 32; ++t) {
+        acc_o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cu][t], pb[cu >> 1][cu & 1], acc_o[0][t], 0, 0, 0);
+        if (cu + 2 < 4) vf[cu + 2][t] = vread(sVb, cu + 2, t);
+      }
     barrier_keep_newest_loads<PER_WAVE>();
   };
 
