@@ -69,6 +69,65 @@ def load_traffic(kernel_key: str, source: str):
     return e.get("bytes_per_launch")
 
 
+class ClockSampler:
+    """Samples the GPU's current shader clock (the '*' level of the DRM
+    pp_dpm_sclk file, which holds the live frequency) every `period` seconds
+    from a background thread while the timed steps run.  MI355X lowers its
+    clock under sustained matrix-core load, so the held clock says how far
+    the published 2.4 GHz peak is from what the chip ran at."""
+
+    def __init__(self, period: float = 0.005):
+        import glob
+        import threading
+        self.path = None
+        for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+            try:
+                if open(os.path.join(d, "vendor")).read().strip() == "0x1002" and \
+                        os.path.exists(os.path.join(d, "pp_dpm_sclk")):
+                    self.path = os.path.join(d, "pp_dpm_sclk")
+                    break
+            except OSError:
+                continue
+        self.period = period
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+
+    def _read(self):
+        try:
+            for line in open(self.path):
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _loop(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.path:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        s = sorted(self.samples)
+        return {"source": "pp_dpm_sclk (live shader clock) sampled during the timed steps",
+                "median_mhz": s[len(s) // 2], "min_mhz": s[0], "max_mhz": s[-1],
+                "samples": len(s)}
+
+
 def cpu_baseline(w, tokens_sample: int = 12288):
     """The oracle, as it stands, on rank 0 of workload `w` for the first
     `tokens_sample` tokens (a shorter sequence of the same block)."""
@@ -479,11 +538,12 @@ def main():
     t_start = time.perf_counter()
     g0 = torch.cuda.Event(enable_timing=True)
     g1 = torch.cuda.Event(enable_timing=True)
-    g0.record(stream)
-    for _ in range(args.steps):
-        step(ev)
-    g1.record(stream)
-    torch.cuda.synchronize()
+    with ClockSampler() as clock:
+        g0.record(stream)
+        for _ in range(args.steps):
+            step(ev)
+        g1.record(stream)
+        torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     gpu_ms = g0.elapsed_time(g1)
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
@@ -529,6 +589,10 @@ def main():
                 "frac": k["frac"]}
     roof["kernel"] = dom
     roof["traffic"] = load_traffic(dom, src)
+    clk = clock.summary()
+    if clk and bound == "mfma":
+        # the same rate against the peak at the clock the chip held
+        clk["frac_at_held_clock"] = round(k["frac"] * 2400.0 / clk["median_mhz"], 4)
 
     st.close()
 
@@ -556,6 +620,7 @@ def main():
         "mfma_peak_frac": None if loading else round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "config": st.config,
         "roofline": roof,
+        "clock": clk,
         "kernels": per_kernel,
         "cpu_baseline": cpu,
     }
