@@ -306,6 +306,25 @@ TP_API tp_status tp_attn_heads_block_split(tp_block_shard *shard, int64_t q_toke
                                            float *lse_parts, int64_t ld_lse,
                                            int64_t lse_part_stride, void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): tp_attn_heads_split
+ * followed by tp_attn_merge in one call, writing tp_attn_heads' result
+ * o[tokens, D_r] (bf16, ldo >= D_r) with the n_splits partial outputs and
+ * log-sum-exps held in the library's own device scratch array instead of
+ * caller buffers.  It allocates nothing and calls no allocating routine.
+ * The array is 64 MiB, a file-scope device variable, so every GPU the
+ * library runs on holds one copy until the process ends; a call needs
+ * n_splits * tokens * (D_r + H/P) * 4 bytes of it and larger requests fail
+ * with TP_ERR_ARG (the detail text gives both sizes).  Every call on a GPU
+ * uses that GPU's one array, whose contents the next call overwrites: calls
+ * that overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  1 <= n_splits <= 16 (else TP_ERR_ARG /
+ * TP_ERR_UNSUPPORTED), n_splits <= tokens; bf16 and head_dim 128 only; o
+ * must not overlap qkv; tokens == 0 is a no-op. */
+TP_API tp_status tp_attn_heads_split_noalloc(tp_block_shard *shard, int64_t tokens, const void *qkv,
+                                             int64_t ldqkv, int32_t n_splits, void *o, int64_t ldo,
+                                             void *stream);
+
 /* Host-only query: the n_splits (1..4) at which tp_attn_heads_split over
  * `tokens` tokens fills the GPU with its long-sequence kernel -- 1 when
  * tp_attn_heads already does (or the shard has no attention, or tokens < 1).

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     TP_MLP_DOWN, TP_MLP_GELU_TANH, TP_MLP_SWIGLU, TP_MLP_UP, TP_OK, TP_QKV, TpBlockConfig, TpBlockShard,
     TpBlockWeights, TpError, lib, make_config, status_string, tp_attn_heads,
     tp_attn_heads_block, tp_attn_heads_block_split, tp_attn_heads_split, tp_attn_merge,
+    tp_attn_heads_split_noalloc,
     tp_attn_split_hint,
     tp_block_shard_create, tp_block_shard_destroy, tp_block_shard_load, tp_colwise_linear,
     tp_colwise_qkv_up, tp_last_error_detail, tp_partial_reduce,

@@ -48,6 +48,7 @@ EXPORTED = (
     "tp_rowwise_split_input_partial", "tp_attn_heads_block", "tp_attn_merge",
     "tp_attn_heads_split", "tp_attn_split_hint", "tp_ulysses_seq_to_heads",
     "tp_ulysses_heads_to_seq", "tp_block_shard_load", "tp_attn_heads_block_split",
+    "tp_attn_heads_split_noalloc",
 )
 
 
@@ -111,6 +112,7 @@ def lib() -> ctypes.CDLL:
                                                      ctypes.c_int, vp]
         L.tp_attn_heads_block.argtypes = [vp, i64, vp, i64, i64, vp, i64, vp, i64, vp, i64, vp]
         L.tp_attn_heads_split.argtypes = [vp, i64, vp, i64, i32, vp, i64, i64, vp, i64, i64, vp]
+        L.tp_attn_heads_split_noalloc.argtypes = [vp, i64, vp, i64, i32, vp, i64, vp]
         L.tp_attn_heads_block_split.argtypes = [vp, i64, vp, i64, i64, vp, i64, i32, vp, i64, i64,
                                                 vp, i64, i64, vp]
         L.tp_ulysses_seq_to_heads.argtypes = [ctypes.POINTER(vp), i32, i64, i64, i64, i64, i32, i32,
@@ -127,6 +129,7 @@ def lib() -> ctypes.CDLL:
                   "tp_attn_heads", "tp_rowwise_linear_partial", "tp_partial_reduce",
                   "tp_rowwise_split_input_partial", "tp_attn_heads_block", "tp_attn_merge",
                   "tp_attn_heads_split", "tp_attn_heads_block_split", "tp_ulysses_seq_to_heads",
+                  "tp_attn_heads_split_noalloc",
                   "tp_ulysses_heads_to_seq"):
             getattr(L, f).restype = ctypes.c_int
         L.tp_status_string.argtypes = [ctypes.c_int]
@@ -375,6 +378,17 @@ def tp_attn_heads_split(shard: TpBlockShard, tokens: int, qkv, o_parts, lse_part
     lp, ldl = _mat(lse_parts[0], "lse_parts[0]", tokens, shard.heads_r, TP_F32)
     _check(lib().tp_attn_heads_split(shard.handle, tokens, qp, ldq, S, op, ldo, o_parts.stride(0),
                                      lp, ldl, lse_parts.stride(0), _stream(stream)))
+
+
+def tp_attn_heads_split_noalloc(shard: TpBlockShard, tokens: int, qkv, o, n_splits: int,
+                                stream=None) -> None:
+    """tp_attn_heads_split + tp_attn_merge in one call, the partial results in
+    the library's per-GPU scratch array (no allocation; calls overlapping on
+    one GPU race)."""
+    qp, ldq = _mat(qkv, "qkv", tokens, 3 * shard.d_r, shard.dtype)
+    op, ldo = _mat(o, "o", tokens, shard.d_r, shard.dtype)
+    _check(lib().tp_attn_heads_split_noalloc(shard.handle, tokens, qp, ldq, int(n_splits), op, ldo,
+                                             _stream(stream)))
 
 
 def tp_attn_split_hint(shard: TpBlockShard, tokens: int) -> int:

@@ -14,6 +14,7 @@
 #include <fcntl.h>
 #include <unistd.h>
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -673,6 +674,100 @@ TP_API tp_status tp_attn_heads_split(tp_block_shard* s, int64_t tokens, const vo
                                      int64_t lse_part_stride, void* stream) {
   return attn_parts(s, tokens, qkv, ldqkv, tokens, qkv, ldqkv, n_splits, o_parts, ldo, o_part_stride,
                     lse_parts, ld_lse, lse_part_stride, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free split attention: the partial outputs and log-sum-exps of
+// the key ranges live in `scratch`, one file-scope device array per GPU,
+// instead of caller buffers.  In host code `scratch` names a host-side stand-in
+// for the array, not its device address: that is looked up once per device
+// (with the device current) and kept in scratch_ptr.
+static constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxScratchDevices];
+
+tp_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(TP_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table covers", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the scratch array");
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return TP_OK;
+}
+
+}  // namespace
+
+TP_API tp_status tp_attn_heads_split_noalloc(tp_block_shard* s, int64_t tokens, const void* qkv,
+                                             int64_t ldqkv, int32_t n_splits, void* o, int64_t ldo,
+                                             void* stream) {
+  tp_status st = check_shard(s);
+  if (st != TP_OK) return st;
+  if (!s->attn) return fail(TP_ERR_ARG, "shard has no attention layers");
+  if (s->cfg.dtype != TP_BF16) return fail(TP_ERR_UNSUPPORTED, "attention is built for bf16 only");
+  if (s->d != 128) return fail(TP_ERR_UNSUPPORTED, "attention is built for head_dim 128 only");
+  if ((st = check_tokens(tokens)) != TP_OK) return st;
+  if (n_splits < 1) return fail(TP_ERR_ARG, "n_splits (%d) < 1", n_splits);
+  if (n_splits > tpk::kMaxMergeParts)
+    return fail(TP_ERR_UNSUPPORTED, "n_splits (%d) > %d", n_splits, tpk::kMaxMergeParts);
+  const int64_t Dr = s->Dr, Hr = s->Hr;
+  if ((st = check_matrix("qkv", qkv, ldqkv, 3 * Dr, s->es)) != TP_OK) return st;
+  if ((st = check_matrix("o", o, ldo, Dr, s->es)) != TP_OK) return st;
+  if (tokens == 0) return TP_OK;
+  if (tokens < n_splits) return fail(TP_ERR_ARG, "fewer tokens than key splits");
+  if (overlap(qkv, span_bytes(tokens, ldqkv, 3 * Dr, s->es), o, span_bytes(tokens, ldo, Dr, s->es)))
+    return fail(TP_ERR_ARG, "o overlaps qkv");
+  // parts, contiguous: n_splits x [tokens, D_r] fp32 outputs, then
+  // n_splits x [tokens, H/P] fp32 log-sum-exps (D_r is a multiple of 128, so
+  // every part starts 16-byte aligned)
+  const int64_t o_part = tokens * Dr, l_part = tokens * Hr;
+  const int64_t need = (int64_t)n_splits * (o_part + l_part) * (int64_t)sizeof(float);
+  if (need > kScratchBytes)
+    return fail(TP_ERR_ARG, "%d key splits of %lld tokens need %lld bytes of scratch; the maximum is %lld",
+                n_splits, (long long)tokens, (long long)need, (long long)kScratchBytes);
+  void* base = nullptr;
+  if ((st = scratch_of_current_device(&base)) != TP_OK) return st;
+  float* o_parts = static_cast<float*>(base);
+  float* l_parts = o_parts + n_splits * o_part;
+  const char* kv = static_cast<const char*>(qkv);
+  const tpk::AttnBlockArgs a{qkv, ldqkv, kv + Dr * s->es, kv + 2 * Dr * s->es, ldqkv,
+                             (int)tokens, (int)tokens, (int)Hr, o_parts, Dr, l_parts, Hr,
+                             n_splits, o_part, l_part};
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = tpk::launch_attn_block_bf16_d128(a, hs);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  tpk::MergeArgs m{};
+  for (int i = 0; i < n_splits; ++i) {
+    m.o[i] = o_parts + i * o_part;
+    m.lse[i] = l_parts + i * l_part;
+  }
+  m.n = n_splits;
+  m.ldo_in = Dr;
+  m.ld_lse_in = Hr;
+  m.T = (int)tokens;
+  m.heads = (int)Hr;
+  m.head_dim = (int)s->d;
+  m.out = o;
+  m.out_bf16 = true;
+  m.ldo = ldo;
+  m.lse_out = nullptr;
+  m.ld_lse_out = 0;
+  e = tpk::launch_attn_merge(m, hs);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return TP_OK;
 }
 
 TP_API int32_t tp_attn_split_hint(const tp_block_shard* s, int64_t tokens) {
