@@ -33,14 +33,22 @@
 //     score: one FMA (scale folded in) and one exp2; the row sum is a bf16
 //     dot2 over the packed weights; the accumulator is rescaled by
 //     exp2(m_old - m_new) only when a row max outgrows the reference by 8
-//     (log2 units).  Keys past T get -inf (last tile only); query rows past T
+//     (log2 units).  The row max itself is taken only for a tile whose
+//     weights, computed against the current reference, lift a lane's row
+//     sum by more than 128 (any score past the slack does), so most tiles
+//     skip it.  Keys past T get -inf (last tile only); query rows past T
 //     are clamped on load and not stored.
+//   * The long-sequence kernel's main loop covers four tiles per iteration,
+//     one per LDS stage, so the stage offsets of its LDS reads are
+//     instruction immediates rather than per-tile address arithmetic.
 //   * Queries and keys/values may come from different tensors and lengths
 //     (a K/V block of a longer sequence, the Ring Attention step of the
 //     Diffusers context-parallelism page): the block form stores the
 //     normalised output in fp32 and the natural log-sum-exp of the scaled
 //     scores, lse = ln 2 * (m + log2 l), for the merge.
 #include "tp_kernels.h"
+
+#include <type_traits>
 
 namespace tpk {
 namespace {
@@ -82,6 +90,65 @@ constexpr float kRescaleSlack = 8.0f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// A score exceeds the reference by more than the slack exactly when its
+// weight exp2(s * scale_log2 - m_ref) exceeds 2^8, which lifts its lane's
+// row sum by more than 128 within the tile.  So each tile's weights are
+// computed against the current reference first, and the row max -- needed
+// only to apply the rule -- is taken only when some lane's sum grew by more
+// than that, or on the first tile (m_ref still -inf, the same in every lane;
+// its provisional weights are not finite).  Otherwise the weights and sum
+// are already those the rule gives, bit for bit, since it would leave the
+// reference unchanged.  After the first tile the reference is finite, so a
+// weight is finite or +inf and the sum is never NaN: the check is an
+// ordinary comparison (this file is built without NaN semantics).
+constexpr float kSumGuard = 128.0f;
+
+__device__ __forceinline__ bool sum_check(float m_ref, float l, float l_before) {
+  return __builtin_amdgcn_ballot_w64(m_ref == -INFINITY || l > l_before + kSumGuard) != 0;
+}
+
+// Weight pair q (0..15) of a 64-key tile: scores (c, e), (c, e + 1) with
+// c = q / 8, e = 2 (q % 8); packed to bf16 for the PV product, and the row
+// sum adds the bf16 values the product uses.
+__device__ __forceinline__ void weight_pair(const f32x16 (&s)[2], int q, float scale_log2, float m,
+                                            float& l, bf16x8 (&pb)[2][2]) {
+  const int c = q >> 3, e = 2 * (q & 7);
+  const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
+  const float p0 = __builtin_amdgcn_exp2f(fmaf(s[c][e], scale_log2, -m));
+  const float p1 = __builtin_amdgcn_exp2f(fmaf(s[c][e + 1], scale_log2, -m));
+  const bf16x2 pp = {static_cast<bf16>(p0), static_cast<bf16>(p1)};
+  l = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l, false);
+  pb[c][e >> 3][e & 7] = pp[0];
+  pb[c][e >> 3][(e & 7) + 1] = pp[1];
+}
+
+// The reference rule, for a tile whose sum check fired: with the row max
+// (this lane's 32 scores, then the other half-wave's), rescale when some
+// row's max outgrew the reference by the slack -- the accumulator, the sum
+// before the tile (l_before) and the tile's weights, recomputed against the
+// new reference.  Otherwise l and pb stand.
+__device__ __forceinline__ void reference_rule(const f32x16 (&s)[2], float scale_log2, int half,
+                                               float& m_ref, float l_before, float& l,
+                                               bf16x8 (&pb)[2][2], f32x16 (&acc_o)[kD / 32]) {
+  float mloc = s[0][0];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s[c][e]);
+  mloc = fmaxf(mloc, other_half(mloc, half)) * scale_log2;
+  if (__builtin_amdgcn_ballot_w64(mloc > m_ref + kRescaleSlack) == 0) return;
+  const float m_new = fmaxf(m_ref, mloc);
+  const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+  m_ref = m_new;
+  l = l_before * alpha;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) weight_pair(s, q, scale_log2, m_new, l, pb);
+#pragma unroll
+  for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc_o[t][e] *= alpha;
+}
 
 // Operands of one launch: head j's Q, K, V at columns j*128 of q, k, v.
 // Key split z of kv_splits (the grid's z index; the pipelined kernel takes
@@ -179,39 +246,14 @@ __device__ __forceinline__ void attn_tile(const u32x4* __restrict__ sK, const u3
         if (key >= T) s[c][e] = -INFINITY;
       }
   }
-  // tile max of this lane's 32 scores, then of the other half-wave's 32
-  float mloc = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-  for (int e = 2; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s[0][e], s[0][e + 1]));
-#pragma unroll
-  for (int e = 0; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s[1][e], s[1][e + 1]));
-  mloc = fmaxf(mloc, other_half(mloc, half)) * scale_log2;
-  // rescale only when some row's max outgrew the reference by the slack
-  if (__builtin_amdgcn_ballot_w64(mloc > m_ref + kRescaleSlack)) {
-    const float m_new = fmaxf(m_ref, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-    m_ref = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int t = 0; t < kD / 32; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc_o[t][e] *= alpha;
-  }
-  // p = exp2(s * log2(e)/sqrt(d) - m_ref), packed to bf16 for the PV product;
-  // the row sum adds the bf16 values the product actually uses
+  // weights against the current reference; the reference rule only when the
+  // sum check fires (see kSumGuard)
   bf16x8 pb[2][2];
-  const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
+  const float l_before = l_run;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[c][e], scale_log2, -m_ref));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[c][e + 1], scale_log2, -m_ref));
-      const bf16x2 pp = {static_cast<bf16>(p0), static_cast<bf16>(p1)};
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
-      pb[c][e >> 3][e & 7] = pp[0];
-      pb[c][e >> 3][(e & 7) + 1] = pp[1];
-    }
+  for (int q = 0; q < 16; ++q) weight_pair(s, q, scale_log2, m_ref, l_run, pb);
+  if (sum_check(m_ref, l_run, l_before))
+    reference_rule(s, scale_log2, half, m_ref, l_before, l_run, pb, acc_o);
   // O^T += V^T P^T.  The P^T operand element j of this lane is key
   // 8 (j / 4) + 4 half + (j % 4) of each 16-key step; the V^T operand is read
   // transposed from row-major V: in each 16-lane group, source lane 4 r + cc
@@ -409,8 +451,7 @@ attn_fwd_pipe(AttnIO io) {
     loff_last[j] = (uint32_t)((int64_t)rlast * io.ldkv * 2 + 16 * c);
   }
   const int64_t tile_bytes = (int64_t)kBKV * io.ldkv * 2;
-  auto load_tile = [&](int kt) {
-    const int buf = kt % NSTAGE;
+  auto load_tile = [&](int kt, int buf) {   // buf = kt % NSTAGE
     const int tt = min(kt, nkt - 1);
     const bool full = tt < nfull;
     const int64_t toff = (int64_t)tt * tile_bytes;
@@ -462,7 +503,6 @@ attn_fwd_pipe(AttnIO io) {
   const int fA = swz(keyA), fB = swz(keyB);
   const int dsub = 16 * ((lane >> 4) & 1) + 4 * cc;
   const int off8 = (dsub & 7) * 2;
-  const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
 
   // K operand of score MFMA i of a tile: key half c = i & 1, k-step
   // st = i >> 1, so neighbouring MFMAs feed different accumulators.
@@ -493,7 +533,11 @@ attn_fwd_pipe(AttnIO io) {
   // tell these reads from the LDS-bound loads in flight and adds no wait for
   // them (the vmcnt wait before each barrier orders every tile's loads before
   // its reads, and a tile's loads get two iterations to land).
-  auto step = [&](int kt, f32x16 (&s_cur)[NQ][2], f32x16 (&s_nxt)[NQ][2]) {
+  auto step = [&](int kt, auto stage_c, f32x16 (&s_cur)[NQ][2], f32x16 (&s_nxt)[NQ][2]) {
+    // stage_c: kt % NSTAGE as a compile-time constant (the LDS addresses of
+    // the tile's reads then fold into the instructions' offsets), or -1
+    constexpr int J = decltype(stage_c)::value;
+    const int cur = J >= 0 ? J : kt % NSTAGE;
     if (kt * kBKV + kBKV > T) {  // last, partial tile: mask keys past T
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -503,8 +547,8 @@ attn_fwd_pipe(AttnIO io) {
           if (key >= T) s_cur[0][c][e] = -INFINITY;
         }
     }
-    load_tile(kt + 3);
-    const u32x4* __restrict__ sKb = sK[(kt + 1) % NSTAGE];
+    load_tile(kt + 3, (cur + 3) % NSTAGE);
+    const u32x4* __restrict__ sKb = sK[(cur + 1) % NSTAGE];
     constexpr int KPF = 6;
     bf16x8 kf[16];
 #pragma unroll
@@ -513,59 +557,29 @@ attn_fwd_pipe(AttnIO io) {
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s_nxt[0][c][e] = 0.0f;
-    float m0 = 0.0f, mloc = 0.0f, m_new = m_ref[0], alpha = 1.0f, l = l_run[0];
-    bool rescale = false;
+    // Score MFMA i, then weight pair i of tile kt against the current
+    // reference; the reference rule only when the sum check fires (see
+    // kSumGuard), before the PV MFMAs.
+    const float l_before = l_run[0];
+    float l = l_before;
     bf16x8 pb[2][2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       s_nxt[0][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[0][i >> 1], s_nxt[0][i & 1], 0, 0, 0);
       if (i + KPF < 16) kf[i + KPF] = kread(sKb, i + KPF);
       __builtin_amdgcn_sched_barrier(0);
-      if (i == 0) {
-        m0 = fmaxf(s_cur[0][0][0], s_cur[0][0][1]);
-#pragma unroll
-        for (int e = 2; e < 16; e += 2) m0 = fmaxf(m0, fmaxf(s_cur[0][0][e], s_cur[0][0][e + 1]));
-      } else if (i == 1) {
-        mloc = m0;
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) mloc = fmaxf(mloc, fmaxf(s_cur[0][1][e], s_cur[0][1][e + 1]));
-      } else if (i == 2) {
-        // rescale only when some row's max outgrew the reference by the slack
-        mloc = fmaxf(mloc, other_half(mloc, half)) * scale_log2;
-        rescale = __builtin_amdgcn_ballot_w64(mloc > m_ref[0] + kRescaleSlack) != 0;
-        m_new = rescale ? fmaxf(m_ref[0], mloc) : m_ref[0];
-        alpha = __builtin_amdgcn_exp2f(m_ref[0] - m_new);
-        m_ref[0] = m_new;
-        l *= alpha;
-      } else {
-        // p = exp2(s * log2(e)/sqrt(d) - m_ref), packed to bf16 for the PV
-        // product; the row sum adds the bf16 values the product uses
-#pragma unroll
-        for (int q = ((i - 3) * 16) / 13; q < ((i - 2) * 16) / 13; ++q) {
-          const int c = q >> 3, e = 2 * (q & 7);
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[0][c][e], scale_log2, -m_new));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[0][c][e + 1], scale_log2, -m_new));
-          const bf16x2 pp = {static_cast<bf16>(p0), static_cast<bf16>(p1)};
-          l = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l, false);
-          pb[c][e >> 3][e & 7] = pp[0];
-          pb[c][e >> 3][(e & 7) + 1] = pp[1];
-        }
-      }
+      weight_pair(s_cur[0], i, scale_log2, m_ref[0], l, pb);
       __builtin_amdgcn_sched_barrier(0);
     }
-    l_run[0] = l;
-    // the weights are used only after the rescale branch; without this, IR
+    // the weights are used only after the check's branch; without this, IR
     // passes sink their computation into the PV block, away from the score
     // MFMAs it is interleaved with
     asm volatile("" :: "v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]), "v"(l));
-    if (rescale) {
-#pragma unroll
-      for (int t = 0; t < kD / 32; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc_o[0][t][e] *= alpha;
-    }
+    if (sum_check(m_ref[0], l, l_before))
+      reference_rule(s_cur[0], scale_log2, half, m_ref[0], l_before, l, pb, acc_o[0]);
+    l_run[0] = l;
     // O^T += V^T P^T
-    const u32x4* __restrict__ sVb = sV[kt % NSTAGE];
+    const u32x4* __restrict__ sVb = sV[cur];
     bf16x8 vf[4][kD / 32];
 #pragma unroll
     for (int cu = 0; cu < 2; ++cu)
@@ -581,18 +595,31 @@ attn_fwd_pipe(AttnIO io) {
     barrier_keep_newest_loads<PER_WAVE>();
   };
 
-  load_tile(0);
-  load_tile(1);
-  load_tile(2);
+  load_tile(0, 0);
+  load_tile(1, 1);
+  load_tile(2, 2);
   __syncthreads();
   f32x16 sa[NQ][2], sb[NQ][2];
   scores(sK[0], sa);
+  // four tiles per iteration, one per LDS stage; the last nkt % 4 with the
+  // stage computed at run time
+  using Stage0 = std::integral_constant<int, 0>;
+  using Stage1 = std::integral_constant<int, 1>;
+  using Stage2 = std::integral_constant<int, 2>;
+  using Stage3 = std::integral_constant<int, 3>;
+  using StageR = std::integral_constant<int, -1>;
   int kt = 0;
-  for (; kt + 1 < nkt; kt += 2) {
-    step(kt, sa, sb);
-    step(kt + 1, sb, sa);
+  for (; kt + 3 < nkt; kt += 4) {
+    step(kt, Stage0{}, sa, sb);
+    step(kt + 1, Stage1{}, sb, sa);
+    step(kt + 2, Stage2{}, sa, sb);
+    step(kt + 3, Stage3{}, sb, sa);
   }
-  if (kt < nkt) step(kt, sa, sb);
+  for (; kt + 1 < nkt; kt += 2) {
+    step(kt, StageR{}, sa, sb);
+    step(kt + 1, StageR{}, sb, sa);
+  }
+  if (kt < nkt) step(kt, StageR{}, sa, sb);
 
 #pragma unroll
   for (int a = 0; a < NQ; ++a)
