@@ -557,20 +557,32 @@ attn_fwd_pipe(AttnIO io) {
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s_nxt[0][c][e] = 0.0f;
-    // Score MFMA i, then weight pair i of tile kt against the current
-    // reference; the reference rule only when the sum check fires (see
-    // kSumGuard), before the PV MFMAs.
+    // Score MFMAs 2j, 2j + 1, then weight pairs 2j, 2j + 1 of tile kt against
+    // the current reference; the reference rule only when the sum check
+    // fires (see kSumGuard), before the PV MFMAs.
+    //
+    // The two waves of a SIMD (w and w + 4) start each tile together at the
+    // barrier, and the older one wins issue: it finishes the tile first and
+    // then idles at the next barrier while the other finishes alone.  Waves
+    // 4-7 therefore take the top issue priority for this phase (the one
+    // with the vector work), which evens the two out.
     const float l_before = l_run[0];
     float l = l_before;
     bf16x8 pb[2][2];
+    if (wave >= NW / 2) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s_nxt[0][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[0][i >> 1], s_nxt[0][i & 1], 0, 0, 0);
-      if (i + KPF < 16) kf[i + KPF] = kread(sKb, i + KPF);
+    for (int i0 = 0; i0 < 16; i0 += 2) {
+#pragma unroll
+      for (int i = i0; i < i0 + 2; ++i) {
+        s_nxt[0][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[0][i >> 1], s_nxt[0][i & 1], 0, 0, 0);
+        if (i + KPF < 16) kf[i + KPF] = kread(sKb, i + KPF);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      weight_pair(s_cur[0], i, scale_log2, m_ref[0], l, pb);
+      weight_pair(s_cur[0], i0, scale_log2, m_ref[0], l, pb);
+      weight_pair(s_cur[0], i0 + 1, scale_log2, m_ref[0], l, pb);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // the weights are used only after the check's branch; without this, IR
     // passes sink their computation into the PV block, away from the score
     // MFMAs it is interleaved with
