@@ -8,11 +8,6 @@
 // of the packed qkv tensor [T, 3*Dr].
 //
 // Design:
-//   * 32 queries per wave, <= 256 VGPRs so two waves share each SIMD.  Short
-//     sequences: 4-wave workgroups, two per CU.  Long sequences: the
-//     software-pipelined form below, 8-wave workgroups sharing each K/V tile
-//     among 256 queries, in which each wave overlaps the next tile's score
-//     MFMAs with this tile's softmax.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (A = a 32-key slab of K from LDS, B = the
 //     wave's Q^T held in registers for the whole kernel).  In the 32x32
@@ -23,24 +18,20 @@
 //     V^T A-operand is read from row-major V with the transposing LDS read
 //     ds_read_b64_tr_b16 (in each 16-lane group, source lane 4 r + c points
 //     at V[k + r][d + 4 c] and lane i receives V[k + e][d + i], e = 0..3).
-//   * K and V tiles of 64 keys go global -> LDS directly
-//     (global_load_lds_dwordx4) into LDS rows of 256 bytes with an XOR chunk
-//     swizzle that keeps both the K reads and the transposed V reads
-//     conflict-free; one barrier per tile.  The 4-wave kernel double-buffers
-//     one tile ahead, the long-sequence kernel keeps four stages and fetches
-//     three tiles ahead.
-//   * Softmax runs in the exp2 domain with few vector instructions per
-//     score: one FMA (scale folded in) and one exp2; the row sum is a bf16
-//     dot2 over the packed weights; the accumulator is rescaled by
-//     exp2(m_old - m_new) only when a row max outgrows the reference by 8
-//     (log2 units).  The row max itself is taken only for a tile whose
-//     weights, computed against the current reference, lift a lane's row
-//     sum by more than 128 (any score past the slack does), so most tiles
-//     skip it.  Keys past T get -inf (last tile only); query rows past T
-//     are clamped on load and not stored.
-//   * The long-sequence kernel's main loop covers four tiles per iteration,
-//     one per LDS stage, so the stage offsets of its LDS reads are
-//     instruction immediates rather than per-tile address arithmetic.
+//   * K and V tiles of 64 keys go global -> LDS directly into LDS rows of 256
+//     bytes with an XOR chunk swizzle that keeps both the K reads and the
+//     transposed V reads conflict-free.
+//   * Softmax in the exp2 domain; the accumulator is rescaled only when a row
+//     max outgrows the running reference by a slack, and the row max itself
+//     is taken only for a tile whose weights, computed against the current
+//     reference, lift a lane's row sum by more than a guard (any score past
+//     the slack does).  Keys past T get -inf (last tile only); query rows
+//     past T are clamped on load and not stored.
+//   * Two kernels.  Short query sets: 4 waves of 32 queries per workgroup,
+//     two workgroups per CU, two waves per SIMD.  Everything else: 4 waves
+//     of 64 queries (one wave per SIMD, one workgroup per CU), in which each
+//     wave interleaves the score MFMAs of the next tile, the PV MFMAs of the
+//     previous one and the softmax of the current one (description below).
 //   * Queries and keys/values may come from different tensors and lengths
 //     (a K/V block of a longer sequence, the Ring Attention step of the
 //     Diffusers context-parallelism page): the block form stores the
@@ -372,146 +363,167 @@ attn_fwd_bf16_d128(AttnIO a) {
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined form for long query sets, launched as NW = 8 waves (two
-// per SIMD, <= 256 VGPRs each) of NQ = 1 sub-tile of 32 queries.  (With NQ
-// sub-tiles a K or V fragment read from LDS would feed NQ MFMAs, but the
-// state of NQ = 2 does not fit the registers of two waves per SIMD, and at
-// one wave per SIMD the compiler spills.)  Within key tile j a wave issues the
-// score MFMAs of tile j+1 in the same straight-line block as the softmax of
-// tile j, one MFMA before each slice of the softmax, so the matrix core and
-// the vector ALU work at the same time inside one wave; then the PV MFMAs of
-// tile j.  Four LDS stages: iteration j reads K of tile j+1
-// and V of tile j, and fetches tile j+3 into the stage tile j-1 used, so
-// every tile's loads have two iterations to land.  Loads past the last tile
-// re-fetch the last tile (harmless, keeps the block branch-free), and the
-// scores computed in the final iteration are discarded.
-template <int N>
-__device__ __forceinline__ void barrier_keep_newest_loads() {
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
+// Long query sets: 64 queries per wave, one wave per SIMD (4-wave workgroups
+// of 256 queries, one per CU).  A K or V fragment read from LDS feeds two
+// MFMAs (the wave's two 32-query blocks), half the LDS bytes per FLOP of 32
+// queries per wave.
+//
+// Each wave's instruction stream alone has to keep the matrix core busy, so
+// one key tile is one straight run of 32 slots, each holding one score MFMA,
+// one PV MFMA and one weight pair:
+//   * score MFMA p: key half 1 of tile kt (p < 16), then key half 0 of tile
+//     kt + 1 (K fragment p / 2 of the 16, feeding both query blocks);
+//   * PV MFMA p of tile kt - 1 (V fragment p / 2, query block p % 2);
+//   * weight pair p of tile kt: blocks (query block 0, key half 0), (1, 0),
+//     (0, 1), (1, 1) -- key half 1 of tile kt is complete by slot 16.
+// A block's scores are thus consumed before the MFMAs of the next tile
+// overwrite it, and one register set holds the scores of both tiles.
+//
+// A weight pair takes two FMAs (scale and reference), two exponentials, one
+// pack and two adds.  The row sum adds the fp32 weights in two accumulators:
+// the bf16 dot product the 4-wave kernel uses waits for the matrix core to
+// drain before it issues, which left it idle for ~20 cycles per weight pair
+// here.
+//
+// The MFMAs are issued from inline asm to pin their registers: the PV
+// accumulators and Q in AGPRs (untouched by the vector code), the scores in
+// VGPRs.  The compiler does not see these as MFMAs, so the fences below
+// provide the wait states between an MFMA writing registers and any other
+// instruction reading or rewriting them.
+//
+// Lazy rescale, as in the other kernels: a tile's weights are computed
+// against the current reference, and only when some lane's row sum grew by
+// more than kSumGuard does the rule run -- here at the end of the tile, from
+// raw scores recomputed out of the tile still resident in LDS (its own
+// registers hold the next tile's scores by then), after the tile's PV MFMAs
+// have drained, so the accumulator rescale sees every earlier tile.
+
+// Rescale slack of this kernel (log2 units) and the row-sum growth that
+// triggers the rule.  Its rule recomputes a tile's scores, so it runs only
+// when a weight may exceed 2^16 (any weight past the slack lifts its lane's
+// sum by more than the guard); fp32 accumulators and bf16 weights hold such
+// values with their full relative precision.
+constexpr float kSlackQ64 = 16.0f;
+constexpr float kGuardQ64 = 65536.0f;
+
+// PV MFMA: accumulator in AGPRs.
+__device__ __forceinline__ void mfma_pv(f32x16& acc, bf16x8 v, bf16x8 p) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
+}
+// Score MFMAs: K fragment in VGPRs, Q in AGPRs, scores in VGPRs; the first
+// k-step starts from zero.
+__device__ __forceinline__ void mfma_s_zero(f32x16& s, bf16x8 k, bf16x8 q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "a"(q));
+}
+__device__ __forceinline__ void mfma_s_acc(f32x16& s, bf16x8 k, bf16x8 q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(k), "a"(q));
+}
+// 24 wait states after the MFMAs writing these registers (an 8-pass MFMA
+// needs fewer before a vector instruction may touch its result).
+__device__ __forceinline__ void fence_s(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void fence_acc(f32x16 (&acc)[2][kD / 32]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                 "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]));
+}
+// After the vector writes of Q into AGPRs, before the first MFMA reads it.
+__device__ __forceinline__ void fence_q(bf16x8 (&qf)[2][kD / 16]) {
+  asm volatile("s_nop 7"
+               : "+a"(qf[0][0]), "+a"(qf[0][1]), "+a"(qf[0][2]), "+a"(qf[0][3]),
+                 "+a"(qf[0][4]), "+a"(qf[0][5]), "+a"(qf[0][6]), "+a"(qf[0][7]),
+                 "+a"(qf[1][0]), "+a"(qf[1][1]), "+a"(qf[1][2]), "+a"(qf[1][3]),
+                 "+a"(qf[1][4]), "+a"(qf[1][5]), "+a"(qf[1][6]), "+a"(qf[1][7]));
+}
+// After vector writes of P operands, before an MFMA reads them.
+__device__ __forceinline__ void fence_p(bf16x8 (&p)[2][2][2]) {
+  asm volatile("s_nop 1"
+               : "+v"(p[0][0][0]), "+v"(p[0][0][1]), "+v"(p[0][1][0]), "+v"(p[0][1][1]),
+                 "+v"(p[1][0][0]), "+v"(p[1][0][1]), "+v"(p[1][1][0]), "+v"(p[1][1][1]));
 }
 
-template <int NQ, int NW, bool LSE>
-__global__ void __launch_bounds__(64 * NW, 1)
-attn_fwd_pipe(AttnIO io) {
-  static_assert(NQ == 1, "one 32-query sub-tile per wave");
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer descriptor over [base, base + bytes): offsets past it read as zero.
+__device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from byte offset voff + soff of the buffer into LDS at
+// dst + 16 lane (dst wave-uniform).
+__device__ __forceinline__ void lds_dma(rsrc_t r, const u32x4* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)voff,
+                                           (int)soff, 0, 0);
+}
+
+template <bool LSE>
+__global__ void __launch_bounds__(256, 1)
+attn_fwd_q64(AttnIO io) {
   constexpr int NSTAGE = 4;
-  constexpr int BQ = NW * 32 * NQ;
-  constexpr int PER_WAVE = 32 / NW;   // 1 KB loads per wave per tile
+  constexpr int BQ = 256;
   __shared__ u32x4 sK[NSTAGE][kBKV * kRowChunks];
   __shared__ u32x4 sV[NSTAGE][kBKV * kRowChunks];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Work order: workgroups are dispatched round-robin over the 8 XCDs (own
-  // L2 each) in linear id order, so the linear id is renumbered to give each
-  // XCD a contiguous run of (query block, head, key split) items, query block
-  // fastest: the workgroups an XCD runs at once are query blocks of one or
-  // two heads and share their K/V tiles in its L2.
+  // XCD-contiguous work order, as in the 8-wave kernel
   const int nqb = gridDim.x, nh = gridDim.y, nb = nqb * nh * gridDim.z;
   const int lin = blockIdx.x + nqb * (blockIdx.y + nh * blockIdx.z);
   const int xcd = lin & 7, per = nb >> 3, rem = nb & 7;
   const int w = xcd * per + min(xcd, rem) + (lin >> 3);
   const int qb = w % nqb, head = (w / nqb) % nh, z = w / (nqb * nh);
-  const int q0 = qb * BQ + wave * 32 * NQ;
+  const int q0 = qb * BQ + wave * 64;
   const int k0 = (int)((int64_t)z * io.Tkv / io.kv_splits);
   const int T = (int)((int64_t)(z + 1) * io.Tkv / io.kv_splits) - k0;   // >= 1
   const bf16* Qg = io.q + head * kD;
-  const bf16* Kg = io.k + head * kD + (int64_t)k0 * io.ldkv;
-  const bf16* Vg = io.v + head * kD + (int64_t)k0 * io.ldkv;
-  const float scale_log2 = io.scale_log2;
   const int half = lane >> 5, l32 = lane & 31;
 
-  bf16x8 qf[NQ][kD / 16];
+  const float scale_log2 = io.scale_log2;
+  // Q^T operands of the two query blocks (queries q0 + 32 a + l32)
+  bf16x8 qf[2][kD / 16];
 #pragma unroll
-  for (int a = 0; a < NQ; ++a) {
+  for (int a = 0; a < 2; ++a) {
     const int64_t row = min(q0 + 32 * a + l32, io.Tq - 1);
 #pragma unroll
     for (int st = 0; st < kD / 16; ++st)
       qf[a][st] = *reinterpret_cast<const bf16x8*>(Qg + row * io.ldq + 16 * st + 8 * half);
   }
+  fence_q(qf);
 
   const int nkt = (T + kBKV - 1) / kBKV;
-  const int nfull = T / kBKV;   // tiles with every key valid
-  // Load n (0..31) of tile kt: K rows (n < 16) or V rows 4 (n & 15) .. + 3;
-  // wave w issues loads PER_WAVE w .. PER_WAVE (w + 1) - 1.  A load's
-  // address is a wave-uniform tile base plus a loop-invariant per-lane 32-bit
-  // offset (row within the tile, chunk); a partial last tile uses offsets
-  // with its rows past T clamped to T - 1.
-  uint32_t loff[PER_WAVE], loff_last[PER_WAVE];
+  const int nfull = T / kBKV;
+  const bool partial = nfull < nkt;
+  // Loads of a tile: 32 of 1 KB (4 rows); wave w issues 8, all of K (w < 2)
+  // or all of V, rows 32 (w & 1) + 4 j + (lane >> 4).  The descriptor ends
+  // at key T of this split: rows past it, and tiles past the last, read as
+  // zero.
+  const uint32_t ldkv2 = (uint32_t)io.ldkv * 2;
+  const bf16* base = (wave < 2 ? io.k : io.v) + head * kD + (int64_t)k0 * io.ldkv;
+  const rsrc_t rs = buffer_rsrc(base, (uint32_t)(T - 1) * ldkv2 + kD * 2);
+  uint32_t loff[8];
 #pragma unroll
-  for (int j = 0; j < PER_WAVE; ++j) {
-    const int n = PER_WAVE * wave + j;
-    const int rr = 4 * (n & 15) + (lane >> 4);
-    const int c = (lane & 15) ^ swz(rr);
-    const int rlast = min(nfull * kBKV + rr, T - 1) - nfull * kBKV;
-    loff[j] = (uint32_t)((int64_t)rr * io.ldkv * 2 + 16 * c);
-    loff_last[j] = (uint32_t)((int64_t)rlast * io.ldkv * 2 + 16 * c);
+  for (int j = 0; j < 8; ++j) {
+    const int rr = 32 * (wave & 1) + 4 * j + (lane >> 4);
+    loff[j] = (uint32_t)rr * ldkv2 + 16 * ((lane & 15) ^ swz(rr));
   }
-  const int64_t tile_bytes = (int64_t)kBKV * io.ldkv * 2;
-  auto load_tile = [&](int kt, int buf) {   // buf = kt % NSTAGE
-    const int tt = min(kt, nkt - 1);
-    const bool full = tt < nfull;
-    const int64_t toff = (int64_t)tt * tile_bytes;
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int n = PER_WAVE * wave + j;
-      const char* src = reinterpret_cast<const char*>(n < 16 ? Kg : Vg) + toff +
-                        (full ? loff[j] : loff_last[j]);
-      u32x4* dst = (n < 16 ? sK[buf] : sV[buf]) + 64 * (n & 15);
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                       (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
-    }
+  const uint32_t tile_bytes = (uint32_t)kBKV * ldkv2;
+  auto load = [&](int kt, int stage, int j) {
+    u32x4* dst = (wave < 2 ? sK[stage] : sV[stage]) + 64 * (8 * (wave & 1) + j);
+    lds_dma(rs, dst, loff[j], (uint32_t)kt * tile_bytes);
   };
 
-  auto scores = [&](const u32x4* __restrict__ sKb, f32x16 (&s)[NQ][2]) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int a = 0; a < NQ; ++a)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[a][c][e] = 0.0f;
-      const int row = 32 * c + l32;
-      const u32x4* kb = sKb + row * kRowChunks;
-      const int f = swz(row);
-#pragma unroll
-      for (int st = 0; st < kD / 16; ++st) {
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, kb[(2 * st + half) ^ f]);
-#pragma unroll
-        for (int a = 0; a < NQ; ++a)
-          s[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[a][st], s[a][c], 0, 0, 0);
-      }
-    }
+  // K operand of key half c, k-step st: rows 32 c + l32, dims 16 st + 8 half
+  auto kread = [&](const u32x4* __restrict__ sKb, int c, int st) {
+    const int row = 32 * c + l32;
+    return __builtin_bit_cast(bf16x8, sKb[row * kRowChunks + ((2 * st + half) ^ swz(row))]);
   };
-
-  f32x16 acc_o[NQ][kD / 32];
-#pragma unroll
-  for (int a = 0; a < NQ; ++a)
-#pragma unroll
-    for (int t = 0; t < kD / 32; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc_o[a][t][e] = 0.0f;
-  float m_ref[NQ], l_run[NQ];
-#pragma unroll
-  for (int a = 0; a < NQ; ++a) { m_ref[a] = -INFINITY; l_run[a] = 0.0f; }
-
-  // V^T operand addressing (see attn_tile): per lane constants
+  // V^T operand of key step cu (16 keys), dim block t: two transposing reads
   const int gi = lane & 15, r = gi >> 2, cc = gi & 3;
   const int keyA = 4 * half + r, keyB = keyA + 8;
   const int fA = swz(keyA), fB = swz(keyB);
   const int dsub = 16 * ((lane >> 4) & 1) + 4 * cc;
   const int off8 = (dsub & 7) * 2;
-
-  // K operand of score MFMA i of a tile: key half c = i & 1, k-step
-  // st = i >> 1, so neighbouring MFMAs feed different accumulators.
-  auto kread = [&](const u32x4* __restrict__ sKb, int i) {
-    const int row = 32 * (i & 1) + l32;
-    return __builtin_bit_cast(bf16x8, sKb[row * kRowChunks + ((2 * (i >> 1) + half) ^ swz(row))]);
-  };
-  // V^T operand of PV MFMA (cu, t): keys 32 c + 16 u .. + 15 (cu = 2 c + u)
-  // of dims 32 t .. + 31, two transposing reads.
   auto vread = [&](const u32x4* __restrict__ sVb, int cu, int t) {
     const int lchunk = (32 * t + dsub) >> 3;
     const int kb = 32 * (cu >> 1) + 16 * (cu & 1);
@@ -521,120 +533,269 @@ attn_fwd_pipe(AttnIO io) {
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pbp));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
+  f32x16 s[2][2];   // scores, [query block][key half]
+  // keys past T get -inf (last tile only)
+  auto mask_half = [&](int kt, int c) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kt * kBKV + 32 * c + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (key >= T) s[a][c][e] = -INFINITY;
+      }
+  };
 
-  // One key tile: s_cur holds the raw scores of tile kt; the scores of tile
-  // kt + 1 go to s_nxt.  Score MFMA i (K read KPF MFMAs ahead) is followed by
-  // slice i of the softmax of tile kt: slices 0-1 the row max, 2 the
-  // reference update, 3-15 the exponentials, weights and row sum.  The
-  // scheduling fences keep that order, so the matrix core and the vector ALU
-  // of the wave work side by side.  Then the rare rescale of the accumulator
-  // and the PV MFMAs, in (key block, dim block) order with the V reads two
-  // key blocks ahead; the LDS pointers are __restrict__ so the compiler can
-  // tell these reads from the LDS-bound loads in flight and adds no wait for
-  // them (the vmcnt wait before each barrier orders every tile's loads before
-  // its reads, and a tile's loads get two iterations to land).
-  auto step = [&](int kt, auto stage_c, f32x16 (&s_cur)[NQ][2], f32x16 (&s_nxt)[NQ][2]) {
-    // stage_c: kt % NSTAGE as a compile-time constant (the LDS addresses of
-    // the tile's reads then fold into the instructions' offsets), or -1
-    constexpr int J = decltype(stage_c)::value;
-    const int cur = J >= 0 ? J : kt % NSTAGE;
-    if (kt * kBKV + kBKV > T) {  // last, partial tile: mask keys past T
+  f32x16 acc_o[2][kD / 32];
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kt * kBKV + 32 * c + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (key >= T) s_cur[0][c][e] = -INFINITY;
-        }
-    }
-    load_tile(kt + 3, (cur + 3) % NSTAGE);
-    const u32x4* __restrict__ sKb = sK[(cur + 1) % NSTAGE];
-    constexpr int KPF = 6;
-    bf16x8 kf[16];
+    for (int t = 0; t < kD / 32; ++t)
 #pragma unroll
-    for (int i = 0; i < KPF; ++i) kf[i] = kread(sKb, i);
+      for (int e = 0; e < 16; ++e) acc_o[a][t][e] = 0.0f;
+  float m_ref[2], l_run[2] = {0.0f, 0.0f};   // references in log2 units of the scaled scores
+  bf16x8 kf[3], vf[3];
+  bf16x8 pA[2][2][2], pB[2][2][2];
+
+  // row max of query block a over the raw scores in s[a] (both lane halves),
+  // scaled to log2 units
+  auto row_max = [&](int a) {
+    float m = s[a][0][0];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s_nxt[0][c][e] = 0.0f;
-    // Score MFMAs 2j, 2j + 1, then weight pairs 2j, 2j + 1 of tile kt against
-    // the current reference; the reference rule only when the sum check
-    // fires (see kSumGuard), before the PV MFMAs.
-    //
-    // The two waves of a SIMD (w and w + 4) start each tile together at the
-    // barrier, and the older one wins issue: it finishes the tile first and
-    // then idles at the next barrier while the other finishes alone.  Waves
-    // 4-7 therefore take the top issue priority for this phase (the one
-    // with the vector work), which evens the two out.
-    const float l_before = l_run[0];
-    float l = l_before;
-    bf16x8 pb[2][2];
-    if (wave >= NW / 2) __builtin_amdgcn_s_setprio(3);
-#pragma unroll
-    for (int i0 = 0; i0 < 16; i0 += 2) {
-#pragma unroll
-      for (int i = i0; i < i0 + 2; ++i) {
-        s_nxt[0][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[0][i >> 1], s_nxt[0][i & 1], 0, 0, 0);
-        if (i + KPF < 16) kf[i + KPF] = kread(sKb, i + KPF);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      weight_pair(s_cur[0], i0, scale_log2, m_ref[0], l, pb);
-      weight_pair(s_cur[0], i0 + 1, scale_log2, m_ref[0], l, pb);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __builtin_amdgcn_s_setprio(0);
-    // the weights are used only after the check's branch; without this, IR
-    // passes sink their computation into the PV block, away from the score
-    // MFMAs it is interleaved with
-    asm volatile("" :: "v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]), "v"(l));
-    if (sum_check(m_ref[0], l, l_before))
-      reference_rule(s_cur[0], scale_log2, half, m_ref[0], l_before, l, pb, acc_o[0]);
-    l_run[0] = l;
-    // O^T += V^T P^T
-    const u32x4* __restrict__ sVb = sV[cur];
-    bf16x8 vf[4][kD / 32];
-#pragma unroll
-    for (int cu = 0; cu < 2; ++cu)
-#pragma unroll
-      for (int t = 0; t < kD / 32; ++t) vf[cu][t] = vread(sVb, cu, t);
-#pragma unroll
-    for (int cu = 0; cu < 4; ++cu)
-#pragma unroll
-      for (int t = 0; t < kD / 32; ++t) {
-        acc_o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cu][t], pb[cu >> 1][cu & 1], acc_o[0][t], 0, 0, 0);
-        if (cu + 2 < 4) vf[cu + 2][t] = vread(sVb, cu + 2, t);
-      }
-    barrier_keep_newest_loads<PER_WAVE>();
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, s[a][c][e]);
+    return fmaxf(m, other_half(m, half)) * scale_log2;
   };
 
-  load_tile(0, 0);
-  load_tile(1, 1);
-  load_tile(2, 2);
-  __syncthreads();
-  f32x16 sa[NQ][2], sb[NQ][2];
-  scores(sK[0], sa);
-  // four tiles per iteration, one per LDS stage; the last nkt % 4 with the
-  // stage computed at run time
+  // Prologue: tiles 0 and 1 resident, raw scores of tile 0; the references
+  // are their row maxima.
+#pragma unroll
+  for (int j = 0; j < 8; ++j) load(0, 0, j);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) load(1, 1, j);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int st = 0; st < kD / 16; ++st)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16x8 k = kread(sK[0], c, st);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        if (st == 0) mfma_s_zero(s[a][c], k, qf[a][0]);
+        else mfma_s_acc(s[a][c], k, qf[a][st]);
+      }
+    }
+  fence_s(s[0][0], s[0][1]);
+  fence_s(s[1][0], s[1][1]);
+  if (nkt == 1 && partial) {
+    mask_half(0, 0);
+    mask_half(0, 1);
+  }
+  m_ref[0] = row_max(0);
+  m_ref[1] = row_max(1);
+  kf[0] = kread(sK[0], 1, 0);
+  kf[1] = kread(sK[0], 1, 1);
+
+  // The reference rule for tile kt, after its sum check fired (see above).
+  auto rule = [&](int kt, const u32x4* __restrict__ sKc, const u32x4* __restrict__ sKn, bool masked,
+                  const float (&lb)[2], float (&l)[2], bf16x8 (&pcur)[2][2][2]) {
+    // the last score MFMAs of the tile (into s[.][0]) land before these
+    // registers take anything else
+    fence_s(s[0][0], s[0][1]);
+    fence_s(s[1][0], s[1][1]);
+    fence_acc(acc_o);
+#pragma unroll
+    for (int st = 0; st < kD / 16; ++st)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 k = kread(sKc, c, st);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          if (st == 0) mfma_s_zero(s[a][c], k, qf[a][0]);
+          else mfma_s_acc(s[a][c], k, qf[a][st]);
+        }
+      }
+    fence_s(s[0][0], s[0][1]);
+    fence_s(s[1][0], s[1][1]);
+    if (masked) {
+      mask_half(kt, 0);
+      mask_half(kt, 1);
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const float mloc = row_max(a);
+      if (__builtin_amdgcn_ballot_w64(mloc > m_ref[a] + kSlackQ64) == 0) continue;
+      const float m_new = fmaxf(m_ref[a], mloc);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref[a] - m_new);
+      m_ref[a] = m_new;
+      float la = lb[a] * alpha, lo = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int c = q >> 3, e = 2 * (q & 7);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[a][c][e], scale_log2, -m_new));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[a][c][e + 1], scale_log2, -m_new));
+        pcur[a][c][e >> 3][e & 7] = static_cast<bf16>(p0);
+        pcur[a][c][e >> 3][(e & 7) + 1] = static_cast<bf16>(p1);
+        la += p0;
+        lo += p1;
+      }
+      l[a] = la + lo;
+      // one accumulator at a time, each back in its AGPRs before the next
+#pragma unroll
+      for (int t = 0; t < kD / 32; ++t) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc_o[a][t][e] *= alpha;
+        asm volatile("" : "+a"(acc_o[a][t]));
+      }
+    }
+    fence_acc(acc_o);
+    // raw scores of S(kt + 1) key half 0 again
+#pragma unroll
+    for (int st = 0; st < kD / 16; ++st) {
+      const bf16x8 k = kread(sKn, 0, st);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        if (st == 0) mfma_s_zero(s[a][0], k, qf[a][0]);
+        else mfma_s_acc(s[a][0], k, qf[a][st]);
+      }
+    }
+  };
+
+  // Tile kt.  On entry: s[.][0] holds the raw scores of S(kt) key half 0,
+  // kf[0..1] the first two K fragments of its key half 1 and
+  // vf[0..1] the first two V fragments of tile kt - 1.
+  // With inline_rule false the step leaves a fired rule to its caller
+  // (returning true, with the sums in lb_s / l_s), so the unrolled loop of
+  // full tiles carries none of the rule's code.
+  float lb_s[2], l_s[2];
+  auto step = [&](int kt, auto stage_c, bool has_prev, bool masked, bf16x8 (&pprev)[2][2][2],
+                  bf16x8 (&pcur)[2][2][2], auto inline_rule) -> bool {
+    constexpr int J = decltype(stage_c)::value;
+    constexpr bool INLINE_RULE = decltype(inline_rule)::value;
+    const int cur = J >= 0 ? J : kt % NSTAGE;
+    const u32x4* __restrict__ sKc = sK[cur];
+    const u32x4* __restrict__ sKn = sK[(cur + 1) % NSTAGE];
+    const u32x4* __restrict__ sVp = sV[(cur + 3) % NSTAGE];
+    // this wave's loads of tile kt + 1 landed, then every wave's; every wave
+    // is also done with tile kt - 2, whose stage the loads below refill
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    fence_s(s[0][0], s[1][0]);
+    if (masked) mask_half(kt, 0);
+    const float lb[2] = {l_run[0], l_run[1]};
+    float l[2] = {l_run[0], l_run[1]}, l2[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int p = 0; p < 32; ++p) {
+      // score MFMA
+      {
+        const int st = (p & 15) >> 1, a = p & 1, c = p < 16 ? 1 : 0;
+        const bf16x8 k = kf[(p >> 1) % 3];
+        if (st == 0) mfma_s_zero(s[a][c], k, qf[a][0]);
+        else mfma_s_acc(s[a][c], k, qf[a][st]);
+        if (a == 0) {
+          const int nf = (p >> 1) + 2;   // two fragments ahead
+          if (nf < 16) kf[nf % 3] = nf < 8 ? kread(sKc, 1, nf) : kread(sKn, 0, nf - 8);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (p == 16) {
+        fence_s(s[0][1], s[1][1]);
+        if (masked) mask_half(kt, 1);
+      }
+      const int wa = (p >> 3) & 1, q = (p & 7) + 8 * (p >> 4);
+      const int wc = q >> 3, we = 2 * (q & 7);
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[wa][wc][we], scale_log2, -m_ref[wa]));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[wa][wc][we + 1], scale_log2, -m_ref[wa]));
+      __builtin_amdgcn_sched_barrier(0);
+      // PV MFMA of tile kt - 1
+      if (has_prev) {
+        const int f = p >> 1, a = p & 1, cu = f >> 2, t = f & 3;
+        mfma_pv(acc_o[a][t], vf[f % 3], pprev[a][cu >> 1][cu & 1]);
+        if (a == 1 && f + 2 < 16) vf[(f + 2) % 3] = vread(sVp, (f + 2) >> 2, (f + 2) & 3);
+      }
+      if (p < 8) load(kt + 2, (cur + 2) % NSTAGE, p);
+      __builtin_amdgcn_sched_barrier(0);
+      pcur[wa][wc][we >> 3][we & 7] = static_cast<bf16>(e0);
+      pcur[wa][wc][we >> 3][(we & 7) + 1] = static_cast<bf16>(e1);
+      l[wa] += e0;
+      l2[wa] += e1;
+      // keeps the sums in their slots (sunk, they would queue up at the end)
+      asm volatile("" : "+v"(l[wa]), "+v"(l2[wa]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l[0] += l2[0];
+    l[1] += l2[1];
+    const bool fire =
+        __builtin_amdgcn_ballot_w64(l[0] > lb[0] + kGuardQ64 || l[1] > lb[1] + kGuardQ64) != 0;
+    if constexpr (INLINE_RULE) {
+      if (__builtin_expect(fire, 0)) rule(kt, sKc, sKn, masked, lb, l, pcur);
+    } else {
+      lb_s[0] = lb[0];
+      lb_s[1] = lb[1];
+      l_s[0] = l[0];
+      l_s[1] = l[1];
+    }
+    l_run[0] = l[0];
+    l_run[1] = l[1];
+    // the first operands of the next tile (both resident since this tile's barrier)
+    kf[0] = kread(sKn, 1, 0);
+    kf[1] = kread(sKn, 1, 1);
+    vf[0] = vread(sV[cur], 0, 0);
+    vf[1] = vread(sV[cur], 0, 1);
+    return !INLINE_RULE && fire;
+  };
+
   using Stage0 = std::integral_constant<int, 0>;
   using Stage1 = std::integral_constant<int, 1>;
   using Stage2 = std::integral_constant<int, 2>;
   using Stage3 = std::integral_constant<int, 3>;
   using StageR = std::integral_constant<int, -1>;
-  int kt = 0;
-  for (; kt + 3 < nkt; kt += 4) {
-    step(kt, Stage0{}, sa, sb);
-    step(kt + 1, Stage1{}, sb, sa);
-    step(kt + 2, Stage2{}, sa, sb);
-    step(kt + 3, Stage3{}, sb, sa);
+  using Inline = std::true_type;
+  // tile t's weights go to pA when t is even, pB when odd
+  step(0, Stage0{}, false, nkt == 1 && partial, pB, pA, Inline{});
+  int kt = 1;
+  for (; kt + 3 < nfull; kt += 4) {
+    step(kt, Stage1{}, true, false, pA, pB, Inline{});
+    step(kt + 1, Stage2{}, true, false, pB, pA, Inline{});
+    step(kt + 2, Stage3{}, true, false, pA, pB, Inline{});
+    step(kt + 3, Stage0{}, true, false, pB, pA, Inline{});
   }
   for (; kt + 1 < nkt; kt += 2) {
-    step(kt, StageR{}, sa, sb);
-    step(kt + 1, StageR{}, sb, sa);
+    step(kt, StageR{}, true, false, pA, pB, Inline{});
+    step(kt + 1, StageR{}, true, kt + 1 == nkt - 1 && partial, pB, pA, Inline{});
   }
-  if (kt < nkt) step(kt, StageR{}, sa, sb);
-
+  if (kt < nkt) step(kt, StageR{}, true, partial, pA, pB, Inline{});
+  // the last iteration's scores of a tile past the end land before their
+  // registers are reused
+  fence_s(s[0][0], s[1][0]);
+  // PV of the last tile
+  {
+    const bool odd = (nkt - 1) & 1;
+    bf16x8 pl[2][2][2];
 #pragma unroll
-  for (int a = 0; a < NQ; ++a)
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) pl[a][c][u] = odd ? pB[a][c][u] : pA[a][c][u];
+    fence_p(pl);
+    const u32x4* __restrict__ sVb = sV[(nkt - 1) % NSTAGE];
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int cu = f >> 2;
+        mfma_pv(acc_o[a][f & 3], vf[f % 3], pl[a][cu >> 1][cu & 1]);
+      }
+      if (f + 2 < 16) vf[(f + 2) % 3] = vread(sVb, (f + 2) >> 2, (f + 2) & 3);
+    }
+  }
+  fence_acc(acc_o);
+  // loads of tiles past the end may still be in flight
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
     store_rows<LSE>(io, head, z, q0 + 32 * a + l32, half, acc_o[a], m_ref[a], l_run[a]);
 }
 
@@ -642,12 +803,12 @@ attn_fwd_pipe(AttnIO io) {
 
 namespace {
 
-// Long query sets: the software-pipelined form in 256-query workgroups (one
-// per CU), when they cover at least three quarters of the 256 CUs;
-// otherwise 128-query workgroups, two per CU.
-// The pipelined kernel needs 256-query workgroups covering three quarters of
-// the CUs.
+// Workgroups of 256 queries: the 64-query-per-wave kernel runs when they
+// number at least kQ64MinWorkgroups and its 32-bit buffer offsets reach every
+// key row; otherwise 128-query workgroups of the 4-wave kernel, two per CU.
+// Key splits are chosen (attn_split_hint) to reach kPipeMinWorkgroups.
 constexpr long kPipeMinWorkgroups = 192;
+constexpr long kQ64MinWorkgroups = 32;
 
 long pipe_workgroups(int Tq, int heads, int splits) {
   return (long)((Tq + 255) / 256) * heads * splits;
@@ -655,9 +816,10 @@ long pipe_workgroups(int Tq, int heads, int splits) {
 
 template <bool LSE>
 void launch_io(const AttnIO& io, int heads, int splits, hipStream_t stream) {
-  if (pipe_workgroups(io.Tq, heads, splits) >= kPipeMinWorkgroups) {
-    const dim3 grid((io.Tq + 255) / 256, heads, splits), block(512);
-    hipLaunchKernelGGL((attn_fwd_pipe<1, 8, LSE>), grid, block, 0, stream, io);
+  const bool offsets32 = ((int64_t)io.Tkv + 4 * kBKV) * io.ldkv * 2 < ((int64_t)1 << 31);
+  if (pipe_workgroups(io.Tq, heads, splits) >= kQ64MinWorkgroups && offsets32) {
+    const dim3 grid((io.Tq + 255) / 256, heads, splits), block(256);
+    hipLaunchKernelGGL((attn_fwd_q64<LSE>), grid, block, 0, stream, io);
   } else {
     const dim3 grid((io.Tq + 127) / 128, heads, splits), block(256);
     hipLaunchKernelGGL((attn_fwd_bf16_d128<4, LSE>), grid, block, 0, stream, io);

@@ -167,3 +167,126 @@ def test_no_mfma_result_read_too_early_at_a_block_start(tmp_path):
     found = [(os.path.basename(s), h) for s, t in zip(srcs, texts) for h in scan(t)]
     assert sum(t.count("v_mfma") for t in texts) > 0, "no MFMA found: the scan read nothing"
     assert not found, "\n".join(f"{s}: {h}" for s, h in found)
+
+
+# ---------------------------------------------------------------------------
+# MFMAs issued from inline asm (the 64-query attention pins its accumulators
+# to AGPRs that way) are not MFMAs to the compiler's hazard recognizer, so
+# within a block it pads nothing around them.  The kernel's own fences supply
+# the wait states; this scan checks every such MFMA in straight-line code:
+# no instruction touches its result registers sooner than NEED_WAIT_STATES
+# after it (a chained srcC of the next MFMA is forwarded by the hardware),
+# and no vector instruction writes one of its source registers fewer than 2
+# wait states before it.
+VALU_WRITE_TO_MFMA = 2
+
+
+def _asm_blocks(text):
+    """Per function, the instruction list with a flag for inline-asm lines."""
+    funcs, cur, in_asm = [], None, False
+    for line in text.splitlines():
+        if ";;#ASMSTART" in line:
+            in_asm = True
+            continue
+        if ";;#ASMEND" in line:
+            in_asm = False
+            continue
+        s = line.split(";")[0].rstrip()
+        if re.match(r"^_Z\w+:$", s):
+            cur = []
+            funcs.append((s[:-1], cur))
+            continue
+        if cur is None:
+            continue
+        if s.startswith(".Lfunc_end"):
+            cur = None
+            continue
+        if re.match(r"^\.LBB\w+:", s):
+            cur.append(("LABEL", "", [], False))
+            continue
+        s = s.strip()
+        if not s or s.startswith("."):
+            continue
+        for part in s.split("\n"):
+            op = part.split()[0]
+            rest = part[len(op):].strip()
+            cur.append((op, rest, [o.strip() for o in rest.split(",")] if rest else [], in_asm))
+    return funcs
+
+
+def scan_inline_mfma(text):
+    found = []
+    for name, ins in _asm_blocks(text):
+        for i, (op, rest, ops, asm) in enumerate(ins):
+            if not (asm and op.startswith("v_mfma")):
+                continue
+            need = NEED_WAIT_STATES.get(op, LOOKBACK)
+            dst = _regs(ops[0])
+            srcs = set().union(*[_regs(o) for o in ops[1:4]])
+            # later instructions touching the result
+            ws = 0
+            for j in range(i + 1, len(ins)):
+                op2, rest2, ops2, _ = ins[j]
+                if op2 == "LABEL" or op2.startswith(("s_branch", "s_cbranch", "s_endpgm")) or ws >= need:
+                    break
+                if op2 == "s_nop":
+                    ws += int(rest2.split()[0]) + 1
+                    continue
+                touched = set().union(*[_regs(o) for o in (ops2[1:3] if op2.startswith("v_mfma") else ops2)])
+                if op2.startswith("v_mfma") and _regs(ops2[0]) == dst and dst <= set().union(*[_regs(o) for o in ops2[3:4]]):
+                    touched = set()   # the next MFMA chaining the accumulator
+                if dst & touched:
+                    found.append((name, f"{op} {rest}", f"{op2} {rest2}", ws))
+                    break
+                ws += 1
+            # earlier vector writes of its sources
+            ws = 0
+            for j in range(i - 1, -1, -1):
+                op2, rest2, ops2, _ = ins[j]
+                if op2 == "LABEL" or ws >= VALU_WRITE_TO_MFMA:
+                    break
+                if op2 == "s_nop":
+                    ws += int(rest2.split()[0]) + 1
+                    continue
+                if op2.startswith("v_") and not op2.startswith("v_mfma") and ops2 and _regs(ops2[0]) & srcs:
+                    found.append((name, f"{op} {rest}", f"{op2} {rest2}", ws))
+                    break
+                ws += 1
+    return found
+
+
+INLINE_SNIPPET = """_Zk:
+\t;;#ASMSTART
+\tv_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]
+\t;;#ASMEND
+{pad}\tv_accvgpr_read_b32 v10, a3
+\tv_mov_b32_e32 v4, v10
+\t;;#ASMSTART
+\tv_mfma_f32_32x32x16_bf16 a[16:31], v[0:3], v[4:7], a[16:31]
+\t;;#ASMEND
+\ts_endpgm
+.Lfunc_end0:
+"""
+
+
+def test_inline_scanner_flags_unpadded_neighbours():
+    hits = scan_inline_mfma(INLINE_SNIPPET.format(pad=""))
+    # the accumulator read right after the first MFMA, the operand write right
+    # before the second
+    assert [h[2].split()[0] for h in hits] == ["v_accvgpr_read_b32", "v_mov_b32_e32"]
+
+
+def test_inline_scanner_accepts_padding():
+    hits = scan_inline_mfma(INLINE_SNIPPET.format(pad="\ts_nop 7\n\ts_nop 2\n"))
+    assert [h[2].split()[0] for h in hits] == ["v_mov_b32_e32"]   # 11 wait states clear the read
+
+
+def test_inline_asm_mfmas_are_padded(tmp_path):
+    srcs = B.sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        texts = list(ex.map(lambda s: _device_isa(s, str(tmp_path / (os.path.basename(s) + ".s"))), srcs))
+    n_inline = sum(len([1 for _, ins in _asm_blocks(t) for x in ins if x[3] and x[0].startswith("v_mfma")])
+                   for t in texts)
+    assert n_inline > 0, "no inline-asm MFMA found: the scan read nothing"
+    found = [(os.path.basename(s), h) for s, t in zip(srcs, texts) for h in scan_inline_mfma(t)]
+    assert not found, "\n".join(f"{s}: {h}" for s, h in found)
