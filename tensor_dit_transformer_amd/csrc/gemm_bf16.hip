@@ -31,12 +31,15 @@
 //     multiple of 64 zero-fills the chunks past K (K must be a multiple of 8).
 #include "tp_kernels.h"
 
+#include <type_traits>
+
 namespace tpk {
 namespace {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
@@ -336,9 +339,10 @@ __device__ __forceinline__ void wait_vmem() {
 // all but the newest N loads of this wave have landed
 template <int N>
 __device__ __forceinline__ void wait_vmem_keep() {
-  static_assert(N == 4 || N == 3, "instantiated counts");
+  static_assert(N == 5 || N == 4 || N == 3, "instantiated counts");
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -545,6 +549,300 @@ gemm_bf16_nt_pingpong(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) 
   store_tiles<KIND, TM, TN, true>(acc, p, ep, m0 + 32 * TM * g, n0 + 64 * q, lane);
 }
 
+// Epilogue of the 16x16 MFMA layout: accumulator (i, j) holds C rows
+// row0 + 16 i + [0, 16) and columns col0 + 16 j + [0, 16); lane l holds
+// column l & 15 of rows 4 (l >> 4) + e, e = 0..3.  A store instruction writes
+// 16 adjacent columns of four rows.  act_from and split are multiples of 16,
+// so a 16-column block lies wholly on one side of each (GELU or none; SwiGLU
+// shapes stay on the 32x32 kernels).
+template <OutKind KIND, bool GELU, bool ROWCHECK, int TM, int TN>
+__device__ __forceinline__ void store_block16(const f32x4 (&acc)[TM][TN], int j, char* p,
+                                              int64_t stride, int rows_left, float bias) {
+  const int64_t stride13 = 13 * stride;
+  if constexpr (KIND == OutKind::F32_ACC) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      float old[4];
+      char* q = p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        old[e] = (!ROWCHECK || 16 * i + e < rows_left) ? *reinterpret_cast<const float*>(q) : 0.0f;
+        q += stride;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!ROWCHECK || 16 * i + e < rows_left) *reinterpret_cast<float*>(p) = old[e] + acc[i][j][e];
+        p += e == 3 ? stride13 : stride;
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (ROWCHECK) asm volatile("" : "+v"(rows_left));
+      if (!ROWCHECK || 16 * i + e < rows_left) {
+        float v = acc[i][j][e] + bias;
+        if constexpr (GELU) v = gelu_tanh(v);
+        if constexpr (KIND == OutKind::BF16)
+          *reinterpret_cast<bf16*>(p) = static_cast<bf16>(v);
+        else
+          *reinterpret_cast<float*>(p) = v;
+      }
+      p += e == 3 ? stride13 : stride;
+    }
+  }
+}
+
+template <OutKind KIND, int TM, int TN>
+__device__ __forceinline__ void store_tiles16(const f32x4 (&acc)[TM][TN], const GemmProblem& p,
+                                              const GemmEpilogue& ep, int row0, int col0, int lane) {
+  constexpr int ES = KIND == OutKind::BF16 ? 2 : 4;
+  const int col_l = lane & 15;
+  const int row_l = 4 * (lane >> 4);
+  const int rows_left = p.M - row0 - row_l;
+  const bool rows_full = row0 + 16 * TM <= p.M;       // wave-uniform
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = col0 + 16 * j + col_l;
+    if (col >= p.N) continue;
+    const bool gelu = KIND != OutKind::F32_ACC && col >= ep.act_from && ep.act == Act::GELU_TANH;
+    const float bias = (KIND != OutKind::F32_ACC && ep.bias) ? ep.bias[col] : 0.0f;
+    const bool second = col >= ep.split;
+    const int ocol = second ? col - ep.split : col;
+    const int64_t ld = second ? ep.ld1 : ep.ld0;
+    char* base = static_cast<char*>(second ? ep.out1 : ep.out0) + ((int64_t)(row0 + row_l) * ld + ocol) * ES;
+    const int64_t stride = ld * ES;
+    if (rows_full) {
+      if (gelu) store_block16<KIND, true, false>(acc, j, base, stride, rows_left, bias);
+      else store_block16<KIND, false, false>(acc, j, base, stride, rows_left, bias);
+    } else {
+      if (gelu) store_block16<KIND, true, true>(acc, j, base, stride, rows_left, bias);
+      else store_block16<KIND, false, true>(acc, j, base, stride, rows_left, bias);
+    }
+  }
+}
+
+// 288x192 tiles, for problems whose 256x256 tiling leaves CUs idle in its
+// last round while this one fills them: at M = 4608 it gives exactly 256
+// tiles per round for N = 3072, 6144 and 9216 (216, 432 and 648 tiles of
+// 256x256 use 84 % of the CUs).  The ping-pong schedule of the 256x256 kernel
+// above, with v_mfma_f32_16x16x32_bf16: group g owns C rows [144 g, 144 g +
+// 144), wave q of a group columns [48 q, 48 q + 48), 9 x 3 accumulators of
+// 16x16; a 64-deep K tile is two 32-deep k-steps.  Operand lane l holds row
+// (l & 15) of its 16-row fragment and 8 K elements from 8 (l >> 4) of the
+// k-step: chunk 4 s + (l >> 4) of the 128-byte LDS row.  A has three LDS
+// stages and B two (108 + 48 KB).  Loads: B 24 per tile (3 per wave), A 36
+// (5 per wave in group 0, 4 in group 1).
+template <OutKind KIND>
+__global__ void __launch_bounds__(512)
+gemm_bf16_nt_pp288(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
+  constexpr int BM = 288, BN = 192;
+  constexpr int TM = 9, TN = 3, KS = 2;
+  constexpr int A_STAGE = BM * kRowChunks;
+  constexpr int B_STAGE = BN * kRowChunks;
+  constexpr int BW = 3;
+  __shared__ u32x4 smem[3 * A_STAGE + 2 * B_STAGE];   // 156 KB
+
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, per = nb >> 3, rem = nb & 7;
+  const int id = xcd * per + min(xcd, rem) + (bid >> 3);
+  const int group = id / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = id - group * kGroupM * tiles_n;
+  const int m0 = (first_m + in_group % gm) * BM;
+  const int n0 = (in_group / gm) * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wave >> 2, q = wave & 3;
+
+  const uint32_t lda2 = (uint32_t)p.lda * 2, ldb2 = (uint32_t)p.ldb * 2;
+  const rsrc_t ra = buffer_rsrc(p.A, (uint32_t)(p.M - 1) * lda2 + (uint32_t)p.K * 2);
+  const rsrc_t rb = buffer_rsrc(p.B, (uint32_t)(p.N - 1) * ldb2 + (uint32_t)p.K * 2);
+  // A rows of this wave's loads: group 0 waves 40 each from 40 q, group 1
+  // waves 32 each from 160 + 32 q; B rows 24 from 24 wave.  8 rows per load;
+  // lane l reads row R + (l >> 3) into physical chunk l & 7 (swizzled).
+  const int lr = lane >> 3, lc = lane & 7;
+  const int arow0 = g == 0 ? 40 * q : 160 + 32 * q;
+  const int brow0 = 24 * wave;
+  uint32_t voa[5], vob[BW];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int R = arow0 + 8 * j;
+    voa[j] = (uint32_t)(m0 + R + lr) * lda2 + (uint32_t)((lc ^ lr ^ ((R >> 3) & 1)) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < BW; ++j) {
+    const int R = brow0 + 8 * j;
+    vob[j] = (uint32_t)(n0 + R + lr) * ldb2 + (uint32_t)((lc ^ lr ^ ((R >> 3) & 1)) * 16);
+  }
+  auto stage_a = [&](int kt) { return smem + (kt % 3) * A_STAGE; };
+  auto stage_b = [&](int kt) { return smem + 3 * A_STAGE + (kt & 1) * B_STAGE; };
+  auto load_a = [&](int kt, int j) {
+    lds_dma(ra, stage_a(kt) + (arow0 + 8 * j) * kRowChunks, voa[j], (uint32_t)kt * (kBK * 2));
+  };
+  auto load_b = [&](int kt, int j) {
+    lds_dma(rb, stage_b(kt) + (brow0 + 8 * j) * kRowChunks, vob[j], (uint32_t)kt * (kBK * 2));
+  };
+  auto b_loads = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < BW; ++j) load_b(kt, j);
+  };
+  // group 0 issues 5 A loads per tile, group 1 four (AW is a template
+  // constant on each group's code path)
+  auto a_loads = [&](int kt, auto aw) {
+    constexpr int AW = decltype(aw)::value;
+#pragma unroll
+    for (int j = 0; j < AW; ++j) load_a(kt, j);
+  };
+
+  const int a_row = 144 * g + (lane & 15);
+  const int b_row = 48 * q + (lane & 15);
+  const int kq = lane >> 4;
+  bf16x8 fa[KS][TM], fb[KS][TN];
+  auto read_tile = [&](int kt) {
+    const u32x4* sa = stage_a(kt);
+    const u32x4* sb = stage_b(kt);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int kc = 4 * s + kq;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[s][i] = __builtin_bit_cast(bf16x8, sa[(a_row + 16 * i) * kRowChunks + swizzle(a_row, kc)]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fb[s][j] = __builtin_bit_cast(bf16x8, sb[(b_row + 16 * j) * kRowChunks + swizzle(b_row, kc)]);
+    }
+  };
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
+  // The tile's 54 MFMAs, with load(l), l < nl, issued after MFMA 2 l.
+  auto multiply = [&](auto&& load, int nl) {
+    int idx = 0;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+          if ((idx & 1) == 0 && (idx >> 1) < nl) {
+            __builtin_amdgcn_sched_barrier(0);
+            load(idx >> 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          ++idx;
+        }
+  };
+  auto none = [](int) {};
+  using AW0 = std::integral_constant<int, 5>;
+  using AW1 = std::integral_constant<int, 4>;
+
+  const int nk = p.K / kBK;
+  b_loads(0);
+  if (g == 0) {
+    a_loads(0, AW0{});
+    if (nk > 1) a_loads(1, AW0{});
+  } else {
+    a_loads(0, AW1{});
+    if (nk > 1) a_loads(1, AW1{});
+  }
+  wait_vmem();
+  wg_barrier();
+  if (g == 0) {
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) {
+      read_tile(kt);
+      __builtin_amdgcn_sched_barrier(0);
+      b_loads(kt + 1);
+      wg_barrier();                       // end of phase 2 kt
+      multiply([&](int j) { load_a(kt + 2, j); }, 5);
+      wait_vmem_keep<5>();                // B tile kt + 1 landed
+      wg_barrier();                       // end of phase 2 kt + 1
+    }
+    if (kt + 1 < nk) {                    // kt = nk - 2
+      read_tile(kt);
+      __builtin_amdgcn_sched_barrier(0);
+      b_loads(kt + 1);
+      wg_barrier();
+      multiply(none, 0);
+      wait_vmem();
+      wg_barrier();
+      ++kt;
+    }
+    read_tile(kt);                        // kt = nk - 1
+    wg_barrier();
+    multiply(none, 0);
+    wg_barrier();
+    wg_barrier();
+  } else {
+    if (nk > 1) b_loads(1);
+    wg_barrier();                         // end of phase 0
+    read_tile(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nk > 2) {
+      a_loads(2, AW1{});
+      wait_vmem_keep<4>();
+    } else {
+      wait_vmem();
+    }
+    wg_barrier();                         // end of phase 1
+    int kt = 1;
+    for (; kt + 2 < nk; ++kt) {
+      multiply([&](int j) { load_b(kt + 1, j); }, BW);   // tile kt - 1
+      wg_barrier();                       // end of phase 2 kt
+      read_tile(kt);
+      __builtin_amdgcn_sched_barrier(0);
+      a_loads(kt + 2, AW1{});
+      wait_vmem_keep<4>();
+      wg_barrier();                       // end of phase 2 kt + 1
+    }
+    if (kt + 1 < nk) {                    // kt = nk - 2 >= 1
+      multiply([&](int j) { load_b(kt + 1, j); }, BW);
+      wg_barrier();
+      read_tile(kt);
+      wait_vmem();
+      wg_barrier();
+      ++kt;
+    }
+    if (kt < nk) {                        // kt = nk - 1 >= 1
+      multiply(none, 0);
+      wg_barrier();
+      read_tile(kt);
+      wg_barrier();
+    }
+    multiply(none, 0);                    // tile nk - 1
+    wg_barrier();
+  }
+
+  store_tiles16<KIND, TM, TN>(acc, p, ep, m0 + 144 * g, n0 + 48 * q, lane);
+}
+
+hipError_t launch_288(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind, hipStream_t stream) {
+  const int tm = (p.M + 287) / 288, tn = (p.N + 191) / 192;
+  const dim3 grid(tm * tn), block(512);
+  switch (kind) {
+    case OutKind::BF16:
+      hipLaunchKernelGGL((gemm_bf16_nt_pp288<OutKind::BF16>), grid, block, 0, stream, p, ep, tm, tn);
+      break;
+    case OutKind::F32_STORE:
+      hipLaunchKernelGGL((gemm_bf16_nt_pp288<OutKind::F32_STORE>), grid, block, 0, stream, p, ep, tm, tn);
+      break;
+    case OutKind::F32_ACC:
+      hipLaunchKernelGGL((gemm_bf16_nt_pp288<OutKind::F32_ACC>), grid, block, 0, stream, p, ep, tm, tn);
+      break;
+  }
+  return hipGetLastError();
+}
+
 // The 8-wave kernel with TM * 64-row tiles (TM 4: 256 x 256, TM 3: 192 x 256).
 template <int TM>
 hipError_t launch_8w(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
@@ -600,11 +898,22 @@ hipError_t launch_gemm_bf16(const GemmProblem& p, const GemmEpilogue& ep, OutKin
   // the rows of a last partial tile (up to 256 past M or N)
   const bool fits32 = (int64_t)(p.M + 256) * p.lda < ((int64_t)1 << 31) &&
                       (int64_t)(p.N + 256) * p.ldb < ((int64_t)1 << 31);
+  // 288x192 tiles when they fill the rounds of CUs at least 8 % better than
+  // 256x256 ones (e.g. every M = 4608 shape with N a multiple of 3072), for
+  // the epilogues the 16x16 layout serves (not SwiGLU)
+  const long t288 = (long)((p.M + 287) / 288) * ((p.N + 191) / 192);
+  const bool fits288 = (int64_t)(p.M + 288) * p.lda < ((int64_t)1 << 31) &&
+                       (int64_t)(p.N + 192) * p.ldb < ((int64_t)1 << 31);
+  auto fill = [](long t) { return (double)t / (double)(((t + 255) / 256) * 256); };
+  const long mid = (long)((p.M + 191) / 192) * ((p.N + 255) / 256);   // 192x256 tiles
+  const double fill_32x32 = big < 256 && mid <= 256 ? fill(mid) : fill(big);
+  if (t288 >= 128 && p.K % kBK == 0 && fits288 && ep.act != Act::SWIGLU &&
+      ep.act_from % 16 == 0 && ep.split % 16 == 0 && fill(t288) > 1.08 * fill_32x32)
+    return launch_288(p, ep, kind, stream);
   if (big >= 128 && p.K % kBK == 0 && fits32) {
     // One partial round of 256-row tiles leaves CUs idle (e.g. 162 tiles at
     // M = 4608, N = 2304); if 192-row tiles still fit in one round, every
     // busy CU has 3/4 of the work.
-    const long mid = (long)((p.M + 191) / 192) * ((p.N + 255) / 256);
     if (big < 256 && mid <= 256) return launch_8w<3>(p, ep, kind, stream);
     return launch_8w<4>(p, ep, kind, stream);
   }

@@ -230,6 +230,45 @@ def test_192_row_tiles_with_gelu_epilogue():
     close_all(shards)
 
 
+def test_288_row_tiles_gelu_store_and_accumulate_with_ragged_edges():
+    # MLP shard M = 4408 = 15 x 288 + 88, up N = 12032 / 4 = 3008 = 15 x 192
+    # + 128, down N = 3072, K = 3072 / 3008: 16 x 16 = 256 tiles of 288 x 192
+    # against 216 of 256 x 256, so both GEMMs take the 16x16-MFMA 288-row
+    # kernel.  In the last tile row wave group 0 stores 88 of its 144 rows
+    # and group 1 none; in the up-projection's last tile column waves 0-1
+    # store all 48 columns, wave 2 32 and wave 3 none.  GELU bf16 store, fp32
+    # store, and the fp32 accumulate form twice onto zeros.
+    w = Workload("mlp288_T4408_D3072_F12032_P4", 4408, 3072, 0, 0, 12032, 4, "bf16")
+    inp = tp_inputs.make_inputs(w, seed=28)
+    ranks, y_ref = full_oracle(w, inp)
+    shards, outs, y = run_all_ranks(w, inp)
+    for r, (buf, ref) in enumerate(zip(outs, ranks)):
+        check_rank(w, buf, ref, H.TOL["bf16"], f"{w.name} rank {r}")
+    assert H.rel_err(H.as_f64(y), y_ref) <= H.TOL["bf16"]
+    p2 = torch.zeros_like(outs[1].partial)
+    for _ in range(2):
+        tp.tp_rowwise_linear_partial(shards[1], tp.TP_MLP_DOWN, w.tokens, outs[1].h, p2, accumulate=True)
+    torch.cuda.synchronize()
+    assert H.rel_err(H.as_f64(p2), 2 * ranks[1]["p_block"]) <= H.TOL["bf16"]
+    close_all(shards)
+
+
+def test_288_row_tiles_fused_colwise_split_and_block_out():
+    # Block shard at M = 4408: the fused colwise launch (N = 2304 + 3008 =
+    # 5312, 448 tiles of 288 x 192 against 378 of 256 x 256 in two rounds)
+    # splits its output at column 2304 (qkv | h, GELU from there on), and the
+    # packed rowwise out (N = 3072, K = 768 + 3008 = 3776) takes the same
+    # kernel with the fp32 store.
+    w = Workload("block288_T4408_D3072_H24_F12032_P4", 4408, 3072, 24, 128, 12032, 4, "bf16")
+    inp = tp_inputs.make_inputs(w, seed=29)
+    ranks, y_ref = full_oracle(w, inp)
+    shards, outs, y = run_all_ranks(w, inp)
+    for r, (buf, ref) in enumerate(zip(outs, ranks)):
+        check_rank(w, buf, ref, H.TOL["bf16"], f"{w.name} rank {r}")
+    assert H.rel_err(H.as_f64(y), y_ref) <= H.TOL["bf16"]
+    close_all(shards)
+
+
 def test_large_rowwise_store_and_accumulate_paths():
     # MLP-only, P = 1, hidden 8192: the down projection is N = 8192 -> 9 x 32 tiles
     w = Workload("big_down_T2125_D8192_F1024_P1", 2125, 8192, 0, 0, 1024, 1, "bf16")
