@@ -1,6 +1,7 @@
-// bf16 GEMM with fp32 accumulate on gfx950 matrix cores:
+// GEMMs with fp32 accumulate on gfx950 matrix cores:
 //   C[M, N] = A[M, K] * B[N, K]^T  (+ bias, GELU-tanh or SwiGLU, bf16 store | fp32 store |
-//   fp32 accumulate)
+//   fp32 accumulate), A and B both bf16 (v_mfma_f32_32x32x16_bf16 and
+//   v_mfma_f32_16x16x32_bf16) or both fp32 (v_mfma_f32_32x32x2_f32).
 //
 // This is the colwise projection (output features = weight dim 0) and the
 // rowwise partial projection (input features = weight dim 1) of the Diffusers
@@ -8,17 +9,18 @@
 // weight slice is an nn.Linear [out, in] matrix, so both operands are
 // K-contiguous and the kernel is one "NT" GEMM with different epilogues.
 //
-// Design (gfx950, 64-wide waves, 160 KB LDS per CU).  Two kernels: a
-// 4-wave register-staged one for small and ragged shapes, and the 8-wave
-// ping-pong kernel further down for large ones (at least 128 tiles of
-// 256x256, K % 64 == 0).  The 4-wave kernel:
+// Design (gfx950, 64-wide waves, 160 KB LDS per CU).  A 4-wave
+// register-staged kernel for small and ragged bf16 shapes and for every fp32
+// one, and the 8-wave ping-pong kernels further down for large bf16 ones (at
+// least 128 tiles of 256x256 or 288x192, K % 64 == 0).  The 4-wave kernel:
 //   * 256 threads = 4 waves in a WM x WN grid; each wave owns a
 //     (BM/WM) x (BN/WN) block of C held in accumulation registers as
-//     32x32 tiles of v_mfma_f32_32x32x16_bf16.
-//   * K advances 64 elements (128 bytes per row) per tile.  A and B tiles are
-//     fetched with 16-byte global loads into registers one tile ahead, then
-//     written to a double-buffered LDS tile; one barrier per K tile.
-// Both kernels:
+//     32x32 MFMA tiles.
+//   * K advances 128 bytes per row per tile (64 bf16 or 32 fp32 elements).
+//     A and B tiles are fetched with 16-byte global loads into registers one
+//     tile ahead, then written to a double-buffered LDS tile; one barrier per
+//     K tile.
+// All kernels:
 //   * LDS rows are 128 bytes; the 16-byte chunk of k-group kc of row r lives
 //     at chunk kc ^ (r & 7) ^ ((r >> 3) & 1), so the rows read by one
 //     ds_read_b128 phase fall in distinct banks.
@@ -26,9 +28,10 @@
 //     contiguous stretch of a grouped tile order (8 tile rows per group), and
 //     the A/B panels it streams are shared by its neighbours in L2.
 //   * Rows past M / N are masked on store; on load the 4-wave kernel clamps
-//     them to the last row and the 8-wave kernel reads them as zero (past
-//     its buffer descriptors' range).  In the 4-wave kernel a K that is not a
-//     multiple of 64 zero-fills the chunks past K (K must be a multiple of 8).
+//     them to the last row and the 8-wave kernels read them as zero (past
+//     their buffer descriptors' range).  In the 4-wave kernel a K that is not
+//     a whole number of tiles zero-fills the chunks past K (K must be a
+//     multiple of the 8 bf16 or 4 fp32 elements of a chunk).
 #include "tp_kernels.h"
 
 #include <type_traits>
@@ -43,7 +46,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kBK = 64;        // K elements per tile
+constexpr int kBK = 64;        // bf16 K elements per tile (128 bytes per row)
 constexpr int kRowChunks = 8;  // 16-byte chunks per LDS tile row
 constexpr int kGroupM = 8;     // tile rows per group in the tile order
 
@@ -183,9 +186,18 @@ __device__ __forceinline__ void store_tiles(const f32x16 (&acc)[TM][TN], const G
   }
 }
 
-template <int BM, int BN, int WM, int WN, OutKind KIND, bool KTAIL>
+// T = bf16: each 16-byte chunk holds 8 k; an MFMA step (32x32x16) takes
+// chunk 2 s + (lane >> 5) of the lane's row, k-step s = 0..3 of the tile.
+// T = float: a chunk holds 4 k; an MFMA step (32x32x2) takes one k per lane
+// half, and the lane half h reads chunks 2 c + h (c = 0..3), so step 4 c + j
+// reduces k = 8 c + j (half 0) and 8 c + 4 + j (half 1): the same k for A
+// and B, each k of the tile once.
+template <class T, int BM, int BN, int WM, int WN, OutKind KIND, bool KTAIL>
 __global__ void __launch_bounds__(kThreads)
-gemm_bf16_nt(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
+gemm_nt_staged(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
+  static_assert(std::is_same<T, bf16>::value || std::is_same<T, float>::value, "bf16 or fp32");
+  constexpr int CE = 16 / sizeof(T);           // elements per 16-byte chunk
+  constexpr int BKT = kRowChunks * CE;          // K elements per tile
   static_assert(WM * WN * 64 == kThreads, "4 waves");
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
@@ -208,25 +220,25 @@ gemm_bf16_nt(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
   const int n0 = (in_group / gm) * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bf16* __restrict__ A = static_cast<const bf16*>(p.A);
-  const bf16* __restrict__ B = static_cast<const bf16*>(p.B);
+  const T* __restrict__ A = static_cast<const T*>(p.A);
+  const T* __restrict__ B = static_cast<const T*>(p.B);
 
   // ---- global -> register staging: thread loads chunk kc of rows r0 + 32 i
   const int ld_row = tid >> 3, ld_kc = tid & 7;
   int64_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i)
-    a_off[i] = (int64_t)min(m0 + ld_row + 32 * i, p.M - 1) * p.lda + ld_kc * 8;
+    a_off[i] = (int64_t)min(m0 + ld_row + 32 * i, p.M - 1) * p.lda + ld_kc * CE;
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i)
-    b_off[i] = (int64_t)min(n0 + ld_row + 32 * i, p.N - 1) * p.ldb + ld_kc * 8;
+    b_off[i] = (int64_t)min(n0 + ld_row + 32 * i, p.N - 1) * p.ldb + ld_kc * CE;
   // the swizzle of rows ld_row + 32 i does not depend on i
   const int st_base = ld_row * kRowChunks + swizzle(ld_row, ld_kc);
 
   u32x4 ra[A_LOADS], rb[B_LOADS];
   auto gload = [&](int kt) {
-    const int k = kt * kBK;
-    const bool in = !KTAIL || (k + ld_kc * 8 < p.K);
+    const int k = kt * BKT;
+    const bool in = !KTAIL || (k + ld_kc * CE < p.K);
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i)
@@ -262,24 +274,31 @@ gemm_bf16_nt(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
     const u32x4* sa = smem + buf * BUF;
     const u32x4* sb = sa + BM * kRowChunks;
 #pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
+    for (int s = 0; s < kRowChunks / 2; ++s) {
       const int kc = 2 * s + khalf;
-      bf16x8 a[TM], b[TN];
+      u32x4 a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = sa[(a_row + 32 * i) * kRowChunks + swizzle(a_row, kc)];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[j] = sb[(b_row + 32 * j) * kRowChunks + swizzle(b_row, kc)];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        a[i] = __builtin_bit_cast(bf16x8, sa[(a_row + 32 * i) * kRowChunks + swizzle(a_row, kc)]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        b[j] = __builtin_bit_cast(bf16x8, sb[(b_row + 32 * j) * kRowChunks + swizzle(b_row, kc)]);
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (std::is_same<T, bf16>::value) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
+          } else {
+            const f32x4 af = __builtin_bit_cast(f32x4, a[i]), bfv = __builtin_bit_cast(f32x4, b[j]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            for (int q = 0; q < 4; ++q)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[q], bfv[q], acc[i][j], 0, 0, 0);
+          }
+        }
     }
   };
 
-  const int nk = (p.K + kBK - 1) / kBK;
+  const int nk = (p.K + BKT - 1) / BKT;
   gload(0);
   sstore(0);
   __syncthreads();
@@ -863,17 +882,18 @@ hipError_t launch_8w(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN>
+template <class T, int BM, int BN, int WM, int WN>
 hipError_t launch_tile(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
                        hipStream_t stream) {
   const int tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
   const dim3 grid(tm * tn), block(kThreads);
-  const bool ktail = (p.K % kBK) != 0;
+  const bool ktail = (p.K % (kRowChunks * (16 / (int)sizeof(T)))) != 0;
 #define TPK_LAUNCH(K_, T_) \
-  hipLaunchKernelGGL((gemm_bf16_nt<BM, BN, WM, WN, K_, T_>), grid, block, 0, stream, p, ep, tm, tn)
+  hipLaunchKernelGGL((gemm_nt_staged<T, BM, BN, WM, WN, K_, T_>), grid, block, 0, stream, p, ep, tm, tn)
   switch (kind) {
     case OutKind::BF16:
-      if (ktail) TPK_LAUNCH(OutKind::BF16, true); else TPK_LAUNCH(OutKind::BF16, false);
+      if constexpr (std::is_same<T, float>::value) return hipErrorInvalidValue;  // fp32 in, fp32 out
+      else if (ktail) TPK_LAUNCH(OutKind::BF16, true); else TPK_LAUNCH(OutKind::BF16, false);
       break;
     case OutKind::F32_STORE:
       if (ktail) TPK_LAUNCH(OutKind::F32_STORE, true); else TPK_LAUNCH(OutKind::F32_STORE, false);
@@ -917,8 +937,16 @@ hipError_t launch_gemm_bf16(const GemmProblem& p, const GemmEpilogue& ep, OutKin
     if (big < 256 && mid <= 256) return launch_8w<3>(p, ep, kind, stream);
     return launch_8w<4>(p, ep, kind, stream);
   }
-  if (big >= 256) return launch_tile<256, 256, 2, 2>(p, ep, kind, stream);
-  return launch_tile<128, 128, 2, 2>(p, ep, kind, stream);
+  if (big >= 256) return launch_tile<bf16, 256, 256, 2, 2>(p, ep, kind, stream);
+  return launch_tile<bf16, 128, 128, 2, 2>(p, ep, kind, stream);
+}
+
+// fp32 operands (the fp32 shards, parity workloads): the register-staged
+// kernel with 128x128 tiles, fp32 out (store or accumulate).
+hipError_t launch_gemm_f32(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind,
+                           hipStream_t stream) {
+  if (kind == OutKind::BF16) return hipErrorInvalidValue;
+  return launch_tile<float, 128, 128, 2, 2>(p, ep, kind, stream);
 }
 
 }  // namespace tpk

@@ -21,12 +21,14 @@ from tensor_dit_transformer_amd import build as B
 
 # Wait states an MFMA result needs before a vector-ALU, LDS or memory
 # instruction may read it: passes + 3 for these (gfx950 bf16: 16x16x32 is
-# 4 passes, 32x32x16 is 8 -- 16 and 32 cycles at the dense bf16 rate); the
-# compiler's own padding for the 16x16x32 accumulator read is 7.  An MFMA
-# missing here fails the scan so that it gets an entry.
+# 4 passes, 32x32x16 is 8 -- 16 and 32 cycles at the dense bf16 rate; fp32
+# 32x32x2 is 16 passes, 64 cycles at the fp32 matrix rate); the compiler's
+# own padding for the 16x16x32 accumulator read is 7.  An MFMA missing here
+# fails the scan so that it gets an entry.
 NEED_WAIT_STATES = {
     "v_mfma_f32_16x16x32_bf16": 7,
     "v_mfma_f32_32x32x16_bf16": 11,
+    "v_mfma_f32_32x32x2_f32": 19,
 }
 LOOKBACK = 24   # beyond every entry above
 
