@@ -445,7 +445,7 @@ __device__ __forceinline__ void fence_p(bf16x8 (&p)[2][2][2]) {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-// Raw buffer descriptor over [base, base + bytes): offsets past it read as zero.
+// Raw buffer descriptor over [base, base + bytes): per-lane offsets past it read as zero.
 __device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -495,9 +495,12 @@ attn_fwd_q64(AttnIO io) {
   const int nfull = T / kBKV;
   const bool partial = nfull < nkt;
   // Loads of a tile: 32 of 1 KB (4 rows); wave w issues 8, all of K (w < 2)
-  // or all of V, rows 32 (w & 1) + 4 j + (lane >> 4).  The descriptor ends
-  // at key T of this split: rows past it, and tiles past the last, read as
-  // zero.
+  // or all of V, rows 32 (w & 1) + 4 j + (lane >> 4).  A whole tile's loads
+  // take the tile's start as a scalar offset.  Only tiles below nfull are
+  // loaded that way: the partial last tile puts its whole offset in the
+  // per-lane register, with rows past key T clamped to row T - 1 (finite data,
+  // whose scores are masked to -inf, so their weights are 0), and tiles past
+  // the last are not loaded.  No load leaves the split's rows [0, T).
   const uint32_t ldkv2 = (uint32_t)io.ldkv * 2;
   const bf16* base = (wave < 2 ? io.k : io.v) + head * kD + (int64_t)k0 * io.ldkv;
   const rsrc_t rs = buffer_rsrc(base, (uint32_t)(T - 1) * ldkv2 + kD * 2);
@@ -508,9 +511,19 @@ attn_fwd_q64(AttnIO io) {
     loff[j] = (uint32_t)rr * ldkv2 + 16 * ((lane & 15) ^ swz(rr));
   }
   const uint32_t tile_bytes = (uint32_t)kBKV * ldkv2;
-  auto load = [&](int kt, int stage, int j) {
+  auto load = [&](int kt, int stage, int j) {   // kt < nfull
     u32x4* dst = (wave < 2 ? sK[stage] : sV[stage]) + 64 * (8 * (wave & 1) + j);
     lds_dma(rs, dst, loff[j], (uint32_t)kt * tile_bytes);
+  };
+  auto load_any = [&](int kt, int stage, int j) {   // any kt >= 0
+    if (kt < nfull) {
+      load(kt, stage, j);
+    } else if (kt < nkt) {
+      const int rr = 32 * (wave & 1) + 4 * j + (lane >> 4);
+      const int row = min(kt * kBKV + rr, T - 1);
+      u32x4* dst = (wave < 2 ? sK[stage] : sV[stage]) + 64 * (8 * (wave & 1) + j);
+      lds_dma(rs, dst, (uint32_t)row * ldkv2 + 16 * ((lane & 15) ^ swz(rr)), 0);
+    }
   };
 
   // K operand of key half c, k-step st: rows 32 c + l32, dims 16 st + 8 half
@@ -570,9 +583,9 @@ attn_fwd_q64(AttnIO io) {
   // Prologue: tiles 0 and 1 resident, raw scores of tile 0; the references
   // are their row maxima.
 #pragma unroll
-  for (int j = 0; j < 8; ++j) load(0, 0, j);
+  for (int j = 0; j < 8; ++j) load_any(0, 0, j);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) load(1, 1, j);
+  for (int j = 0; j < 8; ++j) load_any(1, 1, j);
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
   for (int st = 0; st < kD / 16; ++st)
@@ -663,15 +676,12 @@ attn_fwd_q64(AttnIO io) {
 
   // Tile kt.  On entry: s[.][0] holds the raw scores of S(kt) key half 0,
   // kf[0..1] the first two K fragments of its key half 1 and
-  // vf[0..1] the first two V fragments of tile kt - 1.
-  // With inline_rule false the step leaves a fired rule to its caller
-  // (returning true, with the sums in lb_s / l_s), so the unrolled loop of
-  // full tiles carries none of the rule's code.
-  float lb_s[2], l_s[2];
+  // vf[0..1] the first two V fragments of tile kt - 1.  With whole_c true
+  // the caller guarantees that tile kt + 2 is a whole tile (kt + 2 < nfull).
   auto step = [&](int kt, auto stage_c, bool has_prev, bool masked, bf16x8 (&pprev)[2][2][2],
-                  bf16x8 (&pcur)[2][2][2], auto inline_rule) -> bool {
+                  bf16x8 (&pcur)[2][2][2], auto whole_c) {
     constexpr int J = decltype(stage_c)::value;
-    constexpr bool INLINE_RULE = decltype(inline_rule)::value;
+    constexpr bool WHOLE = decltype(whole_c)::value;
     const int cur = J >= 0 ? J : kt % NSTAGE;
     const u32x4* __restrict__ sKc = sK[cur];
     const u32x4* __restrict__ sKn = sK[(cur + 1) % NSTAGE];
@@ -714,7 +724,10 @@ attn_fwd_q64(AttnIO io) {
         mfma_pv(acc_o[a][t], vf[f % 3], pprev[a][cu >> 1][cu & 1]);
         if (a == 1 && f + 2 < 16) vf[(f + 2) % 3] = vread(sVp, (f + 2) >> 2, (f + 2) & 3);
       }
-      if (p < 8) load(kt + 2, (cur + 2) % NSTAGE, p);
+      if (p < 8) {
+        if constexpr (WHOLE) load(kt + 2, (cur + 2) % NSTAGE, p);
+        else load_any(kt + 2, (cur + 2) % NSTAGE, p);
+      }
       __builtin_amdgcn_sched_barrier(0);
       pcur[wa][wc][we >> 3][we & 7] = static_cast<bf16>(e0);
       pcur[wa][wc][we >> 3][(we & 7) + 1] = static_cast<bf16>(e1);
@@ -728,14 +741,7 @@ attn_fwd_q64(AttnIO io) {
     l[1] += l2[1];
     const bool fire =
         __builtin_amdgcn_ballot_w64(l[0] > lb[0] + kGuardQ64 || l[1] > lb[1] + kGuardQ64) != 0;
-    if constexpr (INLINE_RULE) {
-      if (__builtin_expect(fire, 0)) rule(kt, sKc, sKn, masked, lb, l, pcur);
-    } else {
-      lb_s[0] = lb[0];
-      lb_s[1] = lb[1];
-      l_s[0] = l[0];
-      l_s[1] = l[1];
-    }
+    if (__builtin_expect(fire, 0)) rule(kt, sKc, sKn, masked, lb, l, pcur);
     l_run[0] = l[0];
     l_run[1] = l[1];
     // the first operands of the next tile (both resident since this tile's barrier)
@@ -743,7 +749,6 @@ attn_fwd_q64(AttnIO io) {
     kf[1] = kread(sKn, 1, 1);
     vf[0] = vread(sV[cur], 0, 0);
     vf[1] = vread(sV[cur], 0, 1);
-    return !INLINE_RULE && fire;
   };
 
   using Stage0 = std::integral_constant<int, 0>;
@@ -751,21 +756,23 @@ attn_fwd_q64(AttnIO io) {
   using Stage2 = std::integral_constant<int, 2>;
   using Stage3 = std::integral_constant<int, 3>;
   using StageR = std::integral_constant<int, -1>;
-  using Inline = std::true_type;
-  // tile t's weights go to pA when t is even, pB when odd
-  step(0, Stage0{}, false, nkt == 1 && partial, pB, pA, Inline{});
+  using Whole = std::true_type;
+  using Any = std::false_type;
+  // tile t's weights go to pA when t is even, pB when odd; the unrolled loop
+  // loads up to tile kt + 5, so it runs while that is a whole tile
+  step(0, Stage0{}, false, nkt == 1 && partial, pB, pA, Any{});
   int kt = 1;
-  for (; kt + 3 < nfull; kt += 4) {
-    step(kt, Stage1{}, true, false, pA, pB, Inline{});
-    step(kt + 1, Stage2{}, true, false, pB, pA, Inline{});
-    step(kt + 2, Stage3{}, true, false, pA, pB, Inline{});
-    step(kt + 3, Stage0{}, true, false, pB, pA, Inline{});
+  for (; kt + 5 < nfull; kt += 4) {
+    step(kt, Stage1{}, true, false, pA, pB, Whole{});
+    step(kt + 1, Stage2{}, true, false, pB, pA, Whole{});
+    step(kt + 2, Stage3{}, true, false, pA, pB, Whole{});
+    step(kt + 3, Stage0{}, true, false, pB, pA, Whole{});
   }
   for (; kt + 1 < nkt; kt += 2) {
-    step(kt, StageR{}, true, false, pA, pB, Inline{});
-    step(kt + 1, StageR{}, true, kt + 1 == nkt - 1 && partial, pB, pA, Inline{});
+    step(kt, StageR{}, true, false, pA, pB, Any{});
+    step(kt + 1, StageR{}, true, kt + 1 == nkt - 1 && partial, pB, pA, Any{});
   }
-  if (kt < nkt) step(kt, StageR{}, true, partial, pA, pB, Inline{});
+  if (kt < nkt) step(kt, StageR{}, true, partial, pA, pB, Any{});
   // the last iteration's scores of a tile past the end land before their
   // registers are reused
   fence_s(s[0][0], s[1][0]);
