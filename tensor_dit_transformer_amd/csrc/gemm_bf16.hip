@@ -845,6 +845,275 @@ gemm_bf16_nt_pp288(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
   store_tiles16<KIND, TM, TN>(acc, p, ep, m0 + 144 * g, n0 + 48 * q, lane);
 }
 
+// 256x256 tile on 4 waves, one per SIMD: wave (wm, wn) owns the 128x128
+// block of C at rows 128 wm, columns 128 wn as 16 accumulator tiles of 32x32
+// (256 registers, held in AGPRs).  A fragment read from LDS feeds 4 MFMAs
+// here against 2 in the 8-wave kernel (whose waves own 128x64), so a K tile
+// costs a third fewer LDS bytes.  With one wave per SIMD that wave's
+// instruction stream alone keeps the matrix core busy:
+//   * a 64-deep K tile is 4 k-steps of 16 MFMAs; the 8 fragments of k-step
+//     s + 1 (4 of A, 4 of B, 16 bytes per lane each) are read while the MFMAs
+//     of k-step s run, one read after every second MFMA;
+//   * A has three LDS stages and B two (96 + 64 KB).  Each wave loads a
+//     quarter of every tile (8 rows per load, 16 loads per K tile), one load
+//     after every fourth MFMA: in K tile k the second half of B tile k + 1
+//     (k-step 0), A tile k + 2 (k-steps 1-2) and the first half of B tile
+//     k + 2 (k-step 3);
+//   * one barrier per K tile, after the first 4 MFMAs of k-step 3: the
+//     fragments of k-step 3 (read during k-step 2) have landed by then, so
+//     the LDS wait before the barrier stalls nothing.  Before it every wave
+//     waits for its loads of B tile k + 1; after it the first fragments of
+//     tile k + 1 are read and B tile k + 2 goes into the stage of tile k.
+// Operand loads take the same buffer descriptors as the 8-wave kernel (rows
+// past M or N read as zero).  The accumulators are stored in place: bias,
+// activation and bf16 rounding are applied in the accumulator registers,
+// then every element goes out with a buffer store whose per-lane offset lies
+// past the output buffer for rows at or past M and columns at or past N.
+// Requires K % 64 == 0, act_from and split multiples of 32 (of 64 for
+// SwiGLU), and (M + 256) ld ES < 2^31 for the outputs as for the operands.
+__device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bitsf(uint32_t x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ uint32_t bf16bits(float x) {
+  const bf16 b = static_cast<bf16>(x);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// all but the newest N loads of this wave have landed (N = 8 or 0)
+template <int N>
+__device__ __forceinline__ void wait_vmem_w128() {
+  static_assert(N == 8 || N == 0, "instantiated counts");
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// this wave's LDS reads have landed, then every wave's (the barrier)
+__device__ __forceinline__ void lds_wait_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// In-place epilogue of a wave's TM x TN accumulator tiles at (row0, col0).
+// FIX selects the activation for all the wave's columns at compile time
+// (1: none, 2: GELU-tanh, 3: SwiGLU) or, with 0, per 32-column block.
+template <OutKind KIND, int TM, int TN, int FIX>
+__device__ __forceinline__ void store_tiles_inplace(f32x16 (&acc)[TM][TN], const GemmProblem& p,
+                                                    const GemmEpilogue& ep, int row0, int col0,
+                                                    int lane) {
+  constexpr int ES = KIND == OutKind::BF16 ? 2 : 4;
+  const int col_l = lane & 31;
+  const int row_l = 4 * (lane >> 5);
+  const uint32_t ld0 = (uint32_t)ep.ld0 * ES, ld1 = (uint32_t)ep.ld1 * ES;
+  const rsrc_t r0 = buffer_rsrc(ep.out0, (uint32_t)p.M * ld0);
+  const rsrc_t r1 = buffer_rsrc(ep.out1, (uint32_t)p.M * ld1);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int cb = col0 + 32 * j;                // the block's first column (wave-uniform)
+    if (cb >= p.N) continue;
+    const bool active = FIX != 0 ? FIX != 1 : (KIND != OutKind::F32_ACC && cb >= ep.act_from);
+    const bool glu = FIX != 0 ? FIX == 3 : (active && ep.act == Act::SWIGLU);
+    const bool gelu = FIX != 0 ? FIX == 2 : (active && ep.act == Act::GELU_TANH);
+    if (glu && (j & 1)) continue;                // an up block, consumed with its gate block
+    const int col = cb + col_l;
+    const int ocb = glu ? ep.act_from + ((cb - ep.act_from) >> 1) : cb;
+    const bool second = ocb >= ep.split;
+    const int ocol = (second ? ocb - ep.split : ocb) + col_l;
+    const uint32_t ld = second ? ld1 : ld0;
+    const rsrc_t r = second ? r1 : r0;
+    const bool colok = col < p.N;
+    float bias = 0.0f, bias_up = 0.0f;
+    if constexpr (KIND != OutKind::F32_ACC) {
+      if (ep.bias && colok) {
+        bias = ep.bias[col];
+        if (glu) bias_up = ep.bias[col + 32];
+      }
+    }
+    // columns past N get an offset past every output buffer
+    const uint32_t lane_off = colok ? (uint32_t)(row0 + row_l) * ld + (uint32_t)ocol * ES : 0xF0000000u;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if constexpr (KIND == OutKind::F32_ACC) {
+        float old[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t rw = 32 * i + 8 * (e >> 2) + (e & 3);
+          old[e] = bitsf(__builtin_amdgcn_raw_buffer_load_b32(r, lane_off + rw * ld, 0, 0));
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] += old[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float v = acc[i][j][e] + bias;
+          if (glu) v = silu(v) * (acc[i][j | 1][e] + bias_up);
+          else if (gelu) v = gelu_tanh(v);
+          acc[i][j][e] = ES == 2 ? bitsf(bf16bits(v)) : v;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t rw = 32 * i + 8 * (e >> 2) + (e & 3);
+        const uint32_t x = fbits(acc[i][j][e]);
+        if constexpr (ES == 2)
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)x, r, lane_off + rw * ld, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(x, r, lane_off + rw * ld, 0, 0);
+      }
+    }
+  }
+}
+
+template <OutKind KIND>
+__global__ void __launch_bounds__(256, 1)
+gemm_bf16_nt_w128(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
+  constexpr int TM = 4, TN = 4;
+  constexpr int A_STAGE = 256 * kRowChunks, B_STAGE = 256 * kRowChunks;
+  __shared__ u32x4 smem[3 * A_STAGE + 2 * B_STAGE];   // 160 KB
+
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, per = nb >> 3, rem = nb & 7;
+  const int id = xcd * per + min(xcd, rem) + (bid >> 3);
+  const int group = id / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = id - group * kGroupM * tiles_n;
+  const int m0 = (first_m + in_group % gm) * 256;
+  const int n0 = (in_group / gm) * 256;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lda2 = (uint32_t)p.lda * 2, ldb2 = (uint32_t)p.ldb * 2;
+  const rsrc_t ra = buffer_rsrc(p.A, (uint32_t)(p.M - 1) * lda2 + (uint32_t)p.K * 2);
+  const rsrc_t rb = buffer_rsrc(p.B, (uint32_t)(p.N - 1) * ldb2 + (uint32_t)p.K * 2);
+  // Wave w loads tile rows [64 w, 64 w + 64) of A and of B, 8 per load; lane
+  // l reads row R + (l >> 3) into physical chunk l & 7 (the swizzle).
+  const int lr = lane >> 3, lc = lane & 7;
+  uint32_t voa[8], vob[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int R = wave * 64 + 8 * j;
+    voa[j] = (uint32_t)(m0 + R + lr) * lda2 + (uint32_t)((lc ^ lr ^ ((R >> 3) & 1)) * 16);
+    vob[j] = (uint32_t)(n0 + R + lr) * ldb2 + (uint32_t)((lc ^ lr ^ ((R >> 3) & 1)) * 16);
+  }
+  auto stage_a = [&](int kt) { return smem + (kt % 3) * A_STAGE; };
+  auto stage_b = [&](int kt) { return smem + 3 * A_STAGE + (kt & 1) * B_STAGE; };
+  auto load_a = [&](int kt, int j) {
+    lds_dma(ra, stage_a(kt) + (wave * 64 + 8 * j) * kRowChunks, voa[j], (uint32_t)kt * (kBK * 2));
+  };
+  auto load_b = [&](int kt, int j) {
+    lds_dma(rb, stage_b(kt) + (wave * 64 + 8 * j) * kRowChunks, vob[j], (uint32_t)kt * (kBK * 2));
+  };
+  const int a_row = 128 * wm + (lane & 31), b_row = 128 * wn + (lane & 31), khalf = lane >> 5;
+  bf16x8 fa[2][TM], fb[2][TN];
+  // fragment r of k-step kc / 2 of tile kt into buffer buf: A tile i = r (r < 4), B tile j = r - 4
+  auto read_frag = [&](int kt, int kc, int buf, int r) {
+    if (r < TM) {
+      const u32x4* sa = stage_a(kt);
+      fa[buf][r] = __builtin_bit_cast(bf16x8, sa[(a_row + 32 * r) * kRowChunks + swizzle(a_row, kc)]);
+    } else {
+      const u32x4* sb = stage_b(kt);
+      fb[buf][r - TM] = __builtin_bit_cast(bf16x8, sb[(b_row + 32 * (r - TM)) * kRowChunks + swizzle(b_row, kc)]);
+    }
+  };
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  auto mfma = [&](int buf, int m) {
+    acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][m >> 2], fb[buf][m & 3],
+                                                                 acc[m >> 2][m & 3], 0, 0, 0);
+  };
+
+  const int nk = p.K / kBK;
+  // prologue: B tile 0 and A tiles 0 and 1, then the first half of B tile 1
+#pragma unroll
+  for (int j = 0; j < 8; ++j) load_b(0, j);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) load_a(0, j);
+  if (nk > 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) load_a(1, j);
+  }
+  wait_vmem_w128<0>();
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 8; ++r) read_frag(0, khalf, 0, r);
+  if (nk > 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load_b(1, j);
+  }
+
+  // K tile kt.  NEXT2: tile kt + 2 exists; NEXT1: tile kt + 1 exists.
+  auto tile = [&](int kt, auto next2_c, auto next1_c) {
+    constexpr bool NEXT2 = decltype(next2_c)::value;
+    constexpr bool NEXT1 = decltype(next1_c)::value;
+    // k-steps 0-2: fragments of k-step s + 1 after MFMAs 0, 2, .., 14;
+    // loads after MFMAs 0, 4, 8, 12
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      const int buf = s & 1;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        mfma(buf, m);
+        __builtin_amdgcn_sched_barrier(0);
+        if ((m & 1) == 0) read_frag(kt, 2 * (s + 1) + khalf, buf ^ 1, m >> 1);
+        if ((m & 3) == 0) {
+          if (s == 0) {
+            if constexpr (NEXT1) load_b(kt + 1, 4 + (m >> 2));
+          } else {
+            if constexpr (NEXT2) load_a(kt + 2, 4 * (s - 1) + (m >> 2));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // k-step 3 (buffer 1): the barrier after MFMA 3; then tile kt + 1's
+    // first fragments after MFMAs 4-11 and B tile kt + 2's first half
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      mfma(1, m);
+      __builtin_amdgcn_sched_barrier(0);
+      if (m == 3) {
+        if constexpr (NEXT2) wait_vmem_w128<8>(); else wait_vmem_w128<0>();
+        lds_wait_barrier();
+      }
+      if (m >= 4 && m < 12) {
+        if constexpr (NEXT1) read_frag(kt + 1, khalf, 0, m - 4);
+        if ((m & 1) == 0) {
+          if constexpr (NEXT2) load_b(kt + 2, (m - 4) >> 1);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) tile(kt, T_{}, T_{});
+  if (kt + 1 < nk) {
+    tile(kt, F_{}, T_{});
+    ++kt;
+  }
+  tile(kt, F_{}, F_{});
+
+  // one activation for the wave's 128 columns when they lie on one side of act_from
+  const int c0 = n0 + 128 * wn, r0 = m0 + 128 * wm;
+  if (KIND == OutKind::F32_ACC || c0 + 128 <= ep.act_from || ep.act == Act::NONE)
+    store_tiles_inplace<KIND, TM, TN, 1>(acc, p, ep, r0, c0, lane);
+  else if (c0 >= ep.act_from && ep.act == Act::GELU_TANH)
+    store_tiles_inplace<KIND, TM, TN, 2>(acc, p, ep, r0, c0, lane);
+  else if (c0 >= ep.act_from && ep.act == Act::SWIGLU)
+    store_tiles_inplace<KIND, TM, TN, 3>(acc, p, ep, r0, c0, lane);
+  else
+    store_tiles_inplace<KIND, TM, TN, 0>(acc, p, ep, r0, c0, lane);
+}
+
 hipError_t launch_288(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind, hipStream_t stream) {
   const int tm = (p.M + 287) / 288, tn = (p.N + 191) / 192;
   const dim3 grid(tm * tn), block(512);
@@ -857,6 +1126,23 @@ hipError_t launch_288(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind
       break;
     case OutKind::F32_ACC:
       hipLaunchKernelGGL((gemm_bf16_nt_pp288<OutKind::F32_ACC>), grid, block, 0, stream, p, ep, tm, tn);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_w128(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind, hipStream_t stream) {
+  const int tm = (p.M + 255) / 256, tn = (p.N + 255) / 256;
+  const dim3 grid(tm * tn), block(256);
+  switch (kind) {
+    case OutKind::BF16:
+      hipLaunchKernelGGL((gemm_bf16_nt_w128<OutKind::BF16>), grid, block, 0, stream, p, ep, tm, tn);
+      break;
+    case OutKind::F32_STORE:
+      hipLaunchKernelGGL((gemm_bf16_nt_w128<OutKind::F32_STORE>), grid, block, 0, stream, p, ep, tm, tn);
+      break;
+    case OutKind::F32_ACC:
+      hipLaunchKernelGGL((gemm_bf16_nt_w128<OutKind::F32_ACC>), grid, block, 0, stream, p, ep, tm, tn);
       break;
   }
   return hipGetLastError();
@@ -935,6 +1221,14 @@ hipError_t launch_gemm_bf16(const GemmProblem& p, const GemmEpilogue& ep, OutKin
     // M = 4608, N = 2304); if 192-row tiles still fit in one round, every
     // busy CU has 3/4 of the work.
     if (big < 256 && mid <= 256) return launch_8w<3>(p, ep, kind, stream);
+    // the one-wave-per-SIMD kernel where its in-place epilogue applies: the
+    // activation and the output split fall on 32-column blocks (64 for
+    // SwiGLU) and every output offset fits 31 bits
+    const int64_t es = kind == OutKind::BF16 ? 2 : 4;
+    const bool out_fits = (int64_t)(p.M + 256) * ep.ld0 * es < ((int64_t)1 << 31) &&
+                          (ep.out1 == nullptr || (int64_t)(p.M + 256) * ep.ld1 * es < ((int64_t)1 << 31));
+    const bool blocks = ep.split % 32 == 0 && ep.act_from % (ep.act == Act::SWIGLU ? 64 : 32) == 0;
+    if (out_fits && blocks) return launch_w128(p, ep, kind, stream);
     return launch_8w<4>(p, ep, kind, stream);
   }
   if (big >= 256) return launch_tile<bf16, 256, 256, 2, 2>(p, ep, kind, stream);
