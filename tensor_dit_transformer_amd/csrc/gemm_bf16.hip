@@ -863,7 +863,8 @@ gemm_bf16_nt_pp288(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
 //     fragments of k-step 3 (read during k-step 2) have landed by then, so
 //     the LDS wait before the barrier stalls nothing.  Before it every wave
 //     waits for its loads of B tile k + 1; after it the first fragments of
-//     tile k + 1 are read and B tile k + 2 goes into the stage of tile k.
+//     tile k + 1 are read (two per MFMA) and B tile k + 2 goes into the
+//     stage of tile k.
 // Operand loads take the same buffer descriptors as the 8-wave kernel (rows
 // past M or N read as zero).  The accumulators are stored in place: bias,
 // activation and bf16 rounding are applied in the accumulator registers,
@@ -1074,7 +1075,9 @@ gemm_bf16_nt_w128(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
       }
     }
     // k-step 3 (buffer 1): the barrier after MFMA 3; then tile kt + 1's
-    // first fragments after MFMAs 4-11 and B tile kt + 2's first half
+    // first fragments, two after each of MFMAs 4-7 (so they have landed
+    // well before the next K tile's first MFMAs), and B tile kt + 2's first
+    // half after MFMAs 8-11
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       mfma(1, m);
@@ -1083,11 +1086,14 @@ gemm_bf16_nt_w128(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
         if constexpr (NEXT2) wait_vmem_w128<8>(); else wait_vmem_w128<0>();
         lds_wait_barrier();
       }
-      if (m >= 4 && m < 12) {
-        if constexpr (NEXT1) read_frag(kt + 1, khalf, 0, m - 4);
-        if ((m & 1) == 0) {
-          if constexpr (NEXT2) load_b(kt + 2, (m - 4) >> 1);
+      if (m >= 4 && m < 8) {
+        if constexpr (NEXT1) {
+          read_frag(kt + 1, khalf, 0, 2 * (m - 4));
+          read_frag(kt + 1, khalf, 0, 2 * (m - 4) + 1);
         }
+      }
+      if (m >= 8 && m < 12) {
+        if constexpr (NEXT2) load_b(kt + 2, m - 8);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
