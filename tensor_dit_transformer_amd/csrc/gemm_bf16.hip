@@ -900,7 +900,7 @@ __device__ __forceinline__ void lds_wait_barrier() {
 // FIX selects the activation for all the wave's columns at compile time
 // (1: none, 2: GELU-tanh, 3: SwiGLU) or, with 0, per 32-column block.
 template <OutKind KIND, int TM, int TN, int FIX>
-__device__ __forceinline__ void store_tiles_inplace(f32x16 (&acc)[TM][TN], const GemmProblem& p,
+__device__ __forceinline__ void store_tiles_inplace(const f32x16 (&acc)[TM][TN], const GemmProblem& p,
                                                     const GemmEpilogue& ep, int row0, int col0,
                                                     int lane) {
   constexpr int ES = KIND == OutKind::BF16 ? 2 : 4;
@@ -935,6 +935,9 @@ __device__ __forceinline__ void store_tiles_inplace(f32x16 (&acc)[TM][TN], const
     const uint32_t lane_off = colok ? (uint32_t)(row0 + row_l) * ld + (uint32_t)ocol * ES : 0xF0000000u;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      // one accumulator tile at a time (the barrier below keeps the
+      // scheduler from reading every tile out of the accumulators at once)
+      f32x16 out = acc[i][j];
       if constexpr (KIND == OutKind::F32_ACC) {
         float old[16];
 #pragma unroll
@@ -943,45 +946,61 @@ __device__ __forceinline__ void store_tiles_inplace(f32x16 (&acc)[TM][TN], const
           old[e] = bitsf(__builtin_amdgcn_raw_buffer_load_b32(r, lane_off + rw * ld, 0, 0));
         }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] += old[e];
+        for (int e = 0; e < 16; ++e) out[e] += old[e];
       } else {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float v = acc[i][j][e] + bias;
+          float v = out[e] + bias;
           if (glu) v = silu(v) * (acc[i][j | 1][e] + bias_up);
           else if (gelu) v = gelu_tanh(v);
-          acc[i][j][e] = ES == 2 ? bitsf(bf16bits(v)) : v;
+          out[e] = ES == 2 ? bitsf(bf16bits(v)) : v;
         }
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const uint32_t rw = 32 * i + 8 * (e >> 2) + (e & 3);
-        const uint32_t x = fbits(acc[i][j][e]);
+        const uint32_t x = fbits(out[e]);
         if constexpr (ES == 2)
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)x, r, lane_off + rw * ld, 0, 0);
         else
           __builtin_amdgcn_raw_buffer_store_b32(x, r, lane_off + rw * ld, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-template <OutKind KIND>
+template <OutKind KIND, bool PERSIST>
 __global__ void __launch_bounds__(256, 1)
 gemm_bf16_nt_w128(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
   constexpr int TM = 4, TN = 4;
   constexpr int A_STAGE = 256 * kRowChunks, B_STAGE = 256 * kRowChunks;
   __shared__ u32x4 smem[3 * A_STAGE + 2 * B_STAGE];   // 160 KB
 
-  const int nb = gridDim.x, bid = blockIdx.x;
-  const int xcd = bid & 7, per = nb >> 3, rem = nb & 7;
-  const int id = xcd * per + min(xcd, rem) + (bid >> 3);
-  const int group = id / (kGroupM * tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int in_group = id - group * kGroupM * tiles_n;
-  const int m0 = (first_m + in_group % gm) * 256;
-  const int n0 = (in_group / gm) * 256;
+  // Persistent: workgroup b takes one tile per round of G tiles, the
+  // (b >> 3)-th of its XCD's contiguous stretch of the round (XCD b & 7) in
+  // the grouped tile order.
+  const int ntiles = tiles_m * tiles_n;
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3;
+  auto tile_id = [&](int round) -> int {
+    const int base = round * G;
+    if (base >= ntiles) return -1;
+    const int count = min(G, ntiles - base);
+    const int per = count >> 3, rem = count & 7;
+    if (slot >= per + (xcd < rem ? 1 : 0)) return -1;
+    return base + xcd * per + min(xcd, rem) + slot;
+  };
+  auto origin = [&](int id, int& m0, int& n0) {
+    const int group = id / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM);
+    const int in_group = id - group * kGroupM * tiles_n;
+    m0 = (first_m + in_group % gm) * 256;
+    n0 = (in_group / gm) * 256;
+  };
+  const int full_rounds = ntiles / G;
+  const int n_mine = PERSIST ? full_rounds + (tile_id(full_rounds) >= 0 ? 1 : 0) : 1;   // >= 1
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -990,70 +1009,90 @@ gemm_bf16_nt_w128(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
   const rsrc_t ra = buffer_rsrc(p.A, (uint32_t)(p.M - 1) * lda2 + (uint32_t)p.K * 2);
   const rsrc_t rb = buffer_rsrc(p.B, (uint32_t)(p.N - 1) * ldb2 + (uint32_t)p.K * 2);
   // Wave w loads tile rows [64 w, 64 w + 64) of A and of B, 8 per load; lane
-  // l reads row R + (l >> 3) into physical chunk l & 7 (the swizzle).
+  // l reads row R + (l >> 3) into physical chunk l & 7 (the swizzle).  The
+  // per-lane offset is this part plus the tile's first row times the row
+  // pitch, so rows past M or N lie past the descriptors and read as zero.
   const int lr = lane >> 3, lc = lane & 7;
   uint32_t voa[8], vob[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int R = wave * 64 + 8 * j;
-    voa[j] = (uint32_t)(m0 + R + lr) * lda2 + (uint32_t)((lc ^ lr ^ ((R >> 3) & 1)) * 16);
-    vob[j] = (uint32_t)(n0 + R + lr) * ldb2 + (uint32_t)((lc ^ lr ^ ((R >> 3) & 1)) * 16);
+    voa[j] = (uint32_t)(R + lr) * lda2 + (uint32_t)((lc ^ lr ^ ((R >> 3) & 1)) * 16);
+    vob[j] = (uint32_t)(R + lr) * ldb2 + (uint32_t)((lc ^ lr ^ ((R >> 3) & 1)) * 16);
   }
-  auto stage_a = [&](int kt) { return smem + (kt % 3) * A_STAGE; };
-  auto stage_b = [&](int kt) { return smem + 3 * A_STAGE + (kt & 1) * B_STAGE; };
-  auto load_a = [&](int kt, int j) {
-    lds_dma(ra, stage_a(kt) + (wave * 64 + 8 * j) * kRowChunks, voa[j], (uint32_t)kt * (kBK * 2));
+  // origins of this workgroup's current and next tile
+  int m0, n0, m0n = 0, n0n = 0;
+  origin(tile_id(0), m0, n0);
+  if (n_mine > 1) origin(tile_id(1), m0n, n0n);
+  const int nk = p.K / kBK;
+  // global K-tile u of this workgroup's stream: A stage u % 3, B stage u % 2
+  auto stage_a = [&](int u) { return smem + (u % 3) * A_STAGE; };
+  auto stage_b = [&](int u) { return smem + 3 * A_STAGE + (u & 1) * B_STAGE; };
+  // loads of global K-tile u, K-tile kt of the current tile (kt >= nk: of the next)
+  auto load_a = [&](int u, int kt, int j) {
+    const bool nxt = kt >= nk;
+    const uint32_t row = (uint32_t)(nxt ? m0n : m0) * lda2;
+    lds_dma(ra, stage_a(u) + (wave * 64 + 8 * j) * kRowChunks, voa[j] + row,
+            (uint32_t)(nxt ? kt - nk : kt) * (kBK * 2));
   };
-  auto load_b = [&](int kt, int j) {
-    lds_dma(rb, stage_b(kt) + (wave * 64 + 8 * j) * kRowChunks, vob[j], (uint32_t)kt * (kBK * 2));
+  auto load_b = [&](int u, int kt, int j) {
+    const bool nxt = kt >= nk;
+    const uint32_t row = (uint32_t)(nxt ? n0n : n0) * ldb2;
+    lds_dma(rb, stage_b(u) + (wave * 64 + 8 * j) * kRowChunks, vob[j] + row,
+            (uint32_t)(nxt ? kt - nk : kt) * (kBK * 2));
   };
   const int a_row = 128 * wm + (lane & 31), b_row = 128 * wn + (lane & 31), khalf = lane >> 5;
   bf16x8 fa[2][TM], fb[2][TN];
-  // fragment r of k-step kc / 2 of tile kt into buffer buf: A tile i = r (r < 4), B tile j = r - 4
-  auto read_frag = [&](int kt, int kc, int buf, int r) {
+  // fragment r of k-group kc of global K-tile u into buffer buf: A tile i = r
+  // (r < 4), B tile j = r - 4
+  auto read_frag = [&](int u, int kc, int buf, int r) {
     if (r < TM) {
-      const u32x4* sa = stage_a(kt);
+      const u32x4* sa = stage_a(u);
       fa[buf][r] = __builtin_bit_cast(bf16x8, sa[(a_row + 32 * r) * kRowChunks + swizzle(a_row, kc)]);
     } else {
-      const u32x4* sb = stage_b(kt);
+      const u32x4* sb = stage_b(u);
       fb[buf][r - TM] = __builtin_bit_cast(bf16x8, sb[(b_row + 32 * (r - TM)) * kRowChunks + swizzle(b_row, kc)]);
     }
   };
   f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   auto mfma = [&](int buf, int m) {
     acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][m >> 2], fb[buf][m & 3],
                                                                  acc[m >> 2][m & 3], 0, 0, 0);
   };
+  // a tile's first k-step starts its accumulators from zero
+  auto mfma0 = [&](int m) {
+    const f32x16 zero = {};
+    acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][m >> 2], fb[0][m & 3], zero, 0, 0, 0);
+  };
 
-  const int nk = p.K / kBK;
-  // prologue: B tile 0 and A tiles 0 and 1, then the first half of B tile 1
+  const int total = n_mine * nk;   // K tiles in this workgroup's stream
+  // prologue: B and A of K-tile 0, A of K-tile 1, then the first half of B of K-tile 1
 #pragma unroll
-  for (int j = 0; j < 8; ++j) load_b(0, j);
+  for (int j = 0; j < 8; ++j) load_b(0, 0, j);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) load_a(0, j);
-  if (nk > 1) {
+  for (int j = 0; j < 8; ++j) load_a(0, 0, j);
+  if (total > 1) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) load_a(1, j);
+    for (int j = 0; j < 8; ++j) load_a(1, 1, j);
   }
   wait_vmem_w128<0>();
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 8; ++r) read_frag(0, khalf, 0, r);
-  if (nk > 1) {
+  if (total > 1) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_b(1, j);
+    for (int j = 0; j < 4; ++j) load_b(1, 1, j);
   }
 
-  // K tile kt.  NEXT2: tile kt + 2 exists; NEXT1: tile kt + 1 exists.
-  auto tile = [&](int kt, auto next2_c, auto next1_c) {
+  // Global K tile u = K tile kt of the current tile.  NEXT2: K tile u + 2
+  // exists; NEXT1: u + 1 exists (either may be in the next tile); FRAG1:
+  // u + 1's first fragments are read here (not in a tile's last K tile, so
+  // that no fragment registers stay live across the tile's stores).
+  auto ktile = [&](int u, int kt, auto next2_c, auto next1_c, auto frag1_c, auto first_c) {
     constexpr bool NEXT2 = decltype(next2_c)::value;
     constexpr bool NEXT1 = decltype(next1_c)::value;
+    constexpr bool FRAG1 = decltype(frag1_c)::value;
+    constexpr bool FIRST = decltype(first_c)::value;   // the tile's first K tile
     // k-steps 0-2: fragments of k-step s + 1 after MFMAs 0, 2, .., 14;
     // loads after MFMAs 0, 4, 8, 12
 #pragma unroll
@@ -1061,23 +1100,22 @@ gemm_bf16_nt_w128(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
       const int buf = s & 1;
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
-        mfma(buf, m);
+        if (PERSIST && FIRST && s == 0) mfma0(m); else mfma(buf, m);
         __builtin_amdgcn_sched_barrier(0);
-        if ((m & 1) == 0) read_frag(kt, 2 * (s + 1) + khalf, buf ^ 1, m >> 1);
+        if ((m & 1) == 0) read_frag(u, 2 * (s + 1) + khalf, buf ^ 1, m >> 1);
         if ((m & 3) == 0) {
           if (s == 0) {
-            if constexpr (NEXT1) load_b(kt + 1, 4 + (m >> 2));
+            if constexpr (NEXT1) load_b(u + 1, kt + 1, 4 + (m >> 2));
           } else {
-            if constexpr (NEXT2) load_a(kt + 2, 4 * (s - 1) + (m >> 2));
+            if constexpr (NEXT2) load_a(u + 2, kt + 2, 4 * (s - 1) + (m >> 2));
           }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // k-step 3 (buffer 1): the barrier after MFMA 3; then tile kt + 1's
-    // first fragments, two after each of MFMAs 4-7 (so they have landed
-    // well before the next K tile's first MFMAs), and B tile kt + 2's first
-    // half after MFMAs 8-11
+    // k-step 3 (buffer 1): the barrier after MFMA 3; then K-tile u + 1's
+    // first fragments, two after each of MFMAs 4-7 (so they have landed well
+    // before its first MFMAs), and the first half of B of u + 2 after MFMAs 8-11
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       mfma(1, m);
@@ -1087,37 +1125,84 @@ gemm_bf16_nt_w128(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
         lds_wait_barrier();
       }
       if (m >= 4 && m < 8) {
-        if constexpr (NEXT1) {
-          read_frag(kt + 1, khalf, 0, 2 * (m - 4));
-          read_frag(kt + 1, khalf, 0, 2 * (m - 4) + 1);
+        if constexpr (FRAG1) {
+          read_frag(u + 1, khalf, 0, 2 * (m - 4));
+          read_frag(u + 1, khalf, 0, 2 * (m - 4) + 1);
         }
       }
       if (m >= 8 && m < 12) {
-        if constexpr (NEXT2) load_b(kt + 2, m - 8);
+        if constexpr (NEXT2) load_b(u + 2, kt + 2, m - 8);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  int kt = 0;
-  for (; kt + 2 < nk; ++kt) tile(kt, T_{}, T_{});
-  if (kt + 1 < nk) {
-    tile(kt, F_{}, T_{});
-    ++kt;
+  // the tile's results (with the persistent grid, the loads of the next
+  // tile's first K tiles are in flight meanwhile)
+  auto epilogue = [&]() {
+    const int c0 = n0 + 128 * wn, r0 = m0 + 128 * wm;
+    // one activation for the wave's 128 columns when they lie on one side of act_from
+    if (KIND == OutKind::F32_ACC || c0 + 128 <= ep.act_from || ep.act == Act::NONE)
+      store_tiles_inplace<KIND, TM, TN, 1>(acc, p, ep, r0, c0, lane);
+    else if (c0 >= ep.act_from && ep.act == Act::GELU_TANH)
+      store_tiles_inplace<KIND, TM, TN, 2>(acc, p, ep, r0, c0, lane);
+    else if (c0 >= ep.act_from && ep.act == Act::SWIGLU)
+      store_tiles_inplace<KIND, TM, TN, 3>(acc, p, ep, r0, c0, lane);
+    else
+      store_tiles_inplace<KIND, TM, TN, 0>(acc, p, ep, r0, c0, lane);
+  };
+  if constexpr (!PERSIST) {
+    // one tile: accumulators from zero, K tiles in one loop
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) ktile(kt, kt, T_{}, T_{}, T_{}, F_{});
+    if (kt + 1 < nk) {
+      ktile(kt, kt, F_{}, T_{}, T_{}, F_{});
+      ++kt;
+    }
+    ktile(kt, kt, F_{}, F_{}, F_{}, F_{});
+    epilogue();
+    return;
+  } else {
+    int u = 0;
+    for (int t = 0; t < n_mine; ++t) {
+      // the tile's first K tile starts its accumulators from zero (nk >= 2)
+      int kt = 0;
+      if (t + 1 < n_mine) {
+        ktile(u, kt, T_{}, T_{}, T_{}, T_{});
+        for (++kt, ++u; kt + 1 < nk; ++kt, ++u) ktile(u, kt, T_{}, T_{}, T_{}, F_{});
+        ktile(u, kt, T_{}, T_{}, F_{}, F_{});
+        ++u;
+      } else {
+        if (nk == 2) ktile(u, kt, F_{}, T_{}, T_{}, T_{});
+        else ktile(u, kt, T_{}, T_{}, T_{}, T_{});
+        for (++kt, ++u; kt + 2 < nk; ++kt, ++u) ktile(u, kt, T_{}, T_{}, T_{}, F_{});
+        if (kt + 1 < nk) {
+          ktile(u, kt, F_{}, T_{}, T_{}, F_{});
+          ++kt;
+          ++u;
+        }
+        ktile(u, kt, F_{}, F_{}, F_{}, F_{});
+        ++u;
+      }
+      epilogue();
+      if (t + 1 < n_mine) {
+        m0 = m0n;
+        n0 = n0n;
+        if (t + 2 < n_mine) origin(tile_id(t + 2), m0n, n0n);
+        // the next tile's first fragments (its first K tile was published
+        // by the barrier of this tile's last one)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) read_frag(u, khalf, 0, r);
+      }
+    }
   }
-  tile(kt, F_{}, F_{});
-
-  // one activation for the wave's 128 columns when they lie on one side of act_from
-  const int c0 = n0 + 128 * wn, r0 = m0 + 128 * wm;
-  if (KIND == OutKind::F32_ACC || c0 + 128 <= ep.act_from || ep.act == Act::NONE)
-    store_tiles_inplace<KIND, TM, TN, 1>(acc, p, ep, r0, c0, lane);
-  else if (c0 >= ep.act_from && ep.act == Act::GELU_TANH)
-    store_tiles_inplace<KIND, TM, TN, 2>(acc, p, ep, r0, c0, lane);
-  else if (c0 >= ep.act_from && ep.act == Act::SWIGLU)
-    store_tiles_inplace<KIND, TM, TN, 3>(acc, p, ep, r0, c0, lane);
-  else
-    store_tiles_inplace<KIND, TM, TN, 0>(acc, p, ep, r0, c0, lane);
 }
 
 hipError_t launch_288(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind, hipStream_t stream) {
@@ -1137,18 +1222,52 @@ hipError_t launch_288(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device; 256 on MI355X).
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// One workgroup per compute unit, each looping over its tiles, when every
+// tile costs the same: then the next tile's first loads overlap this tile's
+// stores.  When an activation covers only part of the columns (the fused
+// QKV + up projection), its tiles' epilogues cost several times the others',
+// and one tile per workgroup lets the hardware's dispatch even out the
+// compute units' loads instead.  Also one tile per workgroup when K is a
+// single K tile, which the stream's two-ahead loads would otherwise reach
+// past the next tile.
 hipError_t launch_w128(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind, hipStream_t stream) {
   const int tm = (p.M + 255) / 256, tn = (p.N + 255) / 256;
-  const dim3 grid(tm * tn), block(256);
+  const int ntiles = tm * tn;
+  const bool mixed = kind != OutKind::F32_ACC && ep.act != Act::NONE && ep.act_from > 0 && ep.act_from < p.N;
+  const bool persist = p.K / kBK >= 2 && !mixed && ntiles > cu_count();
+  const dim3 grid(persist ? cu_count() : ntiles), block(256);
   switch (kind) {
     case OutKind::BF16:
-      hipLaunchKernelGGL((gemm_bf16_nt_w128<OutKind::BF16>), grid, block, 0, stream, p, ep, tm, tn);
+      if (persist)
+        hipLaunchKernelGGL((gemm_bf16_nt_w128<OutKind::BF16, true>), grid, block, 0, stream, p, ep, tm, tn);
+      else
+        hipLaunchKernelGGL((gemm_bf16_nt_w128<OutKind::BF16, false>), grid, block, 0, stream, p, ep, tm, tn);
       break;
     case OutKind::F32_STORE:
-      hipLaunchKernelGGL((gemm_bf16_nt_w128<OutKind::F32_STORE>), grid, block, 0, stream, p, ep, tm, tn);
+      if (persist)
+        hipLaunchKernelGGL((gemm_bf16_nt_w128<OutKind::F32_STORE, true>), grid, block, 0, stream, p, ep, tm, tn);
+      else
+        hipLaunchKernelGGL((gemm_bf16_nt_w128<OutKind::F32_STORE, false>), grid, block, 0, stream, p, ep, tm, tn);
       break;
     case OutKind::F32_ACC:
-      hipLaunchKernelGGL((gemm_bf16_nt_w128<OutKind::F32_ACC>), grid, block, 0, stream, p, ep, tm, tn);
+      if (persist)
+        hipLaunchKernelGGL((gemm_bf16_nt_w128<OutKind::F32_ACC, true>), grid, block, 0, stream, p, ep, tm, tn);
+      else
+        hipLaunchKernelGGL((gemm_bf16_nt_w128<OutKind::F32_ACC, false>), grid, block, 0, stream, p, ep, tm, tn);
       break;
   }
   return hipGetLastError();

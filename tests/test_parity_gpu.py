@@ -269,8 +269,24 @@ def test_288_row_tiles_fused_colwise_split_and_block_out():
     close_all(shards)
 
 
+def test_persistent_gemm_several_tiles_per_workgroup_gelu_all_columns():
+    # MLP-only, P = 1: the up-projection (N = 16384, M = 2248 = 8 x 256 + 200,
+    # K = 1024) has 9 x 64 = 576 tiles of 256 x 256 with GELU on every
+    # column, so the one-wave-per-SIMD kernel runs persistent: 256
+    # workgroups, two full rounds and a last one of 64 tiles, each workgroup
+    # loading its next tile's first K tiles before storing the current one.
+    w = Workload("persist_mlp_T2248_D1024_F16384_P1", 2248, 1024, 0, 0, 16384, 1, "bf16")
+    inp = tp_inputs.make_inputs(w, seed=31)
+    ranks, y_ref = full_oracle(w, inp)
+    shards, outs, y = run_all_ranks(w, inp)
+    check_rank(w, outs[0], ranks[0], H.TOL["bf16"], w.name)
+    assert H.rel_err(H.as_f64(y), y_ref) <= H.TOL["bf16"]
+    close_all(shards)
+
+
 def test_large_rowwise_store_and_accumulate_paths():
-    # MLP-only, P = 1, hidden 8192: the down projection is N = 8192 -> 9 x 32 tiles
+    # MLP-only, P = 1, hidden 8192: the down projection is N = 8192 -> 9 x 32 =
+    # 288 tiles, on 256 persistent workgroups (a last round of 32 tiles)
     w = Workload("big_down_T2125_D8192_F1024_P1", 2125, 8192, 0, 0, 1024, 1, "bf16")
     inp = tp_inputs.make_inputs(w, seed=22)
     ranks, y_ref = full_oracle(w, inp)

@@ -161,6 +161,22 @@ def test_bf16_swiglu_block_on_the_8wave_path():
     close(shards)
 
 
+def test_bf16_swiglu_persistent_gemm_all_columns():
+    """MLP-only, P = 1, T = 2248: the gate/up projection has N = 2 x 8192
+    columns, all SwiGLU (9 x 64 = 576 tiles of 256 x 256), so the
+    one-wave-per-SIMD kernel runs persistent (256 workgroups, a last round of
+    64 tiles) with the SwiGLU epilogue; the ragged last tile row stores 200
+    of its 256 rows."""
+    w = Workload("swiglu_mlp_T2248_D1024_F8192_P1", 2248, 1024, 0, 0, 8192, 1, "bf16",
+                 mlp_act="swiglu")
+    inp = tp_inputs.make_inputs(w, seed=12)
+    refs = rank_refs(w, inp)
+    shards, outs = run(w, inp)
+    for r, (b, ref) in enumerate(zip(outs, refs)):
+        check(b, ref, H.TOL["bf16"], f"persistent SwiGLU rank {r}")
+    close(shards)
+
+
 @pytest.mark.parametrize("T", [2100, 2300])
 def test_bf16_swiglu_8wave_ragged_rows(T):
     """The same block at T = 2100 (9 x 22 = 198 tiles of 256 rows, 242 of
