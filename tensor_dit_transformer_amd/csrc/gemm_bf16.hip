@@ -900,7 +900,7 @@ __device__ __forceinline__ void lds_wait_barrier() {
 // FIX selects the activation for all the wave's columns at compile time
 // (1: none, 2: GELU-tanh, 3: SwiGLU) or, with 0, per 32-column block.
 template <OutKind KIND, int TM, int TN, int FIX>
-__device__ __forceinline__ void store_tiles_inplace(const f32x16 (&acc)[TM][TN], const GemmProblem& p,
+__device__ __forceinline__ void store_tiles_inplace(f32x16 (&acc)[TM][TN], const GemmProblem& p,
                                                     const GemmEpilogue& ep, int row0, int col0,
                                                     int lane) {
   constexpr int ES = KIND == OutKind::BF16 ? 2 : 4;
@@ -935,9 +935,9 @@ __device__ __forceinline__ void store_tiles_inplace(const f32x16 (&acc)[TM][TN],
     const uint32_t lane_off = colok ? (uint32_t)(row0 + row_l) * ld + (uint32_t)ocol * ES : 0xF0000000u;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      // one accumulator tile at a time (the barrier below keeps the
-      // scheduler from reading every tile out of the accumulators at once)
-      f32x16 out = acc[i][j];
+      // each element computed in its own accumulator register and stored
+      // from there: no store's data register is rewritten while the store
+      // may be in flight
       if constexpr (KIND == OutKind::F32_ACC) {
         float old[16];
 #pragma unroll
@@ -946,26 +946,25 @@ __device__ __forceinline__ void store_tiles_inplace(const f32x16 (&acc)[TM][TN],
           old[e] = bitsf(__builtin_amdgcn_raw_buffer_load_b32(r, lane_off + rw * ld, 0, 0));
         }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) out[e] += old[e];
+        for (int e = 0; e < 16; ++e) acc[i][j][e] += old[e];
       } else {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float v = out[e] + bias;
+          float v = acc[i][j][e] + bias;
           if (glu) v = silu(v) * (acc[i][j | 1][e] + bias_up);
           else if (gelu) v = gelu_tanh(v);
-          out[e] = ES == 2 ? bitsf(bf16bits(v)) : v;
+          acc[i][j][e] = ES == 2 ? bitsf(bf16bits(v)) : v;
         }
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const uint32_t rw = 32 * i + 8 * (e >> 2) + (e & 3);
-        const uint32_t x = fbits(out[e]);
+        const uint32_t x = fbits(acc[i][j][e]);
         if constexpr (ES == 2)
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)x, r, lane_off + rw * ld, 0, 0);
         else
           __builtin_amdgcn_raw_buffer_store_b32(x, r, lane_off + rw * ld, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -1029,42 +1028,36 @@ gemm_bf16_nt_w128(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
   auto stage_a = [&](int u) { return smem + (u % 3) * A_STAGE; };
   auto stage_b = [&](int u) { return smem + 3 * A_STAGE + (u & 1) * B_STAGE; };
   // loads of global K-tile u, K-tile kt of the current tile (kt >= nk: of the next)
+  // (with one tile per workgroup the tile's rows are folded into the
+  // per-lane offsets once)
+  if constexpr (!PERSIST) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      voa[j] += (uint32_t)m0 * lda2;
+      vob[j] += (uint32_t)n0 * ldb2;
+    }
+  }
   auto load_a = [&](int u, int kt, int j) {
-    const bool nxt = kt >= nk;
-    const uint32_t row = (uint32_t)(nxt ? m0n : m0) * lda2;
-    lds_dma(ra, stage_a(u) + (wave * 64 + 8 * j) * kRowChunks, voa[j] + row,
-            (uint32_t)(nxt ? kt - nk : kt) * (kBK * 2));
-  };
-  auto load_b = [&](int u, int kt, int j) {
-    const bool nxt = kt >= nk;
-    const uint32_t row = (uint32_t)(nxt ? n0n : n0) * ldb2;
-    lds_dma(rb, stage_b(u) + (wave * 64 + 8 * j) * kRowChunks, vob[j] + row,
-            (uint32_t)(nxt ? kt - nk : kt) * (kBK * 2));
-  };
-  const int a_row = 128 * wm + (lane & 31), b_row = 128 * wn + (lane & 31), khalf = lane >> 5;
-  bf16x8 fa[2][TM], fb[2][TN];
-  // fragment r of k-group kc of global K-tile u into buffer buf: A tile i = r
-  // (r < 4), B tile j = r - 4
-  auto read_frag = [&](int u, int kc, int buf, int r) {
-    if (r < TM) {
-      const u32x4* sa = stage_a(u);
-      fa[buf][r] = __builtin_bit_cast(bf16x8, sa[(a_row + 32 * r) * kRowChunks + swizzle(a_row, kc)]);
+    if constexpr (PERSIST) {
+      const bool nxt = kt >= nk;
+      const uint32_t row = (uint32_t)(nxt ? m0n : m0) * lda2;
+      lds_dma(ra, stage_a(u) + (wave * 64 + 8 * j) * kRowChunks, voa[j] + row,
+              (uint32_t)(nxt ? kt - nk : kt) * (kBK * 2));
     } else {
-      const u32x4* sb = stage_b(u);
-      fb[buf][r - TM] = __builtin_bit_cast(bf16x8, sb[(b_row + 32 * (r - TM)) * kRowChunks + swizzle(b_row, kc)]);
+      lds_dma(ra, stage_a(u) + (wave * 64 + 8 * j) * kRowChunks, voa[j], (uint32_t)kt * (kBK * 2));
     }
   };
-  f32x16 acc[TM][TN];
-  auto mfma = [&](int buf, int m) {
-    acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][m >> 2], fb[buf][m & 3],
-                                                                 acc[m >> 2][m & 3], 0, 0, 0);
+  auto load_b = [&](int u, int kt, int j) {
+    if constexpr (PERSIST) {
+      const bool nxt = kt >= nk;
+      const uint32_t row = (uint32_t)(nxt ? n0n : n0) * ldb2;
+      lds_dma(rb, stage_b(u) + (wave * 64 + 8 * j) * kRowChunks, vob[j] + row,
+              (uint32_t)(nxt ? kt - nk : kt) * (kBK * 2));
+    } else {
+      lds_dma(rb, stage_b(u) + (wave * 64 + 8 * j) * kRowChunks, vob[j], (uint32_t)kt * (kBK * 2));
+    }
   };
-  // a tile's first k-step starts its accumulators from zero
-  auto mfma0 = [&](int m) {
-    const f32x16 zero = {};
-    acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][m >> 2], fb[0][m & 3], zero, 0, 0, 0);
-  };
-
+  const int a_row = 128 * wm + (lane & 31), b_row = 128 * wn + (lane & 31), khalf = lane >> 5;
   const int total = n_mine * nk;   // K tiles in this workgroup's stream
   // prologue: B and A of K-tile 0, A of K-tile 1, then the first half of B of K-tile 1
 #pragma unroll
@@ -1077,72 +1070,119 @@ gemm_bf16_nt_w128(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
   }
   wait_vmem_w128<0>();
   __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 8; ++r) read_frag(0, khalf, 0, r);
   if (total > 1) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) load_b(1, 1, j);
   }
-
-  // Global K tile u = K tile kt of the current tile.  NEXT2: K tile u + 2
-  // exists; NEXT1: u + 1 exists (either may be in the next tile); FRAG1:
-  // u + 1's first fragments are read here (not in a tile's last K tile, so
-  // that no fragment registers stay live across the tile's stores).
-  auto ktile = [&](int u, int kt, auto next2_c, auto next1_c, auto frag1_c, auto first_c) {
-    constexpr bool NEXT2 = decltype(next2_c)::value;
-    constexpr bool NEXT1 = decltype(next1_c)::value;
-    constexpr bool FRAG1 = decltype(frag1_c)::value;
-    constexpr bool FIRST = decltype(first_c)::value;   // the tile's first K tile
-    // k-steps 0-2: fragments of k-step s + 1 after MFMAs 0, 2, .., 14;
-    // loads after MFMAs 0, 4, 8, 12
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      const int buf = s & 1;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        if (PERSIST && FIRST && s == 0) mfma0(m); else mfma(buf, m);
-        __builtin_amdgcn_sched_barrier(0);
-        if ((m & 1) == 0) read_frag(u, 2 * (s + 1) + khalf, buf ^ 1, m >> 1);
-        if ((m & 3) == 0) {
-          if (s == 0) {
-            if constexpr (NEXT1) load_b(u + 1, kt + 1, 4 + (m >> 2));
-          } else {
-            if constexpr (NEXT2) load_a(u + 2, kt + 2, 4 * (s - 1) + (m >> 2));
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // k-step 3 (buffer 1): the barrier after MFMA 3; then K-tile u + 1's
-    // first fragments, two after each of MFMAs 4-7 (so they have landed well
-    // before its first MFMAs), and the first half of B of u + 2 after MFMAs 8-11
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      mfma(1, m);
-      __builtin_amdgcn_sched_barrier(0);
-      if (m == 3) {
-        if constexpr (NEXT2) wait_vmem_w128<8>(); else wait_vmem_w128<0>();
-        lds_wait_barrier();
-      }
-      if (m >= 4 && m < 8) {
-        if constexpr (FRAG1) {
-          read_frag(u + 1, khalf, 0, 2 * (m - 4));
-          read_frag(u + 1, khalf, 0, 2 * (m - 4) + 1);
-        }
-      }
-      if (m >= 8 && m < 12) {
-        if constexpr (NEXT2) load_b(u + 2, kt + 2, m - 8);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  // the tile's results (with the persistent grid, the loads of the next
-  // tile's first K tiles are in flight meanwhile)
-  auto epilogue = [&]() {
+  int u = 0;
+  for (int t = 0; t < n_mine; ++t) {
+    // fragments and accumulators live within one tile, so none is carried
+    // across the tile's stores into the next
+    bf16x8 fa[2][TM], fb[2][TN];
+    f32x16 acc[TM][TN];
+    // fragment r of k-group kc of global K-tile u into buffer buf: A tile i
+    // = r (r < 4), B tile j = r - 4
+    auto read_frag = [&](int uu, int kc, int buf, int r) {
+      if (r < TM) {
+        const u32x4* sa = stage_a(uu);
+        fa[buf][r] = __builtin_bit_cast(bf16x8, sa[(a_row + 32 * r) * kRowChunks + swizzle(a_row, kc)]);
+      } else {
+        const u32x4* sb = stage_b(uu);
+        fb[buf][r - TM] = __builtin_bit_cast(bf16x8, sb[(b_row + 32 * (r - TM)) * kRowChunks + swizzle(b_row, kc)]);
+      }
+    };
+    auto mfma = [&](int buf, int m) {
+      acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][m >> 2], fb[buf][m & 3],
+                                                                   acc[m >> 2][m & 3], 0, 0, 0);
+    };
+    // the tile's first k-step starts its accumulators from zero
+    auto mfma0 = [&](int m) {
+      const f32x16 zero = {};
+      acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][m >> 2], fb[0][m & 3], zero, 0, 0, 0);
+    };
+    // Global K tile u = K tile kt of the current tile.  NEXT2: K tile u + 2
+    // exists; NEXT1: u + 1 exists (either may be in the next tile); FRAG1:
+    // u + 1's first fragments are read here (not in a tile's last K tile, so
+    // that no fragment registers stay live across the tile's stores).
+    auto ktile = [&](int u, int kt, auto next2_c, auto next1_c, auto frag1_c, auto first_c) {
+      constexpr bool NEXT2 = decltype(next2_c)::value;
+      constexpr bool NEXT1 = decltype(next1_c)::value;
+      constexpr bool FRAG1 = decltype(frag1_c)::value;
+      constexpr bool FIRST = decltype(first_c)::value;   // the tile's first K tile
+      // k-steps 0-2: fragments of k-step s + 1 after MFMAs 0, 2, .., 14;
+      // loads after MFMAs 0, 4, 8, 12
+  #pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        const int buf = s & 1;
+  #pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          if (FIRST && s == 0) mfma0(m); else mfma(buf, m);
+          __builtin_amdgcn_sched_barrier(0);
+          if ((m & 1) == 0) read_frag(u, 2 * (s + 1) + khalf, buf ^ 1, m >> 1);
+          if ((m & 3) == 0) {
+            if (s == 0) {
+              if constexpr (NEXT1) load_b(u + 1, kt + 1, 4 + (m >> 2));
+            } else {
+              if constexpr (NEXT2) load_a(u + 2, kt + 2, 4 * (s - 1) + (m >> 2));
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // k-step 3 (buffer 1): the barrier after MFMA 3; then K-tile u + 1's
+      // first fragments, two after each of MFMAs 4-7 (so they have landed well
+      // before its first MFMAs), and the first half of B of u + 2 after MFMAs 8-11
+  #pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        mfma(1, m);
+        __builtin_amdgcn_sched_barrier(0);
+        if (m == 3) {
+          if constexpr (NEXT2) wait_vmem_w128<8>(); else wait_vmem_w128<0>();
+          lds_wait_barrier();
+        }
+        if (m >= 4 && m < 8) {
+          if constexpr (FRAG1) {
+            read_frag(u + 1, khalf, 0, 2 * (m - 4));
+            read_frag(u + 1, khalf, 0, 2 * (m - 4) + 1);
+          }
+        }
+        if (m >= 8 && m < 12) {
+          if constexpr (NEXT2) load_b(u + 2, kt + 2, m - 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // the tile's first fragments (its first K tile was published by the
+    // prologue's barrier or by the previous tile's last K tile)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) read_frag(u, khalf, 0, r);
+    int kt = 0;
+    if (t + 1 < n_mine) {
+      ktile(u, kt, T_{}, T_{}, T_{}, T_{});
+      for (++kt, ++u; kt + 1 < nk; ++kt, ++u) ktile(u, kt, T_{}, T_{}, T_{}, F_{});
+      ktile(u, kt, T_{}, T_{}, F_{}, F_{});
+      ++u;
+    } else if (nk == 1) {
+      ktile(u, kt, F_{}, F_{}, F_{}, T_{});
+      ++u;
+    } else {
+      if (nk == 2) ktile(u, kt, F_{}, T_{}, T_{}, T_{});
+      else ktile(u, kt, T_{}, T_{}, T_{}, T_{});
+      for (++kt, ++u; kt + 2 < nk; ++kt, ++u) ktile(u, kt, T_{}, T_{}, T_{}, F_{});
+      if (kt + 1 < nk) {
+        ktile(u, kt, F_{}, T_{}, T_{}, F_{});
+        ++kt;
+        ++u;
+      }
+      ktile(u, kt, F_{}, F_{}, F_{}, F_{});
+      ++u;
+    }
+    // the tile's results (with several tiles per workgroup, the loads of the
+    // next tile's first K tiles are in flight meanwhile); one activation for
+    // the wave's 128 columns when they lie on one side of act_from
     const int c0 = n0 + 128 * wn, r0 = m0 + 128 * wm;
-    // one activation for the wave's 128 columns when they lie on one side of act_from
     if (KIND == OutKind::F32_ACC || c0 + 128 <= ep.act_from || ep.act == Act::NONE)
       store_tiles_inplace<KIND, TM, TN, 1>(acc, p, ep, r0, c0, lane);
     else if (c0 >= ep.act_from && ep.act == Act::GELU_TANH)
@@ -1151,57 +1191,9 @@ gemm_bf16_nt_w128(GemmProblem p, GemmEpilogue ep, int tiles_m, int tiles_n) {
       store_tiles_inplace<KIND, TM, TN, 3>(acc, p, ep, r0, c0, lane);
     else
       store_tiles_inplace<KIND, TM, TN, 0>(acc, p, ep, r0, c0, lane);
-  };
-  if constexpr (!PERSIST) {
-    // one tile: accumulators from zero, K tiles in one loop
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    int kt = 0;
-    for (; kt + 2 < nk; ++kt) ktile(kt, kt, T_{}, T_{}, T_{}, F_{});
-    if (kt + 1 < nk) {
-      ktile(kt, kt, F_{}, T_{}, T_{}, F_{});
-      ++kt;
-    }
-    ktile(kt, kt, F_{}, F_{}, F_{}, F_{});
-    epilogue();
-    return;
-  } else {
-    int u = 0;
-    for (int t = 0; t < n_mine; ++t) {
-      // the tile's first K tile starts its accumulators from zero (nk >= 2)
-      int kt = 0;
-      if (t + 1 < n_mine) {
-        ktile(u, kt, T_{}, T_{}, T_{}, T_{});
-        for (++kt, ++u; kt + 1 < nk; ++kt, ++u) ktile(u, kt, T_{}, T_{}, T_{}, F_{});
-        ktile(u, kt, T_{}, T_{}, F_{}, F_{});
-        ++u;
-      } else {
-        if (nk == 2) ktile(u, kt, F_{}, T_{}, T_{}, T_{});
-        else ktile(u, kt, T_{}, T_{}, T_{}, T_{});
-        for (++kt, ++u; kt + 2 < nk; ++kt, ++u) ktile(u, kt, T_{}, T_{}, T_{}, F_{});
-        if (kt + 1 < nk) {
-          ktile(u, kt, F_{}, T_{}, T_{}, F_{});
-          ++kt;
-          ++u;
-        }
-        ktile(u, kt, F_{}, F_{}, F_{}, F_{});
-        ++u;
-      }
-      epilogue();
-      if (t + 1 < n_mine) {
-        m0 = m0n;
-        n0 = n0n;
-        if (t + 2 < n_mine) origin(tile_id(t + 2), m0n, n0n);
-        // the next tile's first fragments (its first K tile was published
-        // by the barrier of this tile's last one)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) read_frag(u, khalf, 0, r);
-      }
-    }
+    m0 = m0n;
+    n0 = n0n;
+    if (t + 2 < n_mine) origin(tile_id(t + 2), m0n, n0n);
   }
 }
 
