@@ -284,6 +284,35 @@ def test_persistent_gemm_several_tiles_per_workgroup_gelu_all_columns():
     close_all(shards)
 
 
+@pytest.mark.parametrize("act", ["gelu_tanh", "swiglu"])
+def test_one_wave_gemm_activation_boundary_inside_a_wave(act):
+    # Fused colwise with head_dim 32 and hidden 1088 (34 heads, P = 1): qkv
+    # takes columns [0, 3264) and the activation starts at column 3264 =
+    # 25.5 x 128, inside a 128-column wave block.  M = 2048, N = 3264 + 4928
+    # (GELU) or 3264 + 2 x 2464 (SwiGLU gate/up) = 8192 and K = 1088: exactly
+    # 256 tiles of 256 x 256, so the one-wave-per-SIMD kernel runs, and for
+    # that wave its epilogue chooses the activation and the output (qkv or h)
+    # per 32-column block (SwiGLU: a plain pair, then a gate/up pair).  Only
+    # the colwise call: attention is built for head_dim 128.
+    F = 4928 if act == "gelu_tanh" else 2464
+    w = Workload(f"fix0_{act}_T2048_D1088_H34d32_F{F}_P1", 2048, 1088, 34, 32, F, 1, "bf16",
+                 mlp_act=act)
+    inp = tp_inputs.make_inputs(w, seed=32)
+    ref = O.rank_forward(inp.values["x"], inp.values, 1, 0, 34, 32, True, mlp_act=act)
+    shards = H.create_shards(w, inp)
+    x = H.to_device(inp, "x")
+    s = shards[0]
+    qkv = torch.empty((w.tokens, 3 * s.d_r), dtype=torch.bfloat16, device="cuda")
+    h = torch.empty((w.tokens, s.f_r), dtype=torch.bfloat16, device="cuda")
+    tp.tp_colwise_qkv_up(s, w.tokens, x, qkv, h)
+    torch.cuda.synchronize()
+    e_q = H.rel_err(H.as_f64(qkv), ref["qkv_r"])
+    e_h = H.rel_err(H.as_f64(h), ref["h_r"])
+    say(w.name, f"qkv {e_q:.2e} h {e_h:.2e}")
+    assert e_q <= H.TOL["bf16"] and e_h <= H.TOL["bf16"]
+    close_all(shards)
+
+
 def test_large_rowwise_store_and_accumulate_paths():
     # MLP-only, P = 1, hidden 8192: the down projection is N = 8192 -> 9 x 32 =
     # 288 tiles, on 256 persistent workgroups (a last round of 32 tiles)
