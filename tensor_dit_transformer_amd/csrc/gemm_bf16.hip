@@ -11,8 +11,11 @@
 //
 // Design (gfx950, 64-wide waves, 160 KB LDS per CU).  A 4-wave
 // register-staged kernel for small and ragged bf16 shapes and for every fp32
-// one, and the 8-wave ping-pong kernels further down for large bf16 ones (at
-// least 128 tiles of 256x256 or 288x192, K % 64 == 0).  The 4-wave kernel:
+// one; for large bf16 ones (at least 128 tiles, K % 64 == 0) direct-to-LDS
+// kernels further down: 8-wave ping-pong kernels on 288x192 and 192x256
+// tiles, and on 256x256 tiles a one-wave-per-SIMD kernel (persistent when
+// every tile costs the same), with the 8-wave kernel as its fallback
+// (launch_gemm_bf16 chooses).  The register-staged kernel:
 //   * 256 threads = 4 waves in a WM x WN grid; each wave owns a
 //     (BM/WM) x (BN/WN) block of C held in accumulation registers as
 //     32x32 MFMA tiles.
@@ -27,11 +30,12 @@
 //   * Workgroup ids are renumbered so each of the 8 XCDs (own L2) walks a
 //     contiguous stretch of a grouped tile order (8 tile rows per group), and
 //     the A/B panels it streams are shared by its neighbours in L2.
-//   * Rows past M / N are masked on store; on load the 4-wave kernel clamps
-//     them to the last row and the 8-wave kernels read them as zero (past
-//     their buffer descriptors' range).  In the 4-wave kernel a K that is not
-//     a whole number of tiles zero-fills the chunks past K (K must be a
-//     multiple of the 8 bf16 or 4 fp32 elements of a chunk).
+//   * Rows past M / N are masked on store; on load the register-staged
+//     kernel clamps them to the last row and the direct-to-LDS kernels read
+//     them as zero (past their buffer descriptors' range).  In the
+//     register-staged kernel a K that is not a whole number of tiles
+//     zero-fills the chunks past K (K must be a multiple of the 8 bf16 or 4
+//     fp32 elements of a chunk).
 #include "tp_kernels.h"
 
 #include <type_traits>
