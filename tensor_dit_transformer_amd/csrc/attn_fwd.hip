@@ -423,6 +423,12 @@ __device__ __forceinline__ void mfma_s_acc(f32x16& s, bf16x8 k, bf16x8 q) {
 __device__ __forceinline__ void fence_s(f32x16& x, f32x16& y) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
+// No wait states, only an ordering point: where the slot schedule already
+// puts more than an MFMA's wait states of other instructions between the
+// last MFMA writing these registers and the first instruction touching them.
+__device__ __forceinline__ void order_s(f32x16& x, f32x16& y) {
+  asm volatile("" : "+v"(x), "+v"(y));
+}
 __device__ __forceinline__ void fence_acc(f32x16 (&acc)[2][kD / 32]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
@@ -672,6 +678,8 @@ attn_fwd_q64(AttnIO io) {
         else mfma_s_acc(s[a][0], k, qf[a][st]);
       }
     }
+    // the next tile reads these right after its barrier
+    fence_s(s[0][0], s[1][0]);
   };
 
   // Tile kt.  On entry: s[.][0] holds the raw scores of S(kt) key half 0,
@@ -691,7 +699,9 @@ attn_fwd_q64(AttnIO io) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    fence_s(s[0][0], s[1][0]);
+    // key half 0's last score MFMAs were in the previous tile's slots 30 and
+    // 31 (the prologue and the rescale rule end with a fence instead)
+    order_s(s[0][0], s[1][0]);
     if (masked) mask_half(kt, 0);
     const float lb[2] = {l_run[0], l_run[1]};
     float l[2] = {l_run[0], l_run[1]}, l2[2] = {0.0f, 0.0f};
@@ -710,7 +720,9 @@ attn_fwd_q64(AttnIO io) {
       }
       __builtin_amdgcn_sched_barrier(0);
       if (p == 16) {
-        fence_s(s[0][1], s[1][1]);
+        // key half 1's last score MFMAs were in slots 14 and 15, a slot and
+        // a half of other instructions ago
+        order_s(s[0][1], s[1][1]);
         if (masked) mask_half(kt, 1);
       }
       const int wa = (p >> 3) & 1, q = (p & 7) + 8 * (p >> 4);
