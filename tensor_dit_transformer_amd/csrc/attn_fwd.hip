@@ -736,9 +736,11 @@ attn_fwd_q64(AttnIO io) {
         mfma_pv(acc_o[a][t], vf[f % 3], pprev[a][cu >> 1][cu & 1]);
         if (a == 1 && f + 2 < 16) vf[(f + 2) % 3] = vread(sVp, (f + 2) >> 2, (f + 2) & 3);
       }
-      if (p < 8) {
-        if constexpr (WHOLE) load(kt + 2, (cur + 2) % NSTAGE, p);
-        else load_any(kt + 2, (cur + 2) % NSTAGE, p);
+      // the 8 loads of tile kt + 2 in the even slots 0-14, one per two
+      // slots; they land before the next tile's barrier waits on them
+      if (p < 16 && (p & 1) == 0) {
+        if constexpr (WHOLE) load(kt + 2, (cur + 2) % NSTAGE, p >> 1);
+        else load_any(kt + 2, (cur + 2) % NSTAGE, p >> 1);
       }
       __builtin_amdgcn_sched_barrier(0);
       pcur[wa][wc][we >> 3][we & 7] = static_cast<bf16>(e0);
