@@ -174,12 +174,14 @@ def test_no_mfma_result_read_too_early_at_a_block_start(tmp_path):
 # ---------------------------------------------------------------------------
 # MFMAs issued from inline asm (the 64-query attention pins its accumulators
 # to AGPRs that way) are not MFMAs to the compiler's hazard recognizer, so
-# within a block it pads nothing around them.  The kernel's own fences supply
-# the wait states; this scan checks every such MFMA in straight-line code:
+# within a block it pads nothing around them.  The kernel's own fences, or
+# the distance its schedule puts between an MFMA and the first use of its
+# result, supply the wait states; this scan checks every such MFMA: on every
+# path from it, through branches taken or not (a loop's back edge included),
 # no instruction touches its result registers sooner than NEED_WAIT_STATES
 # after it (a chained srcC of the next MFMA is forwarded by the hardware),
-# and no vector instruction writes one of its source registers fewer than 2
-# wait states before it.
+# and in straight-line code no vector instruction writes one of its source
+# registers fewer than 2 wait states before it.
 VALU_WRITE_TO_MFMA = 2
 
 
@@ -203,8 +205,9 @@ def _asm_blocks(text):
         if s.startswith(".Lfunc_end"):
             cur = None
             continue
-        if re.match(r"^\.LBB\w+:", s):
-            cur.append(("LABEL", "", [], False))
+        m = re.match(r"^(\.LBB\w+):", s)
+        if m:
+            cur.append(("LABEL", m.group(1), [], False))
             continue
         s = s.strip()
         if not s or s.startswith("."):
@@ -216,31 +219,55 @@ def _asm_blocks(text):
     return funcs
 
 
+def _touches_result(op2, ops2, dst):
+    touched = set().union(*[_regs(o) for o in (ops2[1:3] if op2.startswith("v_mfma") else ops2)])
+    if op2.startswith("v_mfma") and _regs(ops2[0]) == dst and dst <= set().union(*[_regs(o) for o in ops2[3:4]]):
+        return False   # the next MFMA chaining the accumulator
+    return bool(dst & touched)
+
+
 def scan_inline_mfma(text):
     found = []
     for name, ins in _asm_blocks(text):
+        labels = {x[1]: i for i, x in enumerate(ins) if x[0] == "LABEL"}
         for i, (op, rest, ops, asm) in enumerate(ins):
             if not (asm and op.startswith("v_mfma")):
                 continue
             need = NEED_WAIT_STATES.get(op, LOOKBACK)
             dst = _regs(ops[0])
             srcs = set().union(*[_regs(o) for o in ops[1:4]])
-            # later instructions touching the result
-            ws = 0
-            for j in range(i + 1, len(ins)):
-                op2, rest2, ops2, _ = ins[j]
-                if op2 == "LABEL" or op2.startswith(("s_branch", "s_cbranch", "s_endpgm")) or ws >= need:
-                    break
-                if op2 == "s_nop":
-                    ws += int(rest2.split()[0]) + 1
+            # later instructions touching the result, on every path (a branch
+            # taken or not) until NEED_WAIT_STATES have passed
+            paths, seen, hit = [(i + 1, 0)], set(), None
+            while paths and hit is None:
+                j, ws = paths.pop()
+                if (j, ws) in seen:
                     continue
-                touched = set().union(*[_regs(o) for o in (ops2[1:3] if op2.startswith("v_mfma") else ops2)])
-                if op2.startswith("v_mfma") and _regs(ops2[0]) == dst and dst <= set().union(*[_regs(o) for o in ops2[3:4]]):
-                    touched = set()   # the next MFMA chaining the accumulator
-                if dst & touched:
-                    found.append((name, f"{op} {rest}", f"{op2} {rest2}", ws))
-                    break
-                ws += 1
+                seen.add((j, ws))
+                while j < len(ins) and ws < need:
+                    op2, rest2, ops2, _ = ins[j]
+                    if op2 == "LABEL":
+                        j += 1
+                        continue
+                    if op2 == "s_endpgm":
+                        break
+                    if op2 == "s_nop":
+                        ws += int(rest2.split()[0]) + 1
+                        j += 1
+                        continue
+                    if ops2 and _touches_result(op2, ops2, dst):
+                        hit = (name, f"{op} {rest}", f"{op2} {rest2}", ws)
+                        break
+                    if op2.startswith(("s_cbranch", "s_branch")):
+                        target = rest2.split()[0] if rest2 else ""
+                        if target in labels:
+                            paths.append((labels[target] + 1, ws + 1))
+                        if op2 == "s_branch":
+                            break
+                    ws += 1
+                    j += 1
+            if hit:
+                found.append(hit)
             # earlier vector writes of its sources
             ws = 0
             for j in range(i - 1, -1, -1):
@@ -281,6 +308,30 @@ def test_inline_scanner_flags_unpadded_neighbours():
 def test_inline_scanner_accepts_padding():
     hits = scan_inline_mfma(INLINE_SNIPPET.format(pad="\ts_nop 7\n\ts_nop 2\n"))
     assert [h[2].split()[0] for h in hits] == ["v_mov_b32_e32"]   # 11 wait states clear the read
+
+
+# An MFMA whose result is read after a taken branch, at the top of a loop:
+# only the path through the branch is short.
+BRANCH_SNIPPET = """_Zk:
+.LBB0_1:
+{pad}\tv_accvgpr_read_b32 v10, a3
+\ts_nop 7
+\ts_nop 7
+\t;;#ASMSTART
+\tv_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]
+\t;;#ASMEND
+\ts_cbranch_scc1 .LBB0_1
+\ts_endpgm
+.Lfunc_end0:
+"""
+
+
+def test_inline_scanner_follows_a_taken_branch():
+    hits = scan_inline_mfma(BRANCH_SNIPPET.format(pad=""))
+    assert [(h[2].split()[0], h[3]) for h in hits] == [("v_accvgpr_read_b32", 1)]
+    # 1 (the branch) + 10 wait states clear it
+    assert scan_inline_mfma(BRANCH_SNIPPET.format(pad="\ts_nop 9\n")) == []
+    assert len(scan_inline_mfma(BRANCH_SNIPPET.format(pad="\ts_nop 8\n"))) == 1
 
 
 def test_inline_asm_mfmas_are_padded(tmp_path):
