@@ -720,8 +720,9 @@ attn_fwd_q64(AttnIO io) {
       }
       __builtin_amdgcn_sched_barrier(0);
       if (p == 16) {
-        // key half 1's last score MFMAs were in slots 14 and 15, a slot and
-        // a half of other instructions ago
+        // key half 1's last score MFMAs were in slots 14 and 15, at least a
+        // slot of other instructions ago (tests/test_isa_hazards.py checks
+        // the distance on every path)
         order_s(s[0][1], s[1][1]);
         if (masked) mask_half(kt, 1);
       }
