@@ -713,10 +713,6 @@ attn_fwd_q64(AttnIO io) {
         const bf16x8 k = kf[(p >> 1) % 3];
         if (st == 0) mfma_s_zero(s[a][c], k, qf[a][0]);
         else mfma_s_acc(s[a][c], k, qf[a][st]);
-        if (a == 0) {
-          const int nf = (p >> 1) + 2;   // two fragments ahead
-          if (nf < 16) kf[nf % 3] = nf < 8 ? kread(sKc, 1, nf) : kread(sKn, 0, nf - 8);
-        }
       }
       __builtin_amdgcn_sched_barrier(0);
       if (p == 16) {
@@ -742,6 +738,12 @@ attn_fwd_q64(AttnIO io) {
       if (p < 16 && (p & 1) == 0) {
         if constexpr (WHOLE) load(kt + 2, (cur + 2) % NSTAGE, p >> 1);
         else load_any(kt + 2, (cur + 2) % NSTAGE, p >> 1);
+      }
+      // the K fragment two ahead, in the even slots after the PV MFMA (the
+      // odd slots read V there)
+      if ((p & 1) == 0) {
+        const int nf = (p >> 1) + 2;
+        if (nf < 16) kf[nf % 3] = nf < 8 ? kread(sKc, 1, nf) : kread(sKn, 0, nf - 8);
       }
       __builtin_amdgcn_sched_barrier(0);
       pcur[wa][wc][we >> 3][we & 7] = static_cast<bf16>(e0);
