@@ -14,8 +14,8 @@
 // one; for large bf16 ones (at least 128 tiles, K % 64 == 0) direct-to-LDS
 // kernels further down: 8-wave ping-pong kernels on 288x192 and 192x256
 // tiles, and on 256x256 tiles a one-wave-per-SIMD kernel (persistent when
-// every tile costs the same), with the 8-wave kernel as its fallback
-// (launch_gemm_bf16 chooses).  The register-staged kernel:
+// there are more tiles than compute units), with the 8-wave kernel as its
+// fallback (launch_gemm_bf16 chooses).  The register-staged kernel:
 //   * 256 threads = 4 waves in a WM x WN grid; each wave owns a
 //     (BM/WM) x (BN/WN) block of C held in accumulation registers as
 //     32x32 MFMA tiles.
@@ -1232,19 +1232,18 @@ int cu_count() {
   return cached[dev];
 }
 
-// One workgroup per compute unit, each looping over its tiles, when every
-// tile costs the same: then the next tile's first loads overlap this tile's
-// stores.  When an activation covers only part of the columns (the fused
-// QKV + up projection), its tiles' epilogues cost several times the others',
-// and one tile per workgroup lets the hardware's dispatch even out the
-// compute units' loads instead.  Also one tile per workgroup when K is a
-// single K tile, which the stream's two-ahead loads would otherwise reach
-// past the next tile.
+// One workgroup per compute unit, each looping over its tiles, when there
+// are more tiles than compute units: then the next tile's first loads overlap
+// this tile's stores.  This holds also where an activation covers only part
+// of the columns (the fused QKV + up projection), whose activated tiles'
+// epilogues cost several times the others': a workgroup's share of them
+// differs from another's by at most one, less than the overlap gains.  One
+// tile per workgroup when K is a single K tile, which the stream's two-ahead
+// loads would otherwise reach past the next tile.
 hipError_t launch_w128(const GemmProblem& p, const GemmEpilogue& ep, OutKind kind, hipStream_t stream) {
   const int tm = (p.M + 255) / 256, tn = (p.N + 255) / 256;
   const int ntiles = tm * tn;
-  const bool mixed = kind != OutKind::F32_ACC && ep.act != Act::NONE && ep.act_from > 0 && ep.act_from < p.N;
-  const bool persist = p.K / kBK >= 2 && !mixed && ntiles > cu_count();
+  const bool persist = p.K / kBK >= 2 && ntiles > cu_count();
   const dim3 grid(persist ? cu_count() : ntiles), block(256);
   switch (kind) {
     case OutKind::BF16:

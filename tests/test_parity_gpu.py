@@ -284,18 +284,21 @@ def test_persistent_gemm_several_tiles_per_workgroup_gelu_all_columns():
     close_all(shards)
 
 
+@pytest.mark.parametrize("tokens", [2048, 2248])
 @pytest.mark.parametrize("act", ["gelu_tanh", "swiglu"])
-def test_one_wave_gemm_activation_boundary_inside_a_wave(act):
+def test_one_wave_gemm_activation_boundary_inside_a_wave(act, tokens):
     # Fused colwise with head_dim 32 and hidden 1088 (34 heads, P = 1): qkv
     # takes columns [0, 3264) and the activation starts at column 3264 =
-    # 25.5 x 128, inside a 128-column wave block.  M = 2048, N = 3264 + 4928
-    # (GELU) or 3264 + 2 x 2464 (SwiGLU gate/up) = 8192 and K = 1088: exactly
-    # 256 tiles of 256 x 256, so the one-wave-per-SIMD kernel runs, and for
-    # that wave its epilogue chooses the activation and the output (qkv or h)
-    # per 32-column block (SwiGLU: a plain pair, then a gate/up pair).  Only
-    # the colwise call: attention is built for head_dim 128.
+    # 25.5 x 128, inside a 128-column wave block.  N = 3264 + 4928 (GELU) or
+    # 3264 + 2 x 2464 (SwiGLU gate/up) = 8192 and K = 1088, so the
+    # one-wave-per-SIMD kernel runs, and for that wave its epilogue chooses
+    # the activation and the output (qkv or h) per 32-column block (SwiGLU: a
+    # plain pair, then a gate/up pair).  M = 2048 gives exactly 256 tiles of
+    # 256 x 256, one per workgroup; M = 2248 gives 288 (the last tile row
+    # ragged) on the persistent grid.  Only the colwise call: attention is
+    # built for head_dim 128.
     F = 4928 if act == "gelu_tanh" else 2464
-    w = Workload(f"fix0_{act}_T2048_D1088_H34d32_F{F}_P1", 2048, 1088, 34, 32, F, 1, "bf16",
+    w = Workload(f"fix0_{act}_T{tokens}_D1088_H34d32_F{F}_P1", tokens, 1088, 34, 32, F, 1, "bf16",
                  mlp_act=act)
     inp = tp_inputs.make_inputs(w, seed=32)
     ref = O.rank_forward(inp.values["x"], inp.values, 1, 0, 34, 32, True, mlp_act=act)
